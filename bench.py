@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed quantized linear layer on one MI355X.
+
+Headline (one JSON line on stdout): quantized-linear GB/s at M = 1 on the
+Llama-7B-shaped 4-bit layers 4096x4096, 11008x4096, 4096x11008 (group 128,
+fp16 in/out).  One step = one forward through the three layers.  Weights are
+rotated over enough packed copies (>= 1 GiB) that every step streams them from
+HBM rather than from the 256 MB last-level cache; the activations are resident.
+
+The same run also times, each on its own workload (field "paths"):
+  * SpQR 3-bit + 1% CSR outliers, 33B-shaped layers, M = 1       (GB/s)
+  * W4 MFMA GEMM, 70B-shaped layers, M = 256, bf16 in/out          (TOPS)
+  * SmoothQuant W8A8 int8 GEMM, 11008x4096 and 4096x4096, M = 256  (TOPS)
+and the CPU oracle on a bounded sample ("cpu_baseline").
+
+Timing uses HIP events on the stream the kernels run on: one event pair around
+the K timed steps gives ms_per_step; a second pass with an event pair around
+every launch gives each kernel's average duration, from which the roofline
+figures are derived.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0}
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-paths", action="store_true", help="headline workload only")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# device helpers
+
+def to_dev(torch, a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.float16).cuda()
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda()
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32)).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def copies_for(bytes_per_set):
+    return max(2, -(-ROTATE_BYTES // max(1, bytes_per_set)))
+
+
+def time_steps(torch, step_fns, steps, warmup, copies):
+    """Time ``steps`` steps; return (ms per step, per-launch average ms list).
+
+    step_fns: callables; step i runs every callable with argument i (i selects
+    the weight copy).  The timed steps replay a HIP graph holding one full
+    rotation (``copies`` steps), so host launch overhead stays out of the
+    measurement.  Per-launch durations come from an eager pass with an event
+    pair around every launch, queued behind a GPU sleep so that the host is
+    ahead of the device and the events bracket only the kernels."""
+    for i in range(warmup):
+        for f in step_fns:
+            f(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(copies):
+                for f in step_fns:
+                    f(i)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    reps = max(1, -(-steps // copies))
+    graph.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / (reps * copies)
+    del graph
+    # per-launch durations
+    n = min(steps, 4 * copies)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in step_fns] for _ in range(n)]
+    try:
+        torch.cuda._sleep(200_000_000)
+    except Exception:  # pragma: no cover - sleep kernel unavailable
+        pass
+    for i in range(n):
+        for j, f in enumerate(step_fns):
+            evs[i][j][0].record(s)
+            f(i)
+            evs[i][j][1].record(s)
+    torch.cuda.synchronize()
+    per = [float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(n)]))
+           for j in range(len(step_fns))]
+    return ms_step, per
+
+
+# ---------------------------------------------------------------------------
+# workloads
+
+def w4_layers(torch, qlin, synth, workload, M):
+    cfg = synth.WORKLOADS[workload]
+    G = cfg["G"]
+    xbf = cfg["x_dtype"] == "bf16"
+    layers = []
+    for li, (N, K) in enumerate(cfg["layers"]):
+        W = synth.layer_weight(workload, li)
+        packed = [to_dev(torch, a) for a in qlin.qlin_w4_pack(W, G)]
+        del W
+        X = to_dev(torch, synth.activations(workload, li, M))
+        ydt = torch.bfloat16 if cfg["y_dtype"] == "bf16" else torch.float16
+        Y = torch.empty((M, N), dtype=ydt, device="cuda")
+        wbytes = sum(t.numel() * t.element_size() for t in packed)
+        layers.append(dict(N=N, K=K, M=M, G=G, packed=[packed], X=X, Y=Y, wbytes=wbytes,
+                           xdt=qlin.QLIN_BF16 if xbf else qlin.QLIN_F16,
+                           ydt=qlin.QLIN_BF16 if cfg["y_dtype"] == "bf16" else qlin.QLIN_F16,
+                           io=X.numel() * X.element_size() + Y.numel() * Y.element_size()))
+    rotate(torch, layers)
+    return layers
+
+
+def rotate(torch, layers):
+    per_set = sum(l["wbytes"] for l in layers)
+    R = copies_for(per_set)
+    for l in layers:
+        base = l["packed"][0]
+        l["packed"] = [base] + [[t.clone() for t in base] for _ in range(R - 1)]
+    return R
+
+
+def w4_step_fns(qlin, layers):
+    fns = []
+    for l in layers:
+        def f(i, l=l):
+            qw, sc, qz = l["packed"][i % len(l["packed"])]
+            qlin.qlin_w4_forward(l["X"], l["xdt"], l["M"], l["K"], qw, sc, qz, l["N"], l["G"], l["Y"], l["ydt"])
+        fns.append(f)
+    return fns
+
+
+def spqr_layers(torch, qlin, synth, M):
+    cfg = synth.WORKLOADS["spqr_33b"]
+    layers = []
+    for li, (N, K) in enumerate(cfg["layers"]):
+        W = synth.layer_weight("spqr_33b", li)
+        st = qlin.spqr_pack(W, cfg["outlier_frac"])
+        del W
+        packed = [to_dev(torch, st[k]) for k in ("codes", "stats1", "stats2", "row_ptr", "col_idx", "val")]
+        X = to_dev(torch, synth.activations("spqr_33b", li, M))
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        wbytes = sum(t.numel() * t.element_size() for t in packed)
+        layers.append(dict(N=N, K=K, M=M, nnz=len(st["val"]), packed=[packed], X=X, Y=Y, wbytes=wbytes,
+                           io=X.numel() * 2 + Y.numel() * 2))
+    rotate(torch, layers)
+    return layers
+
+
+def spqr_step_fns(qlin, layers):
+    fns = []
+    for l in layers:
+        def f(i, l=l):
+            c, s1, s2, rp, ci, v = l["packed"][i % len(l["packed"])]
+            qlin.spqr_forward(l["X"], l["M"], l["K"], c, s1, s2, rp, ci, v, l["nnz"], l["N"], l["Y"], qlin.QLIN_F16)
+        fns.append(f)
+    return fns
+
+
+def sq_layers(torch, qlin, synth, M):
+    cfg = synth.WORKLOADS["sq_w8a8"]
+    layers = []
+    for li, (N, K) in enumerate(cfg["layers"]):
+        W = synth.layer_weight("sq_w8a8", li)
+        Xcal = synth.sq_calibration("sq_w8a8", li)
+        s, inv = qlin.sq_compute_smoothing(qlin.sq_act_absmax(Xcal), W, cfg["alpha"])
+        Wq, ws = qlin.sq_pack_weight(W, s)
+        del W
+        packed = [to_dev(torch, Wq), to_dev(torch, ws)]
+        X = to_dev(torch, synth.activations("sq_w8a8", li, M))
+        layers.append(dict(N=N, K=K, M=M, packed=[packed], X=X, inv=to_dev(torch, inv),
+                           Xq=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                           xs=torch.empty((M,), dtype=torch.float32, device="cuda"),
+                           Y=torch.empty((M, N), dtype=torch.float16, device="cuda"),
+                           wbytes=sum(t.numel() * t.element_size() for t in packed)))
+    rotate(torch, layers)
+    return layers
+
+
+def sq_step_fns(qlin, layers):
+    act, gemm = [], []
+    for l in layers:
+        def a(i, l=l):
+            qlin.sq_smooth_quant_act(l["X"], l["inv"], l["M"], l["K"], l["Xq"], l["xs"])
+
+        def g(i, l=l):
+            Wq, ws = l["packed"][i % len(l["packed"])]
+            qlin.sq_int8_gemm(l["Xq"], l["xs"], Wq, ws, l["M"], l["N"], l["K"], l["Y"], qlin.QLIN_F16, None)
+        act.append(a)
+        gemm.append(g)
+    return act, gemm
+
+
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(synth):
+    """The oracle, untouched, on one forward step of the headline workload."""
+    from oracle import w4 as ow4
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cfg = synth.WORKLOADS["w4_llama7b"]
+    packed = []
+    total_bytes = 0
+    for li, (N, K) in enumerate(cfg["layers"]):
+        W = synth.layer_weight("w4_llama7b", li)
+        st = ow4.encode(W, 128)
+        X = synth.activations("w4_llama7b", li, 1)
+        packed.append((X, st, K))
+        total_bytes += sum(a.nbytes for a in st) + X.nbytes + N * 2
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for X, st, K in packed:
+            ow4.forward(X, *st, K, 128)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 5:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    return {"value": total_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full forward step(s) of the three 4-bit layers at M=1 "
+                      f"(numpy fp64 decode + matvec), {dt * 1e3:.0f} ms per step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    from quantized_linear_layers_packed_amd import qlin
+    torch.cuda.set_device(0)
+
+    # ---- headline: W4 GEMV, Llama-7B-shaped layers, M = 1
+    layers = w4_layers(torch, qlin, synth, "w4_llama7b", 1)
+    fns = w4_step_fns(qlin, layers)
+    ms_step, per = time_steps(torch, fns, args.steps, args.warmup, len(layers[0]["packed"]))
+    step_bytes = sum(l["wbytes"] + l["io"] for l in layers)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    kern_ms = sum(per)
+    achieved = step_bytes / (kern_ms * 1e-3) / 1e9
+    per_layer = [{"shape": f"{l['N']}x{l['K']}", "bytes": l["wbytes"] + l["io"], "us": round(p * 1e3, 3),
+                  "GB/s": round((l["wbytes"] + l["io"]) / (p * 1e-3) / 1e9, 1)} for l, p in zip(layers, per)]
+    rot = len(layers[0]["packed"])
+    del layers, fns
+    torch.cuda.empty_cache()
+
+    out = {
+        "metric": "quantized-linear GB/s at M=1 (% HBM peak); TOPS at M=256 (% MFMA peak)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u4 weights, f16 activations, f32 accumulate",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations)",
+        "config": {"workload": "w4_llama7b: 4-bit GEMV, layers 4096x4096 + 11008x4096 + 4096x11008, "
+                               "group 128, M=1, fp16 in/out",
+                   "global_batch": 1, "weight_copies_rotated": rot, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "w4_gemv_kernel", "per_layer": per_layer},
+    }
+
+    if not args.no_paths:
+        paths = {}
+        steps = max(20, args.steps // 4)
+        warm = max(5, args.warmup // 4)
+        # SpQR M=1
+        L = spqr_layers(torch, qlin, synth, 1)
+        ms, per = time_steps(torch, spqr_step_fns(qlin, L), steps, warm, len(L[0]["packed"]))
+        b = sum(l["wbytes"] + l["io"] for l in L)
+        paths["spqr_33b_M1"] = {"value": round(b / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                                "kernel_GB/s": round(b / (sum(per) * 1e-3) / 1e9, 1),
+                                "frac_hbm": round(b / (sum(per) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                "per_layer_us": [round(p * 1e3, 2) for p in per]}
+        del L
+        torch.cuda.empty_cache()
+        # W4 GEMM M=256
+        L = w4_layers(torch, qlin, synth, "w4_llama70b", 256)
+        ms, per = time_steps(torch, w4_step_fns(qlin, L), steps, warm, len(L[0]["packed"]))
+        fl = sum(2.0 * l["M"] * l["N"] * l["K"] for l in L)
+        tf = fl / (sum(per) * 1e-3) / 1e12
+        paths["w4_llama70b_M256"] = {"value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                                     "kernel_TFLOP/s": round(tf, 2), "frac_mfma_f16": round(tf / 2500.0, 4),
+                                     "per_layer_us": [round(p * 1e3, 2) for p in per]}
+        del L
+        torch.cuda.empty_cache()
+        # SmoothQuant M=256
+        L = sq_layers(torch, qlin, synth, 256)
+        act, gemm = sq_step_fns(qlin, L)
+        ms, per = time_steps(torch, [f for pair in zip(act, gemm) for f in pair], steps, warm, len(L[0]["packed"]))
+        ops = sum(2.0 * l["M"] * l["N"] * l["K"] for l in L)
+        gemm_ms = per[1] + per[3]
+        tops = ops / (gemm_ms * 1e-3) / 1e12
+        paths["sq_w8a8_M256"] = {"value": round(ops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS (act+gemm)",
+                                 "gemm_kernel_TOPS": round(tops, 2), "frac_mfma_i8": round(tops / 5000.0, 4),
+                                 "act_us": [round(per[0] * 1e3, 2), round(per[2] * 1e3, 2)],
+                                 "gemm_us": [round(per[1] * 1e3, 2), round(per[3] * 1e3, 2)]}
+        del L
+        torch.cuda.empty_cache()
+        out["paths"] = paths
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(synth)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

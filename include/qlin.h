@@ -1,0 +1,204 @@
+/*
+ * qlin.h — C ABI of the packed quantized linear layer library for MI355X (gfx950).
+ *
+ * One operation, three weight encodings:  Y[M][N] = X[M][K] . W_hat[N][K]^T
+ * (rows of W_hat are output channels, "out x in").
+ *
+ *   W4     4-bit weights in groups of G along K with an fp16 scale and a 4-bit
+ *          zero per group (GPTQ-style storage).  Source: GPTQ bulletin
+ *          ("Makale Bülteni — GPTQ"), lead and "İddia ve Gerçeklik": 4-bit
+ *          weights quantized in blocks such as groups of 128; weight-only, the
+ *          activations stay 16-bit.
+ *   SpQR   a dense 3-bit matrix (groups of 16, bi-level statistics) plus a CSR
+ *          fp16 outlier matrix holding about 1% of the weights, both applied in
+ *          one pass.  Source: SpQR bulletin ("Makale Bülteni — SpQR"),
+ *          "İddia ve Gerçeklik".
+ *   W8A8   SmoothQuant: Y = (X diag(s)^-1)(diag(s) W) with s folded into the
+ *          weights offline, per-token int8 activations, per-channel int8
+ *          weights, int32 accumulation.  Source: SmoothQuant bulletin
+ *          ("Makale Bülteni — SmoothQuant"), "İddia ve Gerçeklik" and its
+ *          equation.
+ *
+ * Conventions for every call:
+ *   - The caller owns every buffer.  Nothing here allocates device memory.
+ *   - *_forward / sq_* device calls take DEVICE pointers and a HIP stream and are
+ *     asynchronous: they validate arguments on the host, enqueue kernels on
+ *     `stream` and return.  A device-side fault surfaces at the caller's next
+ *     synchronization.  Device pointers must be 16-byte aligned.
+ *   - *_pack / *_sizes / sq_act_absmax / sq_compute_smoothing / sq_pack_weight
+ *     are synchronous host code on HOST pointers; they never touch the GPU and
+ *     are deterministic (bit-identical output for identical input).
+ *   - All arrays are row-major and contiguous.  fp16 and bf16 values travel as
+ *     uint16_t bit patterns.
+ *   - Errors: every call returns a qlin_status.  Invalid arguments are reported
+ *     before anything is enqueued; qlin_last_error() then returns a
+ *     thread-local message naming the argument.
+ *   - Calls on distinct streams may run concurrently; the library keeps no
+ *     state besides the thread-local error message.
+ */
+#ifndef QLIN_H
+#define QLIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  QLIN_OK = 0,
+  QLIN_EINVAL = 1,        /* bad size, NULL pointer, inconsistent arguments     */
+  QLIN_EALIGN = 2,        /* a device pointer is not 16-byte aligned            */
+  QLIN_EUNSUPPORTED = 3,  /* valid but not implemented (e.g. a group size)      */
+  QLIN_EHIP = 4           /* the HIP runtime reported an error at launch        */
+} qlin_status;
+
+typedef enum { QLIN_F16 = 1, QLIN_BF16 = 2, QLIN_F32 = 3 } qlin_dtype;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int qlin_version(void);
+/* Static name of a status code. */
+const char* qlin_status_str(int status);
+/* Thread-local description of the last failure in this thread ("" if none). */
+const char* qlin_last_error(void);
+
+/* ======================================================================== */
+/* W4: 4-bit group quantization                                              */
+/* ======================================================================== */
+/* Storage for an N x K weight, group size G (G divides K, G % 8 == 0):
+ *   qweight uint32 [N][K/8]          code of k in bits 4*(k%8) of word k/8
+ *   scales  fp16   [N][K/G]          per-group scale S
+ *   qzeros  uint32 [N][ceil(K/G/8)]  zero z of group g in bits 4*(g%8) of word g/8
+ * Dequantized weight: w_hat = S * (q - z).                                    */
+
+/* Byte sizes of the three arrays.  EINVAL if N, K, G <= 0 or G does not divide K
+ * or G % 8 != 0. */
+qlin_status qlin_w4_sizes(int N, int K, int G,
+                          size_t* qweight_bytes, size_t* scales_bytes, size_t* qzeros_bytes);
+
+/* Round-to-nearest encode of fp32 W [N][K] (host) into the three host arrays.
+ * Per (row, group): lo = min(0, min w), hi = max(0, max w),
+ * S = fp16((hi - lo) / 15) (S = 1 if that is 0), z = clamp(rint(-lo / S), 0, 15),
+ * q = clamp(rint(w / S) + z, 0, 15); fp32 arithmetic, round half to even.
+ * This is the round-to-nearest baseline named by the GPTQ bulletin
+ * ("İddia ve Gerçeklik"); a second-order encoder would fill the same storage. */
+qlin_status qlin_w4_pack(const float* W, int N, int K, int G,
+                         uint32_t* qweight, uint16_t* scales, uint32_t* qzeros);
+
+/* Y = X . W_hat^T on the GPU.
+ *   X  device, [M][K], x_dtype QLIN_F16 or QLIN_BF16
+ *   Y  device, [M][N], y_dtype QLIN_F16, QLIN_BF16 or QLIN_F32
+ * Accumulation is fp32.  M <= 16 runs a fused unpack-dequant GEMV; larger M runs
+ * an MFMA GEMM on exact integer codes with a per-group fp32 rescale.
+ * Requirements: M, N, K > 0; G % 32 == 0; K % G == 0.  EUNSUPPORTED for other G. */
+qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
+                            const uint32_t* qweight, const uint16_t* scales,
+                            const uint32_t* qzeros, int N, int G,
+                            void* Y, int y_dtype, hipStream_t stream);
+
+/* Debug: unpack codes (uint8 [N][K]) and zeros (uint8 [N][K/G]) on the GPU with
+ * the same unpack routine the forward kernels use. */
+qlin_status qlin_w4_unpack(const uint32_t* qweight, const uint32_t* qzeros,
+                           int N, int K, int G, uint8_t* codes, uint8_t* zeros,
+                           hipStream_t stream);
+
+/* ======================================================================== */
+/* SpQR: 3-bit groups of 16 with bi-level statistics + CSR fp16 outliers     */
+/* ======================================================================== */
+/* Storage for an N x K weight (K % 256 == 0):
+ *   codes   uint32 [N][K/32][3]   one 32-code chunk per 3 words (k = 32c..32c+31):
+ *           codes a0..a15 (group 2c) and b0..b15 (group 2c+1); word j has five
+ *           3-bit fields per 16-bit half (field i at bit 16h + 3i):
+ *             word 0: a0..a4 | a5..a9
+ *             word 1: a10 a11 a12 b0 b1 | a13 a14 a15 b2 b3
+ *             word 2: b4..b8 | b9..b13
+ *           b14 bit j -> bit 15 of word j; b15 bit j -> bit 31 of word j.
+ *   stats1  uint32 [N][K/256][3]  16 six-bit fields per 256-weight block; field g
+ *           at bit 6g of the 96-bit little-endian stream = c_s | c_z << 3
+ *   stats2  fp16   [N][K/256][4]  SS_s, ZS_s, SS_z, ZS_z
+ *   row_ptr int32 [N+1], col_idx int32 [nnz] (ascending per row), vals fp16 [nnz]
+ * Dequantized weight: s_hat = SS_s (c_s - ZS_s), z_hat = SS_z (c_z - ZS_z),
+ * w_hat = s_hat (q - z_hat) + (the CSR value at (n, k), if any).
+ * Source: SpQR bulletin, "İddia ve Gerçeklik" (dense 3-bit groups of 16,
+ * quantized statistics, sparse fp16 outliers of about 1%).                   */
+
+/* Byte sizes and the outlier count nnz = floor(outlier_frac * (N*K)).
+ * EINVAL unless N > 0, K > 0, K % 256 == 0 and 0 <= outlier_frac < 1. */
+qlin_status spqr_sizes(int N, int K, double outlier_frac,
+                       size_t* codes_bytes, size_t* stats1_bytes, size_t* stats2_bytes,
+                       int64_t* nnz);
+
+/* Encode fp32 W [N][K] (host).  Outliers: the nnz largest |w| of the whole
+ * matrix, ties to the lower row-major index (magnitude stands in for the
+ * Hessian-sensitivity criterion of the page).  The rest is quantized in fp32:
+ * first level s = (max-min)/7, z = -min/s per group of 16 (s = 1, z = -min if
+ * max == min); second level per 16 groups, separately for the scales and the
+ * zeros: SS = fp16((max-min)/7), ZS = fp16(-min/SS) (SS = 1 if SS == 0 or ZS
+ * is not finite), c = clamp(rint(v/SS + ZS), 0, 7); codes
+ * q = clamp(rint(w/s_hat + z_hat), 0, 7) against the decoded statistics.
+ * nnz_cap is the capacity of col_idx/vals; EINVAL if smaller than nnz. */
+qlin_status spqr_pack(const float* W, int N, int K, double outlier_frac,
+                      uint32_t* codes, uint32_t* stats1, uint16_t* stats2,
+                      int32_t* row_ptr, int32_t* col_idx, uint16_t* vals,
+                      int64_t nnz_cap, int64_t* nnz_out);
+
+/* Y = X . (W_dense + W_sparse)^T on the GPU.  X fp16 [M][K] (device), Y [M][N]
+ * (device, y_dtype QLIN_F16 or QLIN_F32).  The CSR row of output n is added into
+ * the same fp32 accumulator as the dense dot product, in the same kernel pass.
+ * Requirements: 1 <= M <= 16, K % 256 == 0, row_ptr consistent with nnz
+ * (row_ptr[0] = 0, row_ptr[N] = nnz, checked only for nnz >= 0 on the host:
+ * the device arrays are trusted). */
+qlin_status spqr_forward(const uint16_t* X, int M, int K,
+                         const uint32_t* codes, const uint32_t* stats1, const uint16_t* stats2,
+                         const int32_t* row_ptr, const int32_t* col_idx, const uint16_t* vals,
+                         int64_t nnz, int N, void* Y, int y_dtype, hipStream_t stream);
+
+/* Debug: unpack the dense codes (uint8 [N][K]) and the first-level statistic
+ * codes c_s, c_z (uint8 [N][K/16]) on the GPU with the forward kernel's routine. */
+qlin_status spqr_unpack(const uint32_t* codes, const uint32_t* stats1, int N, int K,
+                        uint8_t* q, uint8_t* cs, uint8_t* cz, hipStream_t stream);
+
+/* ======================================================================== */
+/* SmoothQuant W8A8                                                          */
+/* ======================================================================== */
+/* Per-channel max |x| over the calibration rows (host, fp16 [Mcal][K]). */
+qlin_status sq_act_absmax(const uint16_t* Xcal, int Mcal, int K, float* amax);
+
+/* Smoothing vector (host): b_j = max_n |W[n][j]| over fp32 W [N][K];
+ * s_j = amax_j^alpha / b_j^(1 - alpha) in fp64 (s_j = 1 if amax_j or b_j is 0);
+ * s = fp32(s_j), inv_s = 1 / s in fp32.  alpha in [0, 1]; the page's range is
+ * about 0.8-0.85 (SmoothQuant bulletin, "İddia ve Gerçeklik"). */
+qlin_status sq_compute_smoothing(const float* amax, const float* W, int N, int K,
+                                 double alpha, float* s, float* inv_s);
+
+/* Fold s into W and quantize per output channel (host):
+ * W' = W . diag(s); c_n = max_j |W'[n][j]|; w_scale_n = c_n / 127;
+ * Wq = clamp(rint(W' * (127 / c_n)), -127, 127) (zero row: scale 0, codes 0). */
+qlin_status sq_pack_weight(const float* W, const float* s, int N, int K,
+                           int8_t* Wq, float* w_scale);
+
+/* GPU: x~ = fp32(X) * inv_s per channel; per token a_m = max |x~|,
+ * x_scale_m = a_m / 127, Xq = clamp(rint(x~ * (127 / a_m)), -127, 127)
+ * (zero row: scale 0, codes 0).  Bit-exact with the host definition.
+ * X fp16 [M][K], inv_s fp32 [K], Xq int8 [M][K], x_scale fp32 [M] (all device).
+ * Requirements: M > 0, K > 0, K % 8 == 0. */
+qlin_status sq_smooth_quant_act(const uint16_t* X, const float* inv_s, int M, int K,
+                                int8_t* Xq, float* x_scale, hipStream_t stream);
+
+/* GPU: acc[m][n] = sum_k Xq[m][k] * Wq[n][k] (int32, exact);
+ * Y[m][n] = y_dtype(float(acc) * x_scale[m] * w_scale[n]).
+ * Y device [M][N] with y_dtype QLIN_F16 or QLIN_F32; acc_out, if not NULL,
+ * receives acc (int32 [M][N], device).  Requirements: K % 64 == 0, K <= 131072. */
+qlin_status sq_int8_gemm(const int8_t* Xq, const float* x_scale,
+                         const int8_t* Wq, const float* w_scale,
+                         int M, int N, int K, void* Y, int y_dtype,
+                         int32_t* acc_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLIN_H */

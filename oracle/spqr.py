@@ -139,13 +139,17 @@ def second_level(v):
     return SS, ZS, c.astype(np.uint8), v_hat.astype(F32)
 
 
-def quantize(W, p: float = 0.01):
-    """Full encode.  Returns a dict of the unpacked quantities (codes, statistics, CSR)."""
+def quantize(W, p: float = 0.01, mask=None):
+    """Full encode.  Returns a dict of the unpacked quantities (codes, statistics, CSR).
+
+    ``mask`` may carry an outlier selection made on a larger matrix (rows of a
+    layer are encoded independently once the layer-wide selection is known)."""
     W = np.asarray(W, dtype=F32)
     N, K = W.shape
     if K % BLOCK:
         raise ValueError("K must be a multiple of 256")
-    mask = select_outliers(W, n_outliers(N, K, p))
+    if mask is None:
+        mask = select_outliers(W, n_outliers(N, K, p))
     row_ptr, col_idx, val = build_csr(W, mask)
     R = np.where(mask, F32(0.0), W)
     s, z = first_level(R)
@@ -248,13 +252,23 @@ def pack_stats2(SSs, ZSs, SSz, ZSz):
     return np.stack([SSs, ZSs, SSz, ZSz], axis=-1).astype(np.float16)
 
 
-def encode(W, p: float = 0.01):
+def encode(W, p: float = 0.01, mask=None):
     """fp32 W -> storage dict: codes, stats1, stats2, row_ptr, col_idx, val."""
-    d = quantize(W, p)
+    d = quantize(W, p, mask)
     return dict(codes=pack_codes(d["q"]),
                 stats1=pack_stats1(d["cs"], d["cz"]),
                 stats2=pack_stats2(d["SSs"], d["ZSs"], d["SSz"], d["ZSz"]),
                 row_ptr=d["row_ptr"], col_idx=d["col_idx"], val=d["val"])
+
+
+def encode_rows(W, p: float, rows):
+    """Storage of the given rows of a layer, with the outliers selected over the
+    whole layer (the same bytes the full encode holds for those rows)."""
+    W = np.asarray(W, dtype=F32)
+    N, K = W.shape
+    mask = select_outliers(W, n_outliers(N, K, p))
+    rows = np.asarray(rows)
+    return encode(W[rows], p, mask[rows])
 
 
 # ---------------------------------------------------------------------------

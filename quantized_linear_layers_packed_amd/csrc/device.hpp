@@ -1,0 +1,116 @@
+// Device-side types and helpers for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace qlin {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 128-bit streaming load (marked non-temporal: weights are read exactly once).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& f) {
+  static_assert(sizeof(To) == sizeof(From), "size mismatch");
+  return __builtin_bit_cast(To, f);
+}
+
+// fp32 += a.lo*b.lo + a.hi*b.hi for two packed fp16 / bf16 pairs (v_dot2).
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(bitcast<h2_t>(a), bitcast<h2_t>(b), c, false);
+}
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf2_t>(a), bitcast<bf2_t>(b), c, false);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) { return static_cast<float>(bitcast<_Float16>(h)); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return bitcast<float>(static_cast<uint32_t>(h) << 16); }
+
+// Output element stores for the three output dtypes (round to nearest even).
+enum OutKind { OUT_F16 = 0, OUT_BF16 = 1, OUT_F32 = 2 };
+
+template <int OK>
+__device__ __forceinline__ void store_out(void* Y, size_t idx, float v) {
+  if constexpr (OK == OUT_F16) {
+    static_cast<_Float16*>(Y)[idx] = static_cast<_Float16>(v);
+  } else if constexpr (OK == OUT_BF16) {
+    static_cast<__bf16*>(Y)[idx] = static_cast<__bf16>(v);
+  } else {
+    static_cast<float*>(Y)[idx] = v;
+  }
+}
+
+// Sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// 4-bit codes -> packed 16-bit pairs without per-code conversion.
+//
+// A 32-bit word holds codes n0..n7 (n_j in bits 4j..4j+3).  Four and-or steps
+// give four registers with the pairs (n_j, n_{j+4}), j = 0..3, placed inside
+// the mantissa of a 16-bit float whose exponent makes the code an exact
+// integer offset: fp16 0x6400 | (q << 4) = 1024 + 16 q, bf16 0x4300 | (q << 3)
+// = 128 + 8 q.  A dot product against activation pairs (x_j, x_{j+4}) then
+// yields B * sum(x) + D * sum(x q), from which sum(x q) is recovered with the
+// separately accumulated sum(x).
+
+struct W4F16 {
+  static constexpr uint32_t MAGIC = 0x64006400u, MASK = 0x00F000F0u;
+  static constexpr float B_OVER_D = 64.0f, INV_D = 0.0625f;
+  __device__ __forceinline__ static void unpack(uint32_t w, uint32_t p[4]) {
+    p[0] = ((w << 4) & MASK) | MAGIC;
+    p[1] = (w & MASK) | MAGIC;
+    p[2] = ((w >> 4) & MASK) | MAGIC;
+    p[3] = ((w >> 8) & MASK) | MAGIC;
+  }
+  __device__ __forceinline__ static uint32_t code_of(uint16_t half) { return (half >> 4) & 15u; }
+  __device__ __forceinline__ static float dot(uint32_t a, uint32_t b, float c) { return dot2_f16(a, b, c); }
+};
+
+struct W4BF16 {
+  static constexpr uint32_t MAGIC = 0x43004300u, MASK = 0x00780078u;
+  static constexpr float B_OVER_D = 16.0f, INV_D = 0.125f;
+  __device__ __forceinline__ static void unpack(uint32_t w, uint32_t p[4]) {
+    p[0] = ((w << 3) & MASK) | MAGIC;
+    p[1] = ((w >> 1) & MASK) | MAGIC;
+    p[2] = ((w >> 5) & MASK) | MAGIC;
+    p[3] = ((w >> 9) & MASK) | MAGIC;
+  }
+  __device__ __forceinline__ static uint32_t code_of(uint16_t half) { return (half >> 3) & 15u; }
+  __device__ __forceinline__ static float dot(uint32_t a, uint32_t b, float c) { return dot2_bf16(a, b, c); }
+};
+
+// Activation pairs matching the unpack order above: from 8 consecutive 16-bit
+// values h0..h7 (as four 32-bit words u0..u3 = (h0,h1),(h2,h3),(h4,h5),(h6,h7))
+// build (h0,h4), (h1,h5), (h2,h6), (h3,h7).
+__device__ __forceinline__ void pair_up(const uint32_t u[4], uint32_t P[4]) {
+  P[0] = __builtin_amdgcn_perm(u[2], u[0], 0x05040100u);
+  P[1] = __builtin_amdgcn_perm(u[2], u[0], 0x07060302u);
+  P[2] = __builtin_amdgcn_perm(u[3], u[1], 0x05040100u);
+  P[3] = __builtin_amdgcn_perm(u[3], u[1], 0x07060302u);
+}
+
+}  // namespace qlin

@@ -1,0 +1,52 @@
+// Internal launcher interfaces between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace qlin {
+
+struct W4Args {
+  const void* X;
+  int x_dtype;
+  int M, K, N, G;
+  const uint32_t* qweight;
+  const uint16_t* scales;
+  const uint32_t* qzeros;
+  void* Y;
+  int y_dtype;
+};
+
+// Fused GEMV for M <= 16 (activations staged in LDS).
+size_t w4_gemv_lds_bytes(int M, int K);
+void w4_gemv_launch(const W4Args& a, hipStream_t stream);
+// MFMA GEMM for larger batches.
+void w4_gemm_launch(const W4Args& a, hipStream_t stream);
+void w4_unpack_launch(const uint32_t* qweight, const uint32_t* qzeros, int N, int K, int G,
+                      uint8_t* codes, uint8_t* zeros, hipStream_t stream);
+
+struct SpqrArgs {
+  const uint16_t* X;
+  int M, K, N;
+  const uint32_t* codes;
+  const uint32_t* stats1;
+  const uint16_t* stats2;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const uint16_t* vals;
+  void* Y;
+  int y_dtype;
+};
+
+void spqr_gemv_launch(const SpqrArgs& a, hipStream_t stream);
+void spqr_unpack_launch(const uint32_t* codes, const uint32_t* stats1, int N, int K,
+                        uint8_t* q, uint8_t* cs, uint8_t* cz, hipStream_t stream);
+
+void sq_act_launch(const uint16_t* X, const float* inv_s, int M, int K, int8_t* Xq, float* x_scale,
+                   hipStream_t stream);
+void sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
+                    int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream);
+
+}  // namespace qlin

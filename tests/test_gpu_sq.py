@@ -1,0 +1,85 @@
+"""GPU parity of SmoothQuant W8A8 against the oracle: int8 activations, their
+scales and the int32 accumulators bit for bit; fp16 outputs within tolerance."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import smoothquant as osq
+from quantized_linear_layers_packed_amd import qlin
+from tests.gpu_util import check_close, dev, empty, host, say, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+F16, F32 = qlin.QLIN_F16, qlin.QLIN_F32
+
+
+def gpu_act(X, inv_s):
+    torch = torch_cuda()
+    M, K = X.shape
+    Xq = empty((M, K), torch.int8)
+    xs = empty((M,), torch.float32)
+    qlin.sq_smooth_quant_act(dev(X), dev(inv_s), M, K, Xq, xs)
+    return Xq, xs
+
+
+def gpu_gemm(Xq_d, xs_d, Wq_d, ws_d, M, N, K, y_dtype=F16, want_acc=True):
+    torch = torch_cuda()
+    Y = empty((M, N), torch.float16 if y_dtype == F16 else torch.float32)
+    acc = empty((M, N), torch.int32) if want_acc else None
+    qlin.sq_int8_gemm(Xq_d, xs_d, Wq_d, ws_d, M, N, K, Y, y_dtype, acc)
+    return host(Y).astype(np.float64), (host(acc) if want_acc else None)
+
+
+def test_activation_quantization_is_bit_exact():
+    X = synth.activations("sq_w8a8", 0, 2048)
+    W = synth.layer_weight("sq_w8a8", 1)
+    _, inv_s, _, _ = osq.pack(W, synth.sq_calibration("sq_w8a8", 1), 0.85)
+    X = X.copy()
+    X[5] = 0.0                                        # an all-zero token
+    for M in (1, 3, 256, 512, 2048):
+        say(f"sq act M={M}")
+        Xq_d, xs_d = gpu_act(X[:M], inv_s)
+        Xq_o, xs_o = osq.quantize_act(X[:M], inv_s)
+        assert np.array_equal(host(Xq_d), Xq_o)
+        assert host(xs_d).tobytes() == xs_o.tobytes()
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_full_layer_end_to_end(layer):
+    N, K = synth.WORKLOADS["sq_w8a8"]["layers"][layer]
+    W = synth.layer_weight("sq_w8a8", layer)
+    Xcal = synth.sq_calibration("sq_w8a8", layer)
+    s, inv_s = qlin.sq_compute_smoothing(qlin.sq_act_absmax(Xcal), W, 0.85)
+    Wq, ws = qlin.sq_pack_weight(W, s)
+    S_o, inv_o, Wq_o, ws_o = osq.pack(W, Xcal, 0.85)
+    assert inv_s.tobytes() == inv_o.tobytes() and Wq.tobytes() == Wq_o.tobytes() and ws.tobytes() == ws_o.tobytes()
+    Wq_d, ws_d, inv_d = dev(Wq), dev(ws), dev(inv_s)
+    cols = np.unique(np.r_[0, N - 1, np.random.default_rng(layer).choice(N, 510, replace=False)])
+    for M in (256, 512, 2048):
+        say(f"sq_w8a8 layer {layer} {N}x{K} M={M}")
+        X = synth.activations("sq_w8a8", layer, M)
+        Xq_d, xs_d = gpu_act(X, inv_s)
+        Y, acc = gpu_gemm(Xq_d, xs_d, Wq_d, ws_d, M, N, K)
+        Y_o, Xq_o, xs_o, acc_o = osq.forward(X, inv_o, Wq_o[cols], ws_o[cols])
+        assert np.array_equal(host(Xq_d), Xq_o)
+        assert np.array_equal(acc[:, cols], acc_o), "int32 accumulators differ"
+        check_close(Y[:, cols], Y_o, f"{N}x{K} M={M}")
+
+
+def test_gemm_ragged_shapes():
+    r = np.random.default_rng(11)
+    for (M, N, K) in ((1, 100, 64), (3, 129, 192), (33, 64, 128), (100, 257, 4096), (300, 40, 320)):
+        say(f"sq gemm M={M} N={N} K={K}")
+        Xq = r.integers(-127, 128, size=(M, K)).astype(np.int8)
+        Wq = r.integers(-127, 128, size=(N, K)).astype(np.int8)
+        Xq[0, :] = 127
+        Wq[0, :] = -127
+        # scales sized like real ones (absmax / 127) so that |Y| stays inside fp16 range
+        xs = r.uniform(1e-3, 1e-2, M).astype(np.float32)
+        ws = r.uniform(1e-4, 1e-3, N).astype(np.float32)
+        Y, acc = gpu_gemm(dev(Xq), dev(xs), dev(Wq), dev(ws), M, N, K, F32)
+        acc_o = osq.int_gemm(Xq, Wq)
+        assert np.array_equal(acc, acc_o)
+        check_close(Y, osq.dequant_output(acc_o, xs, ws), "f32 out")
+        Y16, _ = gpu_gemm(dev(Xq), dev(xs), dev(Wq), dev(ws), M, N, K, F16, want_acc=False)
+        check_close(Y16, osq.dequant_output(acc_o, xs, ws), "f16 out")

@@ -1,0 +1,142 @@
+"""GPU parity of the W4 path (fused GEMV for M <= 16, MFMA GEMM above) against
+the fp64 oracle, through the C ABI.  Integer unpacking is compared bit for bit;
+float outputs within max|dY| <= 2e-3 max|Y| and relFrob <= 5e-4."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import metrics
+from oracle import w4 as ow4
+from quantized_linear_layers_packed_amd import qlin
+from tests.gpu_util import check_close, dev, empty, host, say, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+F16, BF16, F32 = qlin.QLIN_F16, qlin.QLIN_BF16, qlin.QLIN_F32
+
+
+def _tdtype(code):
+    torch = torch_cuda()
+    return {F16: torch.float16, BF16: torch.bfloat16, F32: torch.float32}[code]
+
+
+def gpu_w4(X, x_dtype, packed_dev, N, K, G, y_dtype):
+    M = X.shape[0]
+    qw, sc, qz = packed_dev
+    Y = empty((M, N), _tdtype(y_dtype))
+    qlin.qlin_w4_forward(dev(X), x_dtype, M, K, qw, sc, qz, N, G, Y, y_dtype)
+    y = host(Y)
+    if y_dtype == BF16:
+        return y                            # bit patterns
+    return y.astype(np.float64)
+
+
+def dev_pack(W, G):
+    return tuple(dev(a) for a in qlin.qlin_w4_pack(W, G))
+
+
+def f32_to_bf16_bits(a):
+    return synth.f32_to_bf16_bits(np.asarray(a, np.float32))
+
+
+def test_unpack_is_bit_exact():
+    torch = torch_cuda()
+    for (N, K, G) in ((1024, 1024, 128), (64, 11008, 128), (32, 512, 32)):
+        say(f"w4 unpack N={N} K={K} G={G}")
+        W = synth.normal_f32((N, K), 0.02, f"gpu/w4/unpack{K}")
+        qw, sc, qz = qlin.qlin_w4_pack(W, G)
+        codes = empty((N, K), torch.uint8)
+        zeros = empty((N, K // G), torch.uint8)
+        qlin.qlin_w4_unpack(dev(qw), dev(qz), N, K, G, codes, zeros)
+        q_ref, z_ref = ow4.unpack(*ow4.encode(W, G)[::2], K, G)
+        assert np.array_equal(host(codes), q_ref)
+        assert np.array_equal(host(zeros), z_ref)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_small_layer(M):
+    say(f"w4_1k M={M}")
+    W = synth.layer_weight("w4_1k", 0)
+    X = synth.activations("w4_1k", 0, M)
+    Y = gpu_w4(X, F16, dev_pack(W, 128), 1024, 1024, 128, F16)
+    check_close(Y, ow4.forward(X, *ow4.encode(W, 128), 1024, 128), f"w4_1k M={M}")
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_llama7b_gemv_full_layer(layer):
+    N, K = synth.WORKLOADS["w4_llama7b"]["layers"][layer]
+    say(f"w4_llama7b layer {layer} {N}x{K} M=1")
+    W = synth.layer_weight("w4_llama7b", layer)
+    X = synth.activations("w4_llama7b", layer, 1)
+    Y = gpu_w4(X, F16, dev_pack(W, 128), N, K, 128, F16)
+    check_close(Y, ow4.forward(X, *ow4.encode(W, 128), K, 128), f"{N}x{K}")
+
+
+@pytest.mark.parametrize("G", [32, 64, 128, 256])
+@pytest.mark.parametrize("x_dtype", [F16, BF16])
+def test_gemv_ragged_shapes_and_dtypes(G, x_dtype):
+    N, K = 37, 3 * 256
+    W = synth.normal_f32((N, K), 0.02, f"gpu/w4/rag{G}")
+    packed = dev_pack(W, G)
+    ref_st = ow4.encode(W, G)
+    for M in (1, 2, 3, 5, 8, 13, 16):
+        say(f"w4 gemv N={N} K={K} G={G} M={M} x={x_dtype}")
+        if x_dtype == F16:
+            X = synth.x_f16(M, K, f"gpu/w4/ragx{M}")
+        else:
+            X = synth.x_bf16_bits(M, K, f"gpu/w4/ragx{M}")
+        ref = ow4.forward(X, *ref_st, K, G)
+        y32 = gpu_w4(X, x_dtype, packed, N, K, G, F32)
+        check_close(y32, ref, f"M={M} f32 out")
+        check_close(gpu_w4(X, x_dtype, packed, N, K, G, F16), ref, f"M={M} f16 out")
+        yb = gpu_w4(X, x_dtype, packed, N, K, G, BF16)
+        assert np.array_equal(yb, f32_to_bf16_bits(y32)), "bf16 store is not RNE of the fp32 result"
+
+
+def test_gemv_batch_rows_are_independent():
+    W = synth.normal_f32((256, 1024), 0.02, "gpu/w4/indep")
+    packed = dev_pack(W, 128)
+    X = synth.x_f16(16, 1024, "gpu/w4/indepx")
+    full = gpu_w4(X, F16, packed, 256, 1024, 128, F32)
+    for m in (0, 5, 15):
+        one = gpu_w4(X[m:m + 1], F16, packed, 256, 1024, 128, F32)
+        assert np.array_equal(one[0], full[m])
+
+
+@pytest.mark.parametrize("x_dtype", [BF16, F16])
+def test_gemm_ragged_shapes(x_dtype):
+    for (N, K, G) in ((200, 512, 128), (256, 1024, 64), (96, 256, 256), (130, 384, 32)):
+        W = synth.normal_f32((N, K), 0.015, f"gpu/w4/gemm{N}")
+        packed = dev_pack(W, G)
+        st = ow4.encode(W, G)
+        for M in (17, 32, 33, 64, 100, 129, 256, 300):
+            say(f"w4 gemm N={N} K={K} G={G} M={M} x={x_dtype}")
+            X = (synth.x_bf16_bits if x_dtype == BF16 else synth.x_f16)(M, K, f"gpu/w4/gemmx{M}")
+            ref = ow4.forward(X, *st, K, G)
+            y32 = gpu_w4(X, x_dtype, packed, N, K, G, F32)
+            check_close(y32, ref, f"M={M} f32")
+            yb = gpu_w4(X, x_dtype, packed, N, K, G, BF16)
+            assert np.array_equal(yb, f32_to_bf16_bits(y32))
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_llama70b_gemm_full_layer_sampled_rows(layer):
+    """Full 70B-shaped layers at M = 32, 64, 256 (bf16 in, bf16 out): the kernel's
+    fp32 result meets the tolerance on 384 sampled output columns, and its bf16
+    output is exactly the RNE rounding of that fp32 result everywhere."""
+    N, K = synth.WORKLOADS["w4_llama70b"]["layers"][layer]
+    W = synth.layer_weight("w4_llama70b", layer)
+    packed = dev_pack(W, 128)
+    rows = np.unique(np.r_[0, N - 1, np.random.default_rng(layer).choice(N, 382, replace=False)])
+    st = ow4.encode(W[rows], 128)
+    del W
+    for M in (32, 64, 256):
+        say(f"w4_llama70b layer {layer} {N}x{K} M={M}")
+        X = synth.activations("w4_llama70b", layer, M)
+        y32 = gpu_w4(X, BF16, packed, N, K, 128, F32)
+        check_close(y32[:, rows], ow4.forward(X, *st, K, 128), f"{N}x{K} M={M}")
+        yb = gpu_w4(X, BF16, packed, N, K, 128, BF16)
+        assert np.array_equal(yb, f32_to_bf16_bits(y32))
+        ref_b = metrics.bf16_bits_to_f64(f32_to_bf16_bits(ow4.forward(X, *st, K, 128)))
+        mism = np.mean(yb[:, rows] != f32_to_bf16_bits(ref_b))
+        say(f"  bf16 outputs differing from bf16(oracle): {mism:.2e}")

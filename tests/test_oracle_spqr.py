@@ -179,3 +179,17 @@ def test_bits_per_parameter_in_the_pages_range():
     assert len(st["val"]) == 443023
     dense_bits = 8.0 * (st["codes"].nbytes + st["stats1"].nbytes + st["stats2"].nbytes) / 6656 ** 2
     assert dense_bits == 3.625
+
+
+def test_row_subset_encode_equals_rows_of_full_encode():
+    W = synth.student_t3_f32((48, 512), 0.02, "pin/spqr/rows")
+    full = spqr.encode(W, 0.01)
+    rows = np.array([0, 5, 17, 47])
+    sub = spqr.encode_rows(W, 0.01, rows)
+    for k in ("codes", "stats1", "stats2"):
+        assert np.array_equal(sub[k], full[k][rows])
+    rp = full["row_ptr"]
+    for i, r in enumerate(rows):
+        a, b = sub["row_ptr"][i], sub["row_ptr"][i + 1]
+        assert np.array_equal(sub["col_idx"][a:b], full["col_idx"][rp[r]:rp[r + 1]])
+        assert np.array_equal(sub["val"][a:b], full["val"][rp[r]:rp[r + 1]])
