@@ -197,6 +197,18 @@ qlin_status sq_int8_gemm(const int8_t* Xq, const float* x_scale,
                          int M, int N, int K, void* Y, int y_dtype,
                          int32_t* acc_out, hipStream_t stream);
 
+/* ======================================================================== */
+/* Measurement aid                                                           */
+/* ======================================================================== */
+/* Plain streaming read of `bytes` (multiple of 16) from device buffer `buf`
+ * with 16-byte vector loads: `grid` workgroups of 256 threads, `unroll` (1, 4
+ * or 8) loads in flight per thread, optionally marked non-temporal.  Writes one
+ * XOR word per workgroup to out[grid] (device) so the loads are kept.  It is the
+ * achievable-bandwidth reference for the memory-bound kernels above (not part
+ * of the layer computation). */
+qlin_status qlin_stream_read(const void* buf, size_t bytes, int grid, int unroll, int nontemporal,
+                             uint32_t* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,7 +49,7 @@ qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
   QLIN_TRY(need_aligned(fn, "qzeros", qzeros));
   QLIN_TRY(need_aligned(fn, "Y", Y));
   W4Args a{X, x_dtype, M, K, N, G, qweight, scales, qzeros, Y, y_dtype};
-  if (M <= 16 && w4_gemv_lds_bytes(M, K) <= 64 * 1024) {
+  if (w4_gemv_supported(M, K, G)) {
     w4_gemv_launch(a, stream);
   } else {
     w4_gemm_launch(a, stream);

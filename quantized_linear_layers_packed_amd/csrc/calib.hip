@@ -1,0 +1,62 @@
+// Measurement aid: a plain streaming read of a device buffer, the reference
+// against which the GEMV kernels' bandwidth is judged.  Each thread reads 16-byte
+// vectors (coalesced, 64 lanes x 16 B per instruction) and folds them with XOR;
+// one word per workgroup is written so the loads cannot be removed.
+
+#include "common.hpp"
+#include "device.hpp"
+
+namespace qlin {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int U, bool NT>
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ p, size_t n16,
+                                                               uint32_t* __restrict__ out) {
+  __shared__ uint32_t red[kThreads / 64];
+  uint32_t acc = 0;
+  const size_t stride = static_cast<size_t>(gridDim.x) * kThreads * U;
+  for (size_t base = static_cast<size_t>(blockIdx.x) * kThreads * U + threadIdx.x; base < n16; base += stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = base + static_cast<size_t>(u) * kThreads;
+      if (i < n16) v[u] = NT ? load_stream16(p + i) : p[i];
+      else v[u] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+}  // namespace
+}  // namespace qlin
+
+using namespace qlin;
+
+extern "C" qlin_status qlin_stream_read(const void* buf, size_t bytes, int grid, int unroll, int nontemporal,
+                                        uint32_t* out, hipStream_t stream) {
+  clear_error();
+  if (!buf || !out || bytes == 0 || bytes % 16 != 0 || grid <= 0)
+    return fail(QLIN_EINVAL, "qlin_stream_read: need non-NULL buffers, bytes % 16 == 0, grid > 0");
+  if (!aligned16(buf)) return fail(QLIN_EALIGN, "qlin_stream_read: buf is not 16-byte aligned");
+  const size_t n16 = bytes / 16;
+  const uint4* p = static_cast<const uint4*>(buf);
+  if (unroll <= 1) {
+    if (nontemporal) hipLaunchKernelGGL((stream_read_kernel<1, true>), dim3(grid), dim3(kThreads), 0, stream, p, n16, out);
+    else hipLaunchKernelGGL((stream_read_kernel<1, false>), dim3(grid), dim3(kThreads), 0, stream, p, n16, out);
+  } else if (unroll <= 4) {
+    if (nontemporal) hipLaunchKernelGGL((stream_read_kernel<4, true>), dim3(grid), dim3(kThreads), 0, stream, p, n16, out);
+    else hipLaunchKernelGGL((stream_read_kernel<4, false>), dim3(grid), dim3(kThreads), 0, stream, p, n16, out);
+  } else {
+    if (nontemporal) hipLaunchKernelGGL((stream_read_kernel<8, true>), dim3(grid), dim3(kThreads), 0, stream, p, n16, out);
+    else hipLaunchKernelGGL((stream_read_kernel<8, false>), dim3(grid), dim3(kThreads), 0, stream, p, n16, out);
+  }
+  return check_launch("qlin_stream_read");
+}

@@ -77,14 +77,24 @@ __device__ __forceinline__ float wave_max(float v) {
 // yields B * sum(x) + D * sum(x q), from which sum(x q) is recovered with the
 // separately accumulated sum(x).
 
+// (a & m) | c in one v_and_or_b32.  gfx9 reads at most one scalar operand per
+// VALU instruction, so the mask is kept in a VGPR and the magic constant is the
+// scalar operand; left to itself the compiler splits this into and + or.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "s"(c));
+  return r;
+}
+
 struct W4F16 {
   static constexpr uint32_t MAGIC = 0x64006400u, MASK = 0x00F000F0u;
   static constexpr float B_OVER_D = 64.0f, INV_D = 0.0625f;
   __device__ __forceinline__ static void unpack(uint32_t w, uint32_t p[4]) {
-    p[0] = ((w << 4) & MASK) | MAGIC;
-    p[1] = (w & MASK) | MAGIC;
-    p[2] = ((w >> 4) & MASK) | MAGIC;
-    p[3] = ((w >> 8) & MASK) | MAGIC;
+    const uint32_t mask = MASK;
+    p[0] = and_or(w << 4, mask, MAGIC);
+    p[1] = and_or(w, mask, MAGIC);
+    p[2] = and_or(w >> 4, mask, MAGIC);
+    p[3] = and_or(w >> 8, mask, MAGIC);
   }
   __device__ __forceinline__ static uint32_t code_of(uint16_t half) { return (half >> 4) & 15u; }
   __device__ __forceinline__ static float dot(uint32_t a, uint32_t b, float c) { return dot2_f16(a, b, c); }
@@ -94,10 +104,11 @@ struct W4BF16 {
   static constexpr uint32_t MAGIC = 0x43004300u, MASK = 0x00780078u;
   static constexpr float B_OVER_D = 16.0f, INV_D = 0.125f;
   __device__ __forceinline__ static void unpack(uint32_t w, uint32_t p[4]) {
-    p[0] = ((w << 3) & MASK) | MAGIC;
-    p[1] = ((w >> 1) & MASK) | MAGIC;
-    p[2] = ((w >> 5) & MASK) | MAGIC;
-    p[3] = ((w >> 9) & MASK) | MAGIC;
+    const uint32_t mask = MASK;
+    p[0] = and_or(w << 3, mask, MAGIC);
+    p[1] = and_or(w >> 1, mask, MAGIC);
+    p[2] = and_or(w >> 5, mask, MAGIC);
+    p[3] = and_or(w >> 9, mask, MAGIC);
   }
   __device__ __forceinline__ static uint32_t code_of(uint16_t half) { return (half >> 3) & 15u; }
   __device__ __forceinline__ static float dot(uint32_t a, uint32_t b, float c) { return dot2_bf16(a, b, c); }

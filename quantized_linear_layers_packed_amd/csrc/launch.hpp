@@ -21,6 +21,7 @@ struct W4Args {
 
 // Fused GEMV for M <= 16 (activations staged in LDS).
 size_t w4_gemv_lds_bytes(int M, int K);
+bool w4_gemv_supported(int M, int K, int G);
 void w4_gemv_launch(const W4Args& a, hipStream_t stream);
 // MFMA GEMM for larger batches.
 void w4_gemm_launch(const W4Args& a, hipStream_t stream);

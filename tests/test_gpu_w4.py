@@ -72,15 +72,18 @@ def test_llama7b_gemv_full_layer(layer):
     check_close(Y, ow4.forward(X, *ow4.encode(W, 128), K, 128), f"{N}x{K}")
 
 
+@pytest.mark.parametrize("K", [3 * 256, 4096 + 512])
 @pytest.mark.parametrize("G", [32, 64, 128, 256])
 @pytest.mark.parametrize("x_dtype", [F16, BF16])
-def test_gemv_ragged_shapes_and_dtypes(G, x_dtype):
-    N, K = 37, 3 * 256
+def test_gemv_ragged_shapes_and_dtypes(G, x_dtype, K):
+    N = 37
     W = synth.normal_f32((N, K), 0.02, f"gpu/w4/rag{G}")
     packed = dev_pack(W, G)
     ref_st = ow4.encode(W, G)
     for M in (1, 2, 3, 5, 8, 13, 16):
         say(f"w4 gemv N={N} K={K} G={G} M={M} x={x_dtype}")
+        if K > 1024 and M not in (1, 2, 16):
+            continue
         if x_dtype == F16:
             X = synth.x_f16(M, K, f"gpu/w4/ragx{M}")
         else:
@@ -140,3 +143,15 @@ def test_llama70b_gemm_full_layer_sampled_rows(layer):
         ref_b = metrics.bf16_bits_to_f64(f32_to_bf16_bits(ow4.forward(X, *st, K, 128)))
         mism = np.mean(yb[:, rows] != f32_to_bf16_bits(ref_b))
         say(f"  bf16 outputs differing from bf16(oracle): {mism:.2e}")
+
+
+def test_small_batch_beyond_the_gemv_range_uses_the_gemm():
+    """M <= 16 with K above the GEMV's single-pass range runs the MFMA GEMM."""
+    N, K = 64, 20480
+    W = synth.normal_f32((N, K), 0.02, "gpu/w4/longk")
+    packed = dev_pack(W, 128)
+    st = ow4.encode(W, 128)
+    for M in (1, 5):
+        say(f"w4 long-K N={N} K={K} M={M}")
+        X = synth.x_f16(M, K, f"gpu/w4/longkx{M}")
+        check_close(gpu_w4(X, F16, packed, N, K, 128, F32), ow4.forward(X, *st, K, 128), f"M={M}")
