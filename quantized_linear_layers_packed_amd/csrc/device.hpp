@@ -53,6 +53,19 @@ __device__ __forceinline__ void store_out(void* Y, size_t idx, float v) {
   }
 }
 
+// XCD-aware tile order.  Workgroups are dispatched round-robin over the 8 XCDs
+// (each with its own L2), so linear workgroup b lands on XCD b % 8.  This maps
+// b to a tile index such that every XCD owns one contiguous range of tiles;
+// with tiles numbered M-block fastest, the workgroups of one XCD share weight
+// columns and neighbouring activation rows in their L2.  Bijective on [0, T).
+__device__ __forceinline__ int xcd_tile(int b, int T) {
+  constexpr int X = 8;
+  const int per = T / X, rem = T % X;
+  const int xcd = b % X, slot = b / X;
+  const int base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  return base + slot;
+}
+
 // Sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

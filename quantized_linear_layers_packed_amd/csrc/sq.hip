@@ -14,9 +14,9 @@
 //
 // GEMM kernel: v_mfma_i32_32x32x32_i8, exact int32 accumulation
 // (|acc| <= K * 127^2 < 2^31 for K <= 131072).  The token tile of Xq is staged
-// in LDS per 128-wide K step and shared by four waves, each of which streams its
-// own 32 weight rows straight from HBM into MFMA operand registers (16 int8 per
-// lane per step).  Epilogue: float(acc) * x_scale[m] * w_scale[n], rounded once.
+// in LDS per 128-wide K step (double buffered) and shared by the waves; each
+// wave streams its own weight rows from HBM into MFMA operand registers one K
+// step ahead.  Epilogue: float(acc) * x_scale[m] * w_scale[n], rounded once.
 
 #include "common.hpp"
 #include "device.hpp"
@@ -77,79 +77,154 @@ __global__ __launch_bounds__(kActThreads) void sq_act_kernel(const uint16_t* __r
   }
 }
 
-constexpr int kGemmThreads = 256;   // 4 waves x 32 output columns
-constexpr int kBK = 128;            // K bytes staged per iteration (4 MFMA steps)
+constexpr int kGemmThreads = 256;   // 4 waves
+constexpr int kBK = 128;            // K bytes per pipeline step (4 MFMA steps)
 
-template <int TM, int OUTK>
+// Tiles of 32 x 32 outputs; waves WM x WN, each TM x TN tiles.  Within one
+// 128-byte K step, MFMA step st and lane half h use bytes 64h + 16st .. +15 of
+// both operands (a fixed permutation of k, identical for A and B), so each lane
+// streams 64 contiguous bytes of its weight row per K step.  The next K step's
+// weights are loaded into registers and its activation tile into the second
+// LDS buffer while the current one is multiplied.
+template <int WM, int WN, int TM, int TN, int OUTK>
 __global__ __launch_bounds__(kGemmThreads) void sq_gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int8_t* __restrict__ Wq, const float* __restrict__ w_scale,
     int M, int N, int K, void* __restrict__ Y, int32_t* __restrict__ acc_out) {
-  constexpr int BM = 32 * TM;
-  constexpr int ROW = kBK + 16;      // LDS row stride in bytes (padding against bank conflicts)
-  __shared__ __attribute__((aligned(16))) int8_t As[BM * ROW];
+  static_assert(WM * WN == 4, "four waves");
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  constexpr int ROW = kBK + 16;                          // LDS row stride in bytes
+  constexpr int PIECES = BM * kBK / 16;                  // 16-byte activation pieces per K step
+  constexpr int APT = (PIECES + kGemmThreads - 1) / kGemmThreads;
+  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * ROW];
 
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int wm = wv / WN, wn = wv % WN;
   const int col = lane & 31, half = lane >> 5;
-  const int m0 = blockIdx.y * BM;
-  const int n = blockIdx.x * 128 + wv * 32 + col;
-  const bool n_ok = n < N;
-  const int8_t* wrow = Wq + static_cast<size_t>(n_ok ? n : 0) * K;
+  const int MB = (M + BM - 1) / BM;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (tile % MB) * BM;
+  const int n0 = (tile / MB) * BN + wn * TN * 32;
+  const int nk = (K + kBK - 1) / kBK;
 
-  i32x16_t acc[TM];
+  const int8_t* wrow[TN];
+  bool nok[TN];
 #pragma unroll
-  for (int t = 0; t < TM; ++t) acc[t] = i32x16_t{};
+  for (int t = 0; t < TN; ++t) {
+    const int n = n0 + 32 * t + col;
+    nok[t] = n < N;
+    wrow[t] = Wq + static_cast<size_t>(nok[t] ? n : 0) * K;
+  }
 
-  for (int k0 = 0; k0 < K; k0 += kBK) {
-    __syncthreads();
-    for (int it = threadIdx.x; it < BM * (kBK / 16); it += kGemmThreads) {
-      const int r = it / (kBK / 16), c = it - r * (kBK / 16);
+  uint4 av[APT];
+  uint4 bq[TN][4];
+  auto load_a = [&](int kk) {
+#pragma unroll
+    for (int p = 0; p < APT; ++p) {
+      const int piece = tid + p * kGemmThreads;
+      const int r = piece / (kBK / 16), c = piece - r * (kBK / 16);
       const int m = m0 + r;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (m < M && k0 + 16 * c < K) v = *reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(m) * K + k0 + 16 * c);
-      *reinterpret_cast<uint4*>(As + r * ROW + 16 * c) = v;
+      const int k = kk * kBK + 16 * c;
+      av[p] = (piece < PIECES && m < M && k < K)
+                  ? *reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(m) * K + k)
+                  : make_uint4(0u, 0u, 0u, 0u);
     }
-    __syncthreads();
-    const int steps = min(kBK, K - k0) / 32;
+  };
+  auto store_a = [&](int buf) {
 #pragma unroll
-    for (int st = 0; st < kBK / 32; ++st) {
-      if (st < steps) {
-        i32x4_t b = i32x4_t{};
-        if (n_ok) b = *reinterpret_cast<const i32x4_t*>(wrow + k0 + 32 * st + 16 * half);
+    for (int p = 0; p < APT; ++p) {
+      const int piece = tid + p * kGemmThreads;
+      if (piece < PIECES) {
+        const int r = piece / (kBK / 16), c = piece - r * (kBK / 16);
+        *reinterpret_cast<uint4*>(&As[buf][r * ROW + 16 * c]) = av[p];
+      }
+    }
+  };
+  auto load_b = [&](int kk) {
 #pragma unroll
-        for (int t = 0; t < TM; ++t) {
-          const i32x4_t a = *reinterpret_cast<const i32x4_t*>(As + (32 * t + col) * ROW + 32 * st + 16 * half);
-          acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[t], 0, 0, 0);
+    for (int t = 0; t < TN; ++t) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int k = kk * kBK + 64 * half + 16 * st;
+        bq[t][st] = (nok[t] && k < K) ? load_stream16(wrow[t] + k) : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+
+  i32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < TN; ++t) acc[i][t] = i32x16_t{};
+
+  load_a(0);
+  load_b(0);
+  store_a(0);
+  __syncthreads();
+
+  for (int kk = 0; kk < nk; ++kk) {
+    const int buf = kk & 1;
+    uint4 bcur[TN][4];
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) bcur[t][st] = bq[t][st];
+    if (kk + 1 < nk) {
+      load_a(kk + 1);
+      load_b(kk + 1);
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = (wm * TM + i) * 32 + col;
+        const i32x4_t a = *reinterpret_cast<const i32x4_t*>(&As[buf][r * ROW + 64 * half + 16 * st]);
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+          const i32x4_t b = bitcast<i32x4_t>(bcur[t][st]);
+          acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[i][t], 0, 0, 0);
         }
       }
     }
+    if (kk + 1 < nk) {
+      store_a(buf ^ 1);
+      __syncthreads();
+    }
   }
 
-  if (!n_ok) return;
-  const float ws = w_scale[n];
 #pragma unroll
-  for (int t = 0; t < TM; ++t) {
+  for (int t = 0; t < TN; ++t) {
+    if (!nok[t]) continue;
+    const int n = n0 + 32 * t + col;
+    const float ws = w_scale[n];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (m < M) {
-        const size_t idx = static_cast<size_t>(m) * N + n;
-        store_out<OUTK>(Y, idx, static_cast<float>(acc[t][r]) * x_scale[m] * ws);
-        if (acc_out) acc_out[idx] = acc[t][r];
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + (wm * TM + i) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (m < M) {
+          const size_t idx = static_cast<size_t>(m) * N + n;
+          store_out<OUTK>(Y, idx, static_cast<float>(acc[i][t][r]) * x_scale[m] * ws);
+          if (acc_out) acc_out[idx] = acc[i][t][r];
+        }
       }
     }
   }
 }
 
-template <int TM>
+template <int WM, int WN, int TM, int TN>
 void gemm_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
             void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
-  dim3 grid((N + 127) / 128, (M + 32 * TM - 1) / (32 * TM));
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  dim3 grid(((N + BN - 1) / BN) * ((M + BM - 1) / BM));
   if (y_dtype == QLIN_F32)
-    hipLaunchKernelGGL((sq_gemm_kernel<TM, OUT_F32>), grid, dim3(kGemmThreads), 0, stream, Xq, xsc, Wq, wsc, M, N, K, Y, acc_out);
+    hipLaunchKernelGGL((sq_gemm_kernel<WM, WN, TM, TN, OUT_F32>), grid, dim3(kGemmThreads), 0, stream,
+                       Xq, xsc, Wq, wsc, M, N, K, Y, acc_out);
   else
-    hipLaunchKernelGGL((sq_gemm_kernel<TM, OUT_F16>), grid, dim3(kGemmThreads), 0, stream, Xq, xsc, Wq, wsc, M, N, K, Y, acc_out);
+    hipLaunchKernelGGL((sq_gemm_kernel<WM, WN, TM, TN, OUT_F16>), grid, dim3(kGemmThreads), 0, stream,
+                       Xq, xsc, Wq, wsc, M, N, K, Y, acc_out);
 }
 
 }  // namespace
@@ -161,9 +236,13 @@ void sq_act_launch(const uint16_t* X, const float* inv_s, int M, int K, int8_t* 
 
 void sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
                     int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
-  if (M <= 32) gemm_t<1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-  else if (M <= 64) gemm_t<2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-  else gemm_t<4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+  // Largest tile that still gives every CU a workgroup; small batches use one
+  // 32-row tile with the four waves side by side along N.
+  auto wgs = [&](int bm, int bn) { return static_cast<long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (M <= 32) gemm_t<1, 4, 1, 1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+  else if (wgs(128, 128) >= 256) gemm_t<2, 2, 2, 2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+  else if (wgs(64, 128) >= 256) gemm_t<2, 2, 1, 2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+  else gemm_t<2, 2, 1, 1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
 }
 
 }  // namespace qlin

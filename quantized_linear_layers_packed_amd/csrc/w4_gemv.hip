@@ -108,6 +108,8 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) v4[i] = src[i];
       }
+      // sum of the 32 activations: dot products with (1, 1) pairs
+      const uint32_t ones = XBF16 ? 0x3F803F80u : 0x3C003C00u;
       float sum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -116,13 +118,7 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
         pair_up(u, P);
         xl[(static_cast<size_t>(m) * 4 + i) * C + c] = make_uint4(P[0], P[1], P[2], P[3]);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          if constexpr (XBF16) {
-            sum += bf16_bits_to_f32(static_cast<uint16_t>(u[jj])) + bf16_bits_to_f32(static_cast<uint16_t>(u[jj] >> 16));
-          } else {
-            sum += f16_bits_to_f32(static_cast<uint16_t>(u[jj])) + f16_bits_to_f32(static_cast<uint16_t>(u[jj] >> 16));
-          }
-        }
+        for (int jj = 0; jj < 4; ++jj) sum = Codec::dot(u[jj], ones, sum);
       }
       xs[m * C + c] = sum;
     }
