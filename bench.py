@@ -43,6 +43,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-paths", action="store_true", help="headline workload only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--summarize", metavar="DIR",
+                   help="summarize rocprofv3 csv output under DIR (trace/, fetch/, write/) and exit")
+    p.add_argument("--calibrate", action="store_true",
+                   help="first run a plain 256 MiB device copy (known traffic) 5 times, for counter scaling")
     return p.parse_args()
 
 
@@ -255,8 +259,105 @@ def cpu_baseline(synth):
                       f"(numpy fp64 decode + matvec), {dt * 1e3:.0f} ms per step"}
 
 
+# ---------------------------------------------------------------------------
+# profile summaries (rocprofv3 csv -> text) and the counter-based traffic figure
+
+GEMV_SOURCES = ("quantized_linear_layers_packed_amd/csrc/w4_gemv.hip",
+                "quantized_linear_layers_packed_amd/csrc/device.hpp")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "w4_gemv_w4_llama7b_m1_counters.txt")
+COPY_BYTES = 256 << 20
+
+
+def source_hash(paths=GEMV_SOURCES):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def short_name(name):
+    base = name.replace("(anonymous namespace)::", "").replace("qlin::", "")
+    if base.startswith("void "):
+        base = base[5:]
+    return base.split("(")[0][:90]
+
+
+def summarize(d):
+    import csv
+    from collections import defaultdict
+    out = []
+    tr = os.path.join(d, "trace", "run_kernel_trace.csv")
+    if os.path.exists(tr):
+        groups = defaultdict(list)
+        with open(tr) as f:
+            for r in csv.DictReader(f):
+                key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["LDS_Block_Size"]))
+                groups[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        out.append("kernel trace (rocprofv3 --kernel-trace --stats): per kernel and launch shape")
+        out.append(f"{'kernel':92s} {'grid':>9s} {'lds':>6s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s}")
+        for (k, g, l), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            if "spin_kernel" in k or "FillFunctor" in k:
+                continue
+            out.append(f"{k:92s} {g:9d} {l:6d} {len(v):6d} {np.mean(v) / 1e3:9.3f} {np.min(v) / 1e3:9.3f}")
+    cnt = {}
+    for c in ("fetch", "write"):
+        p = os.path.join(d, c, "run_counter_collection.csv")
+        if not os.path.exists(p):
+            continue
+        groups = defaultdict(list)
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]), int(r["LDS_Block_Size"]))
+                groups[key].append(float(r["Counter_Value"]))
+        cnt[c] = {k: float(np.mean(v)) for k, v in groups.items()}
+    if cnt:
+        out.append("")
+        out.append("counters (rocprofv3 --pmc FETCH_SIZE / --pmc WRITE_SIZE, KiB per dispatch, mean)")
+        scale = {}
+        for c in cnt:
+            copy = [v for k, v in cnt[c].items() if k[0].startswith("stream_copy_kernel")]
+            scale[c] = (COPY_BYTES / 1024.0) / copy[0] if copy else None
+            out.append(f"  {c}: plain copy of {COPY_BYTES >> 20} MiB reads {copy[0] if copy else float('nan'):.1f} KiB"
+                       f" -> scale {scale[c]:.4f}")
+        keys = sorted(set().union(*[set(v) for v in cnt.values()]))
+        for k in keys:
+            if "FillFunctor" in k[0]:
+                continue
+            f_ = cnt.get("fetch", {}).get(k, float("nan"))
+            w_ = cnt.get("write", {}).get(k, float("nan"))
+            out.append(f"  {k[0]:90s} grid {k[1]:9d} lds {k[2]:6d}  fetch {f_:12.1f}  write {w_:10.1f}")
+        gemv = [k for k in keys if k[0].startswith("w4_gemv_kernel")]
+        if gemv and scale.get("fetch") and scale.get("write"):
+            fb = sum(cnt["fetch"][k] for k in gemv) * 1024 * scale["fetch"]
+            wb = sum(cnt["write"][k] for k in gemv) * 1024 * scale["write"]
+            rec = {"kernel": "w4_gemv_kernel", "launch_shapes": len(gemv), "fetch_bytes_per_step": round(fb),
+                   "write_bytes_per_step": round(wb), "scale_fetch": scale["fetch"], "scale_write": scale["write"],
+                   "source_sha256": source_hash()}
+            out.append("COUNTERS_JSON: " + json.dumps(rec))
+    return "\n".join(out)
+
+
+def counter_traffic():
+    """Calibrated HBM bytes per step of the W4 GEMV from the committed counter
+    summary, or None when the summary is missing or the kernel source changed."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            line = [l for l in f if l.startswith("COUNTERS_JSON: ")][-1]
+        rec = json.loads(line[len("COUNTERS_JSON: "):])
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash():
+        return None
+    return rec["fetch_bytes_per_step"] + rec["write_bytes_per_step"]
+
+
 def main():
     args = parse()
+    if args.summarize:
+        print(summarize(args.summarize))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
@@ -266,6 +367,15 @@ def main():
     import synth
     from quantized_linear_layers_packed_amd import qlin
     torch.cuda.set_device(0)
+
+    if args.calibrate:
+        nb = 256 << 20
+        src = torch.ones(nb // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            qlin.qlin_stream_copy(dst, src, nb)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- headline: W4 GEMV, Llama-7B-shaped layers, M = 1
     layers = w4_layers(torch, qlin, synth, "w4_llama7b", 1)
@@ -298,8 +408,9 @@ def main():
                                "group 128, M=1, fp16 in/out",
                    "global_batch": 1, "weight_copies_rotated": rot, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "w4_gemv_kernel", "per_layer": per_layer},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
+                     "kernel": "w4_gemv_kernel", "per": "step of three launches (bytes per step / kernel time per step)",
+                     "algorithmic_bytes": step_bytes, "per_layer": per_layer},
     }
 
     if not args.no_paths:

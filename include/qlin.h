@@ -209,6 +209,11 @@ qlin_status sq_int8_gemm(const int8_t* Xq, const float* x_scale,
 qlin_status qlin_stream_read(const void* buf, size_t bytes, int grid, int unroll, int nontemporal,
                              uint32_t* out, hipStream_t stream);
 
+/* Plain device-to-device copy of `bytes` (multiple of 16, both buffers 16-byte
+ * aligned) with 16-byte loads and stores: a kernel of known traffic (bytes read
+ * + bytes written) against which hardware fetch/write counters are scaled. */
+qlin_status qlin_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

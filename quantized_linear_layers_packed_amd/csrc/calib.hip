@@ -1,7 +1,10 @@
-// Measurement aid: a plain streaming read of a device buffer, the reference
-// against which the GEMV kernels' bandwidth is judged.  Each thread reads 16-byte
+// Measurement aids: a plain streaming read of a device buffer (the achievable
+// bandwidth reference for the memory-bound kernels) and a plain copy (the
+// known-size reference that scales the hardware byte counters).  Each thread reads 16-byte
 // vectors (coalesced, 64 lanes x 16 B per instruction) and folds them with XOR;
 // one word per workgroup is written so the loads cannot be removed.
+
+#include <algorithm>
 
 #include "common.hpp"
 #include "device.hpp"
@@ -35,6 +38,12 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
   if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
+__global__ __launch_bounds__(kThreads) void stream_copy_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                                               size_t n16) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
 }  // namespace
 }  // namespace qlin
 
@@ -59,4 +68,16 @@ extern "C" qlin_status qlin_stream_read(const void* buf, size_t bytes, int grid,
     else hipLaunchKernelGGL((stream_read_kernel<8, false>), dim3(grid), dim3(kThreads), 0, stream, p, n16, out);
   }
   return check_launch("qlin_stream_read");
+}
+
+extern "C" qlin_status qlin_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  clear_error();
+  if (!dst || !src || bytes == 0 || bytes % 16 != 0)
+    return fail(QLIN_EINVAL, "qlin_stream_copy: need non-NULL buffers and bytes % 16 == 0");
+  if (!aligned16(dst) || !aligned16(src)) return fail(QLIN_EALIGN, "qlin_stream_copy: buffers must be 16-byte aligned");
+  const size_t n16 = bytes / 16;
+  const int grid = static_cast<int>(std::min<size_t>((n16 + kThreads - 1) / kThreads, 4096));
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(grid), dim3(kThreads), 0, stream, static_cast<uint4*>(dst),
+                     static_cast<const uint4*>(src), n16);
+  return check_launch("qlin_stream_copy");
 }

@@ -43,7 +43,7 @@ EXPORTS = (
     "qlin_w4_sizes", "qlin_w4_pack", "qlin_w4_forward", "qlin_w4_unpack",
     "spqr_sizes", "spqr_pack", "spqr_forward", "spqr_unpack",
     "sq_act_absmax", "sq_compute_smoothing", "sq_pack_weight", "sq_smooth_quant_act", "sq_int8_gemm",
-    "qlin_stream_read",
+    "qlin_stream_read", "qlin_stream_copy",
 )
 
 _vp, _i, _i64, _sz, _d = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.c_double
@@ -65,6 +65,7 @@ _sigs = {
     "sq_smooth_quant_act": ([_vp, _vp, _i, _i, _vp, _vp, _vp], _i),
     "sq_int8_gemm": ([_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp], _i),
     "qlin_stream_read": ([_vp, _sz, _i, _i, _i, _vp, _vp], _i),
+    "qlin_stream_copy": ([_vp, _vp, _sz, _vp], _i),
 }
 for _name, (_args, _res) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -238,3 +239,7 @@ def sq_int8_gemm(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype=QLIN_F16, acc_out
 def qlin_stream_read(buf, nbytes, grid, unroll, nontemporal, out, stream=None):
     _check(_lib.qlin_stream_read(_ptr(buf), nbytes, grid, unroll, int(bool(nontemporal)), _ptr(out),
                                  _stream(stream)))
+
+
+def qlin_stream_copy(dst, src, nbytes, stream=None):
+    _check(_lib.qlin_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)))
