@@ -99,6 +99,13 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   return r;
 }
 
+// Same with the or-operand in a VGPR.
+__device__ __forceinline__ uint32_t and_or_v(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+  return r;
+}
+
 struct W4F16 {
   static constexpr uint32_t MAGIC = 0x64006400u, MASK = 0x00F000F0u;
   static constexpr float B_OVER_D = 64.0f, INV_D = 0.0625f;

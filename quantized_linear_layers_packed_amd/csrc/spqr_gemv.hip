@@ -30,20 +30,21 @@ namespace qlin {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kLPR = 16;                 // lanes per output row
-constexpr int kRowsPerWG = kThreads / kLPR;
-constexpr size_t kLdsBudget = 48 * 1024;
+constexpr int kWaves = 8;                // output rows (one per wavefront) per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr size_t kLdsBudget = 60 * 1024;
 
-// fp16 pair (1024 + 8 c_lo, 1024 + 8 c_hi) from field i of both halves of w.
+// fp16 pair (1024 + 8 c_lo, 1024 + 8 c_hi) from field i of both halves of w:
+// a shift and one v_and_or_b32.
 __device__ __forceinline__ uint32_t field_pair(uint32_t w, int i) {
-  constexpr uint32_t MASK = 0x00380038u, MAGIC = 0x64006400u;
+  constexpr uint32_t MAGIC = 0x64006400u;
+  const uint32_t mask = 0x00380038u;
   switch (i) {
-    case 0: return ((w << 3) & MASK) | MAGIC;
-    case 1: return (w & MASK) | MAGIC;
-    case 2: return ((w >> 3) & MASK) | MAGIC;
-    case 3: return ((w >> 6) & MASK) | MAGIC;
-    default: return ((w >> 9) & MASK) | MAGIC;
+    case 0: return and_or(w << 3, mask, MAGIC);
+    case 1: return and_or(w, mask, MAGIC);
+    case 2: return and_or(w >> 3, mask, MAGIC);
+    case 3: return and_or(w >> 6, mask, MAGIC);
+    default: return and_or(w >> 9, mask, MAGIC);
   }
 }
 
@@ -55,7 +56,10 @@ __device__ __forceinline__ void unpack_chunk(uint32_t w0, uint32_t w1, uint32_t 
     p[5 + i] = field_pair(w1, i);
     p[10 + i] = field_pair(w2, i);
   }
-  p[15] = ((w0 >> 12) & 0x00080008u) | ((w1 >> 11) & 0x00100010u) | ((w2 >> 10) & 0x00200020u) | 0x64006400u;
+  // (b14, b15) from the spare bits 15 / 31 of the three words
+  const uint32_t t0 = and_or(w0 >> 12, 0x00080008u, 0x64006400u);
+  const uint32_t t1 = and_or_v(w1 >> 11, 0x00100010u, t0);
+  p[15] = and_or_v(w2 >> 10, 0x00200020u, t1);
 }
 
 // Within-chunk offsets (k % 32) of the two codes of pair p.
@@ -86,29 +90,56 @@ __device__ __forceinline__ uint32_t half_of(const uint32_t u[16], int o) {
   return (u[o >> 1] >> (16 * (o & 1))) & 0xFFFFu;
 }
 
-template <int MT, int OUTK>
+// One wavefront per output row.  Lane l reads chunks l, l + 64, ... of the
+// current K slice (12 bytes each, 768 contiguous bytes per load instruction).
+// Everything the wave needs from HBM for the slice is requested up front: its
+// chunks, the statistics of the slice's blocks (written to a per-wave LDS area
+// as [stats1 w0, w1, w2, stats2 w0] + [stats2 w1] so that a chunk fetches them
+// with two LDS reads) and, on the first slice, up to 4 CSR entries per lane.
+// After the dense chunks, the row's CSR entries that fall in the slice add into
+// the same accumulators; one 64-lane reduction per row and batch entry.
+template <int MT, int BPL, int OUTK>
 __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
     const uint16_t* __restrict__ X, int M, int K, int KS,
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ stats1,
     const uint16_t* __restrict__ stats2, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const uint16_t* __restrict__ vals,
     int N, void* __restrict__ Y) {
+  constexpr int kCsr = 4;                             // CSR entries per lane held in registers
   extern __shared__ uint4 smem[];
   const int CS = KS >> 5;                             // chunks per slice
+  const int BS = KS >> 8;                             // statistic blocks per slice
   uint4* xl = smem;                                   // [MT][4][CS] pair quads
   float* xs = reinterpret_cast<float*>(smem + static_cast<size_t>(MT) * 4 * CS);   // [MT][2*CS]
+  const int wv = threadIdx.x >> 6;
+  uint4* st4 = reinterpret_cast<uint4*>(xs + static_cast<size_t>(MT) * 2 * CS) + static_cast<size_t>(wv) * BS;
+  uint32_t* st1 = reinterpret_cast<uint32_t*>(reinterpret_cast<uint4*>(xs + static_cast<size_t>(MT) * 2 * CS) +
+                                              static_cast<size_t>(kWaves) * BS) + static_cast<size_t>(wv) * BS;
 
   const int lane = threadIdx.x & 63;
-  const int sub = lane & (kLPR - 1);
-  const int n = blockIdx.x * kRowsPerWG + (threadIdx.x >> 4);
-  const bool row_ok = n < N;
+  const int n = blockIdx.x * kWaves + wv;
+  const bool nok = n < N;
   const int nb = K >> 8;
-  const size_t nrow = static_cast<size_t>(row_ok ? n : 0);
+  const size_t nrow = nok ? static_cast<size_t>(n) : 0;
   const uint32_t* crow = codes + nrow * (K >> 5) * 3;
   const uint32_t* s1row = stats1 + nrow * nb * 3;
   const uint2* s2row = reinterpret_cast<const uint2*>(stats2) + nrow * nb;
-  const int e0 = row_ok ? row_ptr[n] : 0;
-  const int e1 = row_ok ? row_ptr[n + 1] : 0;
+  const int e0 = nok ? row_ptr[n] : 0;
+  const int e1 = nok ? row_ptr[n + 1] : 0;
+
+  // CSR entries of this row held by this lane: e0 + lane + 64 i
+  int ccol[kCsr];
+  float cval[kCsr];
+#pragma unroll
+  for (int i = 0; i < kCsr; ++i) {
+    const int e = e0 + lane + 64 * i;
+    ccol[i] = -1;
+    cval[i] = 0.0f;
+    if (e < e1) {
+      ccol[i] = col_idx[e];
+      cval[i] = f16_bits_to_f32(vals[e]);
+    }
+  }
 
   float res[MT];
 #pragma unroll
@@ -116,9 +147,35 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
 
   for (int k0 = 0; k0 < K; k0 += KS) {
     const int ks = min(KS, K - k0);
-    const int cs = ks >> 5;
-    // ---- stage the activation slice as pairs + per-group sums
+    const int cs = ks >> 5, bs = ks >> 8;
+    const int cbase = k0 >> 5, bbase = k0 >> 8;
+    // ---- weight and statistics loads of this slice
+    uint3 w[BPL];
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+      const int c = 64 * b + lane;
+      if (nok && c < cs) w[b] = *reinterpret_cast<const uint3*>(crow + 3 * (cbase + c));
+    }
+    uint3 s1[2];
+    uint2 s2[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int blk = 64 * t + lane;
+      if (nok && blk < bs) {
+        s1[t] = *reinterpret_cast<const uint3*>(s1row + 3 * (bbase + blk));
+        s2[t] = s2row[bbase + blk];
+      }
+    }
+    // ---- stage the activation slice as pairs + per-group sums; this row's statistics
     __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int blk = 64 * t + lane;
+      if (nok && blk < bs) {
+        st4[blk] = make_uint4(s1[t].x, s1[t].y, s1[t].z, s2[t].x);
+        st1[blk] = s2[t].y;
+      }
+    }
     for (int it = threadIdx.x; it < M * cs; it += kThreads) {
       const int m = it / cs, c = it - m * cs;
       const uint4* src = reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K + k0) + 4 * c;
@@ -134,78 +191,76 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         xl[(static_cast<size_t>(m) * 4 + q) * CS + c] = make_uint4(P[4 * q], P[4 * q + 1], P[4 * q + 2], P[4 * q + 3]);
+      // group sums by dot products with (1, 1): pairs 0..7 hold group 2c, 8..15 group 2c+1
       float sa = 0.0f, sb = 0.0f;
 #pragma unroll
-      for (int o = 0; o < 16; ++o) {
-        sa += f16_bits_to_f32(static_cast<uint16_t>(half_of(u, o)));
-        sb += f16_bits_to_f32(static_cast<uint16_t>(half_of(u, 16 + o)));
+      for (int p = 0; p < 8; ++p) {
+        sa = dot2_f16(P[p], 0x3C003C00u, sa);
+        sb = dot2_f16(P[8 + p], 0x3C003C00u, sb);
       }
       xs[m * 2 * CS + 2 * c] = sa;
       xs[m * 2 * CS + 2 * c + 1] = sb;
     }
     __syncthreads();
-    if (!row_ok) continue;
+    if (!nok) continue;
 
-    // ---- dense 3-bit part over this slice
-    const int cbase = k0 >> 5;
-    for (int c = sub; c < cs; c += kLPR) {
-      const int cg = cbase + c;                       // global chunk index
-      const uint32_t* cw = crow + 3 * cg;
-      const uint32_t w0 = __builtin_nontemporal_load(cw);
-      const uint32_t w1 = __builtin_nontemporal_load(cw + 1);
-      const uint32_t w2 = __builtin_nontemporal_load(cw + 2);
-      const int b = cg >> 3, j = cg & 7;
-      const uint32_t* sw = s1row + 3 * b;
-      const uint64_t lo64 = static_cast<uint64_t>(sw[0]) | (static_cast<uint64_t>(sw[1]) << 32);
-      const uint64_t hi64 = static_cast<uint64_t>(sw[1]) | (static_cast<uint64_t>(sw[2]) << 32);
-      const int off = 12 * j;
-      const uint32_t f = static_cast<uint32_t>((off <= 52 ? (lo64 >> off) : (hi64 >> (off - 32))) & 0xFFFu);
-      const uint2 s2 = s2row[b];
-      const float SSs = f16_bits_to_f32(static_cast<uint16_t>(s2.x));
-      const float ZSs = f16_bits_to_f32(static_cast<uint16_t>(s2.x >> 16));
-      const float SSz = f16_bits_to_f32(static_cast<uint16_t>(s2.y));
-      const float ZSz = f16_bits_to_f32(static_cast<uint16_t>(s2.y >> 16));
-      const float sA = SSs * (static_cast<float>(f & 7u) - ZSs);
-      const float zA = SSz * (static_cast<float>((f >> 3) & 7u) - ZSz);
-      const float sB = SSs * (static_cast<float>((f >> 6) & 7u) - ZSs);
-      const float zB = SSz * (static_cast<float>((f >> 9) & 7u) - ZSz);
-
-      uint32_t p[16];
-      unpack_chunk(w0, w1, w2, p);
+    // ---- dense 3-bit part
+    const int nfull = cs >> 6;                         // blocks of 64 chunks with every lane busy
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < M) {
-          float aA = 0.0f, aB = 0.0f;
+    for (int b = 0; b < BPL; ++b) {
+      const int c = 64 * b + lane;
+      if (b < nfull || (b == nfull && c < cs)) {
+        const int blk = c >> 3, j = c & 7;             // block within the slice; chunk within the block
+        const uint4 sb4 = st4[blk];
+        const uint32_t szw = st1[blk];
+        const int off = 12 * j;                         // bit offset of the chunk's two 6-bit fields
+        const uint32_t lo = off < 32 ? sb4.x : (off < 64 ? sb4.y : sb4.z);
+        const uint32_t hi = off < 32 ? sb4.y : sb4.z;
+        const uint32_t f = static_cast<uint32_t>(((static_cast<uint64_t>(hi) << 32) | lo) >> (off & 31)) & 0xFFFu;
+        const float SSs = f16_bits_to_f32(static_cast<uint16_t>(sb4.w));
+        const float ZSs = f16_bits_to_f32(static_cast<uint16_t>(sb4.w >> 16));
+        const float SSz = f16_bits_to_f32(static_cast<uint16_t>(szw));
+        const float ZSz = f16_bits_to_f32(static_cast<uint16_t>(szw >> 16));
+        const float sA = SSs * (static_cast<float>(f & 7u) - ZSs);
+        const float zA = SSz * (static_cast<float>((f >> 3) & 7u) - ZSz);
+        const float sB = SSs * (static_cast<float>((f >> 6) & 7u) - ZSs);
+        const float zB = SSz * (static_cast<float>((f >> 9) & 7u) - ZSz);
+        uint32_t p[16];
+        unpack_chunk(w[b].x, w[b].y, w[b].z, p);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint4 xp = xl[(static_cast<size_t>(m) * 4 + q) * CS + c];
-            if (q < 2) {
-              aA = dot2_f16(p[4 * q], xp.x, aA);
-              aA = dot2_f16(p[4 * q + 1], xp.y, aA);
-              aA = dot2_f16(p[4 * q + 2], xp.z, aA);
-              aA = dot2_f16(p[4 * q + 3], xp.w, aA);
-            } else {
-              aB = dot2_f16(p[4 * q], xp.x, aB);
-              aB = dot2_f16(p[4 * q + 1], xp.y, aB);
-              aB = dot2_f16(p[4 * q + 2], xp.z, aB);
-              aB = dot2_f16(p[4 * q + 3], xp.w, aB);
+        for (int m = 0; m < MT; ++m) {
+          if (m < M) {
+            float aA = 0.0f, aB = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint4 xp = xl[(static_cast<size_t>(m) * 4 + q) * CS + c];
+              if (q < 2) {
+                aA = dot2_f16(p[4 * q], xp.x, aA);
+                aA = dot2_f16(p[4 * q + 1], xp.y, aA);
+                aA = dot2_f16(p[4 * q + 2], xp.z, aA);
+                aA = dot2_f16(p[4 * q + 3], xp.w, aA);
+              } else {
+                aB = dot2_f16(p[4 * q], xp.x, aB);
+                aB = dot2_f16(p[4 * q + 1], xp.y, aB);
+                aB = dot2_f16(p[4 * q + 2], xp.z, aB);
+                aB = dot2_f16(p[4 * q + 3], xp.w, aB);
+              }
             }
+            // sum x (c - z_hat) = acc / 8 - (128 + z_hat) * sum(x)
+            const float2 xab = reinterpret_cast<const float2*>(xs)[static_cast<size_t>(m) * CS + c];
+            const float tA = fmaf(aA, 0.125f, -(128.0f + zA) * xab.x);
+            const float tB = fmaf(aB, 0.125f, -(128.0f + zB) * xab.y);
+            res[m] = fmaf(sA, tA, res[m]);
+            res[m] = fmaf(sB, tB, res[m]);
           }
-          // sum x (c - z_hat) = acc / 8 - (128 + z_hat) * sum(x)
-          const float xa = xs[m * 2 * CS + 2 * c], xb = xs[m * 2 * CS + 2 * c + 1];
-          const float tA = fmaf(aA, 0.125f, -(128.0f + zA) * xa);
-          const float tB = fmaf(aB, 0.125f, -(128.0f + zB) * xb);
-          res[m] = fmaf(sA, tA, res[m]);
-          res[m] = fmaf(sB, tB, res[m]);
         }
       }
     }
 
     // ---- CSR outliers of this row whose column falls in the slice
-    for (int e = e0 + sub; e < e1; e += kLPR) {
-      const int col = col_idx[e] - k0;
-      if (col < 0 || col >= ks) continue;
-      const float v = f16_bits_to_f32(vals[e]);
+    auto outlier = [&](int colg, float v) {
+      const int col = colg - k0;
+      if (col < 0 || col >= ks) return;
       const int c = col >> 5, slot = pair_slot(col & 31);
       const int q = slot >> 3, wi = (slot >> 1) & 3, hh = slot & 1;
 #pragma unroll
@@ -216,37 +271,54 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
           res[m] = fmaf(f16_bits_to_f32(xh), v, res[m]);
         }
       }
-    }
+    };
+#pragma unroll
+    for (int i = 0; i < kCsr; ++i)
+      if (ccol[i] >= 0) outlier(ccol[i], cval[i]);
+    for (int e = e0 + lane + 64 * kCsr; e < e1; e += 64) outlier(col_idx[e], f16_bits_to_f32(vals[e]));
   }
 
-  // ---- 16-lane reduction and store
+  // ---- 64-lane reduction and store
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    float r = res[m];
-    r += __shfl_xor(r, 8, 64);
-    r += __shfl_xor(r, 4, 64);
-    r += __shfl_xor(r, 2, 64);
-    r += __shfl_xor(r, 1, 64);
-    if (m < M && row_ok && sub == 0) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, r);
+    if (m < M) {
+      const float r = wave_sum(res[m]);
+      if (nok && lane == 0) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, r);
+    }
   }
+}
+
+template <int MT, int BPL>
+void launch_k(const SpqrArgs& a, int KS, hipStream_t stream) {
+  const int CS = KS / 32, BS = KS / 256;
+  const size_t lds = static_cast<size_t>(MT) * 4 * CS * 16 + static_cast<size_t>(MT) * 2 * CS * 4 +
+                     static_cast<size_t>(kWaves) * BS * 20;
+  const int grid = (a.N + kWaves - 1) / kWaves;
+  if (a.y_dtype == QLIN_F32)
+    hipLaunchKernelGGL((spqr_gemv_kernel<MT, BPL, OUT_F32>), dim3(grid), dim3(kThreads), lds, stream,
+                       a.X, a.M, a.K, KS, a.codes, a.stats1, a.stats2, a.row_ptr, a.col_idx, a.vals, a.N, a.Y);
+  else
+    hipLaunchKernelGGL((spqr_gemv_kernel<MT, BPL, OUT_F16>), dim3(grid), dim3(kThreads), lds, stream,
+                       a.X, a.M, a.K, KS, a.codes, a.stats1, a.stats2, a.row_ptr, a.col_idx, a.vals, a.N, a.Y);
 }
 
 template <int MT>
 void launch_m(const SpqrArgs& a, hipStream_t stream) {
-  // slice length: a multiple of 512 whose activation pairs + sums fit the budget
-  // bytes per k: MT * 2 (fp16 pairs) + MT * 4 / 16 (one fp32 sum per group of 16)
-  int KS = static_cast<int>(kLdsBudget * 4 / (static_cast<size_t>(MT) * 9)) / 512 * 512;
-  if (KS < 512) KS = 512;
+  // K slice (multiple of 256): staged activations (2.25 bytes per value and batch
+  // row) plus the waves' statistics (20 bytes per 256 values and wave) within
+  // the LDS budget; at most 16 chunk loads per lane (32768 values) and at most
+  // 128 statistic blocks per slice (two per lane)
+  const double per_k = 2.25 * MT + 20.0 * kWaves / 256.0;
+  int KS = static_cast<int>(static_cast<double>(kLdsBudget) / per_k);
+  if (KS > 32768) KS = 32768;
+  KS = KS / 256 * 256;
+  if (KS < 256) KS = 256;
   if (KS > a.K) KS = a.K;
-  const int CS = KS / 32;
-  const size_t lds = static_cast<size_t>(MT) * 4 * CS * 16 + static_cast<size_t>(MT) * 2 * CS * 4;
-  const int grid = (a.N + kRowsPerWG - 1) / kRowsPerWG;
-  if (a.y_dtype == QLIN_F32)
-    hipLaunchKernelGGL((spqr_gemv_kernel<MT, OUT_F32>), dim3(grid), dim3(kThreads), lds, stream,
-                       a.X, a.M, a.K, KS, a.codes, a.stats1, a.stats2, a.row_ptr, a.col_idx, a.vals, a.N, a.Y);
-  else
-    hipLaunchKernelGGL((spqr_gemv_kernel<MT, OUT_F16>), dim3(grid), dim3(kThreads), lds, stream,
-                       a.X, a.M, a.K, KS, a.codes, a.stats1, a.stats2, a.row_ptr, a.col_idx, a.vals, a.N, a.Y);
+  const int blocks = (KS / 32 + 63) / 64;
+  if (blocks <= 4) launch_k<MT, 4>(a, KS, stream);
+  else if (blocks <= 8) launch_k<MT, 8>(a, KS, stream);
+  else if (blocks <= 12) launch_k<MT, 12>(a, KS, stream);
+  else launch_k<MT, 16>(a, KS, stream);
 }
 
 // Debug: dense codes and first-level statistic codes via the forward's routines.
