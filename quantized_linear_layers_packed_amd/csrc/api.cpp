@@ -51,6 +51,8 @@ qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
   W4Args a{X, x_dtype, M, K, N, G, qweight, scales, qzeros, Y, y_dtype};
   if (w4_gemv_supported(M, K, G)) {
     w4_gemv_launch(a, stream);
+  } else if (G >= 128) {
+    QLIN_TRY(w4_gemm_sk_launch(a, stream));
   } else {
     w4_gemm_launch(a, stream);
   }

@@ -6,6 +6,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "../../include/qlin.h"
+
 namespace qlin {
 
 struct W4Args {
@@ -23,7 +25,9 @@ struct W4Args {
 size_t w4_gemv_lds_bytes(int M, int K);
 bool w4_gemv_supported(int M, int K, int G);
 void w4_gemv_launch(const W4Args& a, hipStream_t stream);
-// MFMA GEMM for larger batches.
+// MFMA GEMM for larger batches: stream-K kernel for groups of 128 / 256
+// (uses the library workspace), one-group-per-step kernel for 32 / 64.
+qlin_status w4_gemm_sk_launch(const W4Args& a, hipStream_t stream);
 void w4_gemm_launch(const W4Args& a, hipStream_t stream);
 void w4_unpack_launch(const uint32_t* qweight, const uint32_t* qzeros, int N, int K, int G,
                       uint8_t* codes, uint8_t* zeros, hipStream_t stream);

@@ -1,0 +1,61 @@
+// Stream-K partition of a GEMM's (output tile, K step) iteration space over a
+// fixed number of workgroups, and the fix-up of tiles whose K range is shared.
+//
+// Units u = tile * ksteps + kstep are dealt out in P contiguous ranges
+// [begin(p), begin(p + 1)), begin(p) = floor(p * U / P), so every workgroup gets
+// the same amount of multiply work whatever the tile count.  A tile covered by
+// one range is finished in place; otherwise each contributing workgroup writes
+// its fp32 partial tile to a workspace slot (two slots per workgroup: the tile
+// its range starts in, and the tile it ends in), bumps the tile's counter, and
+// the last one to arrive adds the partials in K order (the result does not
+// depend on arrival order), writes the output and resets the counter.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace qlin {
+
+struct SkPlan {
+  int ksteps;        // K steps per tile
+  long long units;   // tiles * ksteps
+  int P;             // workgroups
+};
+
+__device__ __forceinline__ long long sk_begin(const SkPlan& s, int p) {
+  return (static_cast<long long>(p) * s.units) / s.P;
+}
+
+// Workgroup whose range holds unit u.
+__device__ __forceinline__ int sk_owner(const SkPlan& s, long long u) {
+  return static_cast<int>(((u + 1) * s.P + s.units - 1) / s.units) - 1;
+}
+
+// Partial tiles cross XCDs, whose L2 caches are not coherent with each other.
+// Device-scope fences would write back and invalidate the whole L2 of the
+// issuing XCD (and so every other workgroup's cached operands) at each hand-off;
+// instead the partials are written and read with device-coherent accesses
+// (performed at the device coherence point, bypassing the non-coherent caches),
+// the writer drains its stores before the workgroup barrier, and the arrival
+// counter is a relaxed device-scope atomic issued after that barrier.
+__device__ __forceinline__ void sk_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float sk_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sk_drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ int sk_arrive(int* counter) {
+  return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sk_reset(int* counter) {
+  __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workspace slot holding workgroup q's partial of tile t.
+__device__ __forceinline__ int sk_slot(const SkPlan& s, int q, int t) {
+  return 2 * q + ((sk_begin(s, q) / s.ksteps) == t ? 0 : 1);
+}
+
+}  // namespace qlin

@@ -1,0 +1,317 @@
+// W4 dequant -> fp16 MFMA GEMM for batches past the GEMV range (group size 128
+// or 256), gfx950.
+//
+// Y[m][n] = sum_g S[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g])
+//
+// At larger batch the weight-only layer becomes compute bound and the dequant
+// work is what erodes the gain (GPTQ bulletin, "İddia ve Gerçeklik").  Layout of
+// the work:
+//   * one workgroup = 4 waves side by side along N; a wave owns all BM = 32 TM
+//     rows of the tile and 32 output columns, so every packed word is turned into
+//     fp16 once and feeds TM matrix instructions;
+//   * B operand: a lane unpacks one word (8 codes of its column) per
+//     v_mfma_f32_32x32x16_f16 into the exact fp16 integers q - z, in natural k
+//     order: a byte permute + an and-or place each code in the mantissa of
+//     1024.0 and one packed fp16 subtraction removes 1024 + z.  No rounding;
+//   * A operand: the activation tile of one 128-wide K step, converted to fp16
+//     (bf16 inputs exactly, for values in the fp16 normal range) and stored in
+//     LDS as 256-byte rows whose 16-byte chunks are XOR-swizzled by the row, so
+//     the 32 rows an MFMA reads land in distinct banks; double buffered;
+//   * each K step's fp32 products are scaled by the group's fp16 scale into the
+//     running fp32 result (one fused multiply-add per output and step);
+//   * packed words, the group scale/zero and the activations are fetched R - 1
+//     K steps ahead into R-deep register rings (every load unconditional, so the
+//     compiler's in-order wait counts never drain the rings): with a few waves
+//     per CU, the bytes in flight have to cover the memory latency;
+//   * the (tile, K step) space is split evenly over one workgroup per CU
+//     (stream-K); tiles shared by several workgroups are summed in K order by
+//     the last workgroup to finish them.
+
+#include <algorithm>
+#include <type_traits>
+
+#include "common.hpp"
+#include "device.hpp"
+#include "launch.hpp"
+#include "splitk.hpp"
+#include "workspace.hpp"
+
+namespace qlin {
+
+namespace {
+
+constexpr int kThreads = 256;   // 4 waves along N
+constexpr int kBN = 128;        // output columns per tile
+constexpr int kKS = 128;        // K per step (16 packed words per column)
+
+// Eight fp16 values q - z in natural k order from one packed word.
+__device__ __forceinline__ h8_t dequant_nat(uint32_t w, h2_t zz) {
+  const uint32_t t = w >> 4;
+  h8_t b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // byte j of w holds codes 2j (low nibble) and 2j + 1; t's byte j has code 2j + 1 low
+    const uint32_t sel = static_cast<uint32_t>(j) | (0x0Cu << 8) | (static_cast<uint32_t>(4 + j) << 16) | (0x0Cu << 24);
+    const uint32_t pr = __builtin_amdgcn_perm(t, w, sel);
+    const h2_t d = bitcast<h2_t>(and_or(pr, 0x000F000Fu, 0x64006400u)) - zz;   // exact
+    b[2 * j] = d[0];
+    b[2 * j + 1] = d[1];
+  }
+  return b;
+}
+
+// Two bf16 values -> two fp16 values (exact in the fp16 normal range).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
+  const float lo = bitcast<float>(u << 16);
+  const float hi = bitcast<float>(u & 0xFFFF0000u);
+  return bitcast<uint32_t>(__builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// Calls f(step index I, kk) for I = 0 .. R-1 while kk < k1; false once the range is done.
+template <int I, int R, class F>
+__device__ __forceinline__ bool run_steps(F& f, int& kk, int k1) {
+  f(std::integral_constant<int, I>{}, kk);
+  if (++kk >= k1) return false;
+  if constexpr (I + 1 < R) return run_steps<I + 1, R>(f, kk, k1);
+  else return true;
+}
+
+template <int TM, int R, bool XBF16, int OUTK>
+__global__ __launch_bounds__(kThreads) void w4_gemm_sk_kernel(
+    const uint16_t* X, int M, int K, const uint32_t* qweight, const uint16_t* scales,
+    const uint32_t* qzeros, int N, int gsh, int tiles_n, SkPlan plan, void* Y, float* ws, int* counters) {
+  // (no __restrict__: with it the prefetch loads count as invariant and get sunk
+  // across the step barriers to their first use, which defeats the prefetch)
+  constexpr int BM = 32 * TM;
+  constexpr int APT = BM * 16 / kThreads;   // 16-byte activation pieces per thread per step
+  static_assert(APT >= 1, "tile too small");
+  extern __shared__ uint4 smem[];
+  __shared__ int s_last;
+  uint4* const As0 = smem;
+  uint4* const As1 = smem + BM * 16;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int col = lane & 31, h = lane >> 5;
+  const int ng = K >> (7 + gsh);              // quantization groups per row
+  const int nzw = (ng + 7) >> 3;               // zero-point words per row
+  const int swz = col & 15;                    // chunk swizzle of the rows this lane reads
+
+  const int p = xcd_tile(blockIdx.x, gridDim.x);
+  long long u = sk_begin(plan, p);
+  const long long u_end = sk_begin(plan, p + 1);
+
+  while (u < u_end) {
+    const int t = static_cast<int>(u / plan.ksteps);
+    const int k0 = static_cast<int>(u - static_cast<long long>(t) * plan.ksteps);
+    const int k1 = static_cast<int>(std::min<long long>(plan.ksteps, k0 + (u_end - u)));
+    const int m0 = (t / tiles_n) * BM;
+    const int n = (t % tiles_n) * kBN + 32 * wv + col;
+    const bool nok = n < N;
+    const size_t nn = static_cast<size_t>(min(n, N - 1));
+    const uint32_t* qrow = qweight + nn * (K >> 3);
+    const uint16_t* srow = scales + nn * ng;
+    const uint32_t* zrow = qzeros + nn * nzw;
+
+    // ---- loaders
+    // Every load below is issued unconditionally (rows, columns and steps past
+    // the end are clamped to valid addresses and masked at use): with loads
+    // behind branches the count of younger loads would depend on the path and
+    // the compiler would drain the whole prefetch queue before each use.
+    uint4 av[R][APT];                          // activation ring: step k0 + j in set j % R
+    auto load_a = [&](int s, uint4 (&v)[APT]) {
+#pragma unroll
+      for (int j = 0; j < APT; ++j) {
+        const int piece = tid + j * kThreads;
+        const int r = piece >> 4, c = piece & 15;
+        const int m = min(m0 + r, M - 1);
+        v[j] = *reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K + s * kKS + 8 * c);
+      }
+    };
+    auto store_a = [&](uint4* dst, const uint4 (&src)[APT]) {
+#pragma unroll
+      for (int j = 0; j < APT; ++j) {
+        const int piece = tid + j * kThreads;
+        const int r = piece >> 4, c = piece & 15;
+        uint4 v = src[j];
+        if constexpr (XBF16) {
+          v.x = bf16x2_to_f16x2(v.x);
+          v.y = bf16x2_to_f16x2(v.y);
+          v.z = bf16x2_to_f16x2(v.z);
+          v.w = bf16x2_to_f16x2(v.w);
+        }
+        const bool live = m0 + r < M;
+        v.x = live ? v.x : 0u;
+        v.y = live ? v.y : 0u;
+        v.z = live ? v.z : 0u;
+        v.w = live ? v.w : 0u;
+        dst[r * 16 + (c ^ (r & 15))] = v;
+      }
+    };
+    uint4 bq[R][2];                            // weight ring: step k0 + j in set j % R
+    uint32_t bs[R], bz[R];
+    auto load_b = [&](int s, uint4 (&w)[2], uint32_t& sc, uint32_t& zw) {
+      const uint4* src = reinterpret_cast<const uint4*>(qrow) + 4 * s;
+      w[0] = src[h];                           // words 4h .. 4h+3 of the step
+      w[1] = src[2 + h];                       // words 8+4h .. 8+4h+3
+      const int g = s >> gsh;
+      sc = srow[g];
+      zw = zrow[g >> 3];
+    };
+
+    f32x16_t acc[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) acc[i] = f32x16_t{};
+
+    // ---- prologue
+    const int klast = k1 - 1;
+#pragma unroll
+    for (int j = 0; j < R - 1; ++j) load_b(min(k0 + j, klast), bq[j], bs[j], bz[j]);
+#pragma unroll
+    for (int j = 0; j < R; ++j) load_a(min(k0 + j, klast), av[j]);
+    store_a(As0, av[0]);
+    __syncthreads();
+
+    auto step = [&](auto set_c, int kk) {
+      constexpr int S = decltype(set_c)::value;
+      constexpr int SB = (S + R - 1) % R;      // set of step kk - 1, free since that step
+      load_b(min(kk + R - 1, klast), bq[SB], bs[SB], bz[SB]);
+      __builtin_amdgcn_sched_barrier(0);       // keep the prefetch issued here, ahead of the math
+      const uint4* Ab = ((kk - k0) & 1) ? As1 : As0;
+      const int g = kk >> gsh;
+      const uint32_t z = (bz[S] >> (4 * (g & 7))) & 15u;
+      const _Float16 zb = static_cast<_Float16>(1024.0f + static_cast<float>(z));
+      const h2_t zz = {zb, zb};
+      f32x16_t part[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) part[i] = f32x16_t{};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const uint4 q4 = bq[S][st >> 2];
+        const uint32_t w = (st & 3) == 0 ? q4.x : (st & 3) == 1 ? q4.y : (st & 3) == 2 ? q4.z : q4.w;
+        const h8_t b = dequant_nat(w, zz);
+        const int c = 8 * (st >> 2) + 4 * h + (st & 3);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const h8_t a = bitcast<h8_t>(Ab[(32 * i + col) * 16 + (c ^ swz)]);
+          part[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, part[i], 0, 0, 0);
+        }
+      }
+      const float sc = f16_bits_to_f32(static_cast<uint16_t>(bs[S]));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = fmaf(sc, part[i][r], acc[i][r]);
+      // the next step's activations (past the range end this rewrites the idle
+      // buffer), then the fetch three steps ahead into the set of step kk
+      // (emptied at the end of the previous step)
+      constexpr int S1 = (S + 1) % R;
+      store_a(((kk + 1 - k0) & 1) ? As1 : As0, av[S1]);
+      load_a(min(kk + R, klast), av[S]);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    };
+
+    int kk = k0;
+    while (run_steps<0, R>(step, kk, k1)) {
+    }
+
+    // ---- finish the tile: lane holds column n, rows 8*(r/4) + 4*h + r%4 of each 32-row block
+    bool write = true;
+    if (k0 != 0 || k1 != plan.ksteps) {
+      const int first = sk_owner(plan, static_cast<long long>(t) * plan.ksteps);
+      const int last = sk_owner(plan, static_cast<long long>(t + 1) * plan.ksteps - 1);
+      float* mine = ws + static_cast<size_t>(sk_slot(plan, p, t)) * (BM * kBN);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sk_store(mine + ((wv * TM + i) * 16 + r) * 64 + lane, acc[i][r]);
+      sk_drain_stores();
+      __syncthreads();
+      if (tid == 0) s_last = sk_arrive(&counters[t]) == last - first;
+      __syncthreads();
+      write = s_last != 0;
+      if (write) {
+        f32x16_t tot[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) tot[i] = f32x16_t{};
+        for (int q = first; q <= last; ++q) {
+          if (q == p) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) tot[i] += acc[i];
+          } else {
+            const float* other = ws + static_cast<size_t>(sk_slot(plan, q, t)) * (BM * kBN);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) tot[i][r] += sk_load(other + ((wv * TM + i) * 16 + r) * 64 + lane);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) acc[i] = tot[i];
+        if (tid == 0) sk_reset(&counters[t]);
+      }
+    }
+    if (write && nok) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, acc[i][r]);
+        }
+    }
+    u += k1 - k0;
+  }
+}
+
+template <int TM, int R, bool XBF16, int OUTK>
+qlin_status launch_sk(const W4Args& a, hipStream_t stream) {
+  constexpr int BM = 32 * TM;
+  const size_t lds = static_cast<size_t>(2) * BM * 16 * sizeof(uint4);
+  static int occ = 0;                          // resident workgroups per CU (register / LDS bound)
+  if (occ == 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, w4_gemm_sk_kernel<TM, R, XBF16, OUTK>, kThreads, lds) !=
+            hipSuccess || o <= 0)
+      o = 1;
+    occ = std::min(o, 2);
+  }
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + kBN - 1) / kBN;
+  const long long tiles = static_cast<long long>(tiles_m) * tiles_n;
+  SkPlan plan;
+  plan.ksteps = a.K / kKS;
+  plan.units = tiles * plan.ksteps;
+  plan.P = static_cast<int>(std::min<long long>(static_cast<long long>(occ) * device_cus(), plan.units));
+  Workspace w;
+  const qlin_status s = get_workspace(static_cast<size_t>(2) * plan.P * BM * kBN * sizeof(float),
+                                      static_cast<size_t>(tiles), stream, "qlin_w4_forward", &w);
+  if (s != QLIN_OK) return s;
+  const int gsh = a.G == 256 ? 1 : 0;
+  hipLaunchKernelGGL((w4_gemm_sk_kernel<TM, R, XBF16, OUTK>), dim3(plan.P), dim3(kThreads), lds, stream,
+                     static_cast<const uint16_t*>(a.X), a.M, a.K, a.qweight, a.scales, a.qzeros, a.N, gsh, tiles_n,
+                     plan, a.Y, w.partials, w.counters);
+  return QLIN_OK;
+}
+
+template <int TM, int R, bool XBF16>
+qlin_status launch_o(const W4Args& a, hipStream_t stream) {
+  if (a.y_dtype == QLIN_F16) return launch_sk<TM, R, XBF16, OUT_F16>(a, stream);
+  if (a.y_dtype == QLIN_BF16) return launch_sk<TM, R, XBF16, OUT_BF16>(a, stream);
+  return launch_sk<TM, R, XBF16, OUT_F32>(a, stream);
+}
+
+template <int TM, int R>
+qlin_status launch_x(const W4Args& a, hipStream_t stream) {
+  return a.x_dtype == QLIN_BF16 ? launch_o<TM, R, true>(a, stream) : launch_o<TM, R, false>(a, stream);
+}
+
+}  // namespace
+
+qlin_status w4_gemm_sk_launch(const W4Args& a, hipStream_t stream) {
+  if (a.M <= 32) return launch_x<1, 6>(a, stream);
+  if (a.M <= 64) return launch_x<2, 4>(a, stream);
+  return launch_x<4, 4>(a, stream);
+}
+
+}  // namespace qlin
