@@ -129,7 +129,7 @@ qlin_status sq_int8_gemm(const int8_t* Xq, const float* x_scale, const int8_t* W
   QLIN_TRY(need_aligned(fn, "Wq", Wq));
   QLIN_TRY(need_aligned(fn, "Y", Y));
   if (acc_out) QLIN_TRY(need_aligned(fn, "acc_out", acc_out));
-  sq_gemm_launch(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+  QLIN_TRY(sq_gemm_launch(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream));
   return check_launch(fn);
 }
 

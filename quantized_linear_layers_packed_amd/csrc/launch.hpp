@@ -51,7 +51,7 @@ void spqr_unpack_launch(const uint32_t* codes, const uint32_t* stats1, int N, in
 
 void sq_act_launch(const uint16_t* X, const float* inv_s, int M, int K, int8_t* Xq, float* x_scale,
                    hipStream_t stream);
-void sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
-                    int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream);
+qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
+                           int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream);
 
 }  // namespace qlin

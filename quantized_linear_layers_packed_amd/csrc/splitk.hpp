@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 namespace qlin {
 
@@ -45,6 +46,12 @@ __device__ __forceinline__ void sk_store(float* p, float v) {
 __device__ __forceinline__ float sk_load(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void sk_store(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int sk_load(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void sk_drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ int sk_arrive(int* counter) {
   return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -56,6 +63,21 @@ __device__ __forceinline__ void sk_reset(int* counter) {
 // Workspace slot holding workgroup q's partial of tile t.
 __device__ __forceinline__ int sk_slot(const SkPlan& s, int q, int t) {
   return 2 * q + ((sk_begin(s, q) / s.ksteps) == t ? 0 : 1);
+}
+
+}  // namespace qlin
+
+namespace qlin {
+
+// Calls f(I, kk) for I = 0 .. R-1 while kk < k1 (a K loop unrolled by the depth R
+// of the register rings, so every ring index is a compile-time constant);
+// returns false once the range is done.
+template <int I, int R, class F>
+__device__ __forceinline__ bool sk_run_steps(F& f, int& kk, int k1) {
+  f(std::integral_constant<int, I>{}, kk);
+  if (++kk >= k1) return false;
+  if constexpr (I + 1 < R) return sk_run_steps<I + 1, R>(f, kk, k1);
+  else return true;
 }
 
 }  // namespace qlin

@@ -15,12 +15,16 @@
 // GEMM kernel: v_mfma_i32_32x32x32_i8, exact int32 accumulation
 // (|acc| <= K * 127^2 < 2^31 for K <= 131072).  The token tile of Xq is staged
 // in LDS per 128-wide K step (double buffered) and shared by the waves; each
-// wave streams its own weight rows from HBM into MFMA operand registers one K
-// step ahead.  Epilogue: float(acc) * x_scale[m] * w_scale[n], rounded once.
+// wave streams its own weight rows from HBM into MFMA operand registers, R - 1
+// K steps ahead.  Epilogue: float(acc) * x_scale[m] * w_scale[n], rounded once.
+
+#include <algorithm>
 
 #include "common.hpp"
 #include "device.hpp"
 #include "launch.hpp"
+#include "splitk.hpp"
+#include "workspace.hpp"
 
 namespace qlin {
 
@@ -77,154 +81,206 @@ __global__ __launch_bounds__(kActThreads) void sq_act_kernel(const uint16_t* __r
   }
 }
 
-constexpr int kGemmThreads = 256;   // 4 waves
-constexpr int kBK = 128;            // K bytes per pipeline step (4 MFMA steps)
+constexpr int kGemmThreads = 256;   // 4 waves side by side along N
+constexpr int kBN = 128;            // output columns per tile
+constexpr int kBK = 128;            // K bytes per step (4 MFMA steps of 32)
 
-// Tiles of 32 x 32 outputs; waves WM x WN, each TM x TN tiles.  Within one
-// 128-byte K step, MFMA step st and lane half h use bytes 64h + 16st .. +15 of
-// both operands (a fixed permutation of k, identical for A and B), so each lane
-// streams 64 contiguous bytes of its weight row per K step.  The next K step's
-// weights are loaded into registers and its activation tile into the second
-// LDS buffer while the current one is multiplied.
-template <int WM, int WN, int TM, int TN, int OUTK>
-__global__ __launch_bounds__(kGemmThreads) void sq_gemm_kernel(
-    const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
-    const int8_t* __restrict__ Wq, const float* __restrict__ w_scale,
-    int M, int N, int K, void* __restrict__ Y, int32_t* __restrict__ acc_out) {
-  static_assert(WM * WN == 4, "four waves");
-  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  constexpr int ROW = kBK + 16;                          // LDS row stride in bytes
-  constexpr int PIECES = BM * kBK / 16;                  // 16-byte activation pieces per K step
-  constexpr int APT = (PIECES + kGemmThreads - 1) / kGemmThreads;
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * ROW];
+// Tiles of BM = 32 TM rows x 128 columns; a wave owns all BM rows and 32
+// columns.  Within one 128-byte K step, MFMA step st and lane half h use bytes
+// 64h + 16st .. +15 of both operands (a fixed permutation of k, identical for A
+// and B), so each lane streams 64 contiguous bytes of its weight row per step.
+// Activation rows go to LDS as 128-byte rows whose 16-byte chunks are
+// XOR-swizzled by row / 2, so the 32 rows an MFMA reads fall in distinct banks.
+// Weights and activations are fetched R - 1 steps ahead into register rings,
+// with every load unconditional (clamped addresses) so that the compiler's
+// in-order wait counts never drain the rings.  The (tile, K step) space is
+// split evenly over the workgroups (stream-K); shared tiles are summed (int32,
+// exact) by the last workgroup to finish them.
+template <int TM, int R, int OUTK>
+__global__ __launch_bounds__(kGemmThreads) void sq_gemm_sk_kernel(
+    const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
+    int M, int N, int K, int tiles_n, SkPlan plan, void* Y, int32_t* acc_out, int* ws, int* counters) {
+  // (no __restrict__: it would let the prefetch loads be sunk across the step
+  // barriers to their first use)
+  constexpr int BM = 32 * TM;
+  constexpr int APT = BM * 8 / kGemmThreads;   // 16-byte activation pieces per thread per step
+  static_assert(APT >= 1, "tile too small");
+  extern __shared__ uint4 smem[];
+  __shared__ int s_last;
+  uint4* const As0 = smem;
+  uint4* const As1 = smem + BM * 8;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int wm = wv / WN, wn = wv % WN;
-  const int col = lane & 31, half = lane >> 5;
-  const int MB = (M + BM - 1) / BM;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int m0 = (tile % MB) * BM;
-  const int n0 = (tile / MB) * BN + wn * TN * 32;
-  const int nk = (K + kBK - 1) / kBK;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int col = lane & 31, h = lane >> 5;
+  const int swz = (col >> 1) & 7;
 
-  const int8_t* wrow[TN];
-  bool nok[TN];
+  const int p = xcd_tile(blockIdx.x, gridDim.x);
+  long long u = sk_begin(plan, p);
+  const long long u_end = sk_begin(plan, p + 1);
+
+  while (u < u_end) {
+    const int t = static_cast<int>(u / plan.ksteps);
+    const int k0 = static_cast<int>(u - static_cast<long long>(t) * plan.ksteps);
+    const int k1 = static_cast<int>(std::min<long long>(plan.ksteps, k0 + (u_end - u)));
+    const int klast = k1 - 1;
+    const int m0 = (t / tiles_n) * BM;
+    const int n = (t % tiles_n) * kBN + 32 * wv + col;
+    const bool nok = n < N;
+    const size_t nn = static_cast<size_t>(min(n, N - 1));
+    const int8_t* wrow = Wq + nn * K;
+
+    // Activation rows past M are read from row M - 1 and never stored.  When
+    // K % 128 == 64 the last step is half full: its addresses are clamped into
+    // the row and its activation chunks past K are zeroed at staging, so the
+    // weight bytes they meet contribute nothing.
+    uint4 av[R][APT];
+    auto load_a = [&](int s, uint4 (&v)[APT]) {
 #pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    const int n = n0 + 32 * t + col;
-    nok[t] = n < N;
-    wrow[t] = Wq + static_cast<size_t>(nok[t] ? n : 0) * K;
-  }
-
-  uint4 av[APT];
-  uint4 bq[TN][4];
-  auto load_a = [&](int kk) {
-#pragma unroll
-    for (int p = 0; p < APT; ++p) {
-      const int piece = tid + p * kGemmThreads;
-      const int r = piece / (kBK / 16), c = piece - r * (kBK / 16);
-      const int m = m0 + r;
-      const int k = kk * kBK + 16 * c;
-      av[p] = (piece < PIECES && m < M && k < K)
-                  ? *reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(m) * K + k)
-                  : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < APT; ++p) {
-      const int piece = tid + p * kGemmThreads;
-      if (piece < PIECES) {
-        const int r = piece / (kBK / 16), c = piece - r * (kBK / 16);
-        *reinterpret_cast<uint4*>(&As[buf][r * ROW + 16 * c]) = av[p];
+      for (int j = 0; j < APT; ++j) {
+        const int piece = tid + j * kGemmThreads;
+        const int r = piece >> 3, c = piece & 7;
+        const int m = min(m0 + r, M - 1);
+        const int kb = min(s * kBK + 16 * c, K - 16);
+        v[j] = *reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(m) * K + kb);
       }
-    }
-  };
-  auto load_b = [&](int kk) {
+    };
+    auto store_a = [&](uint4* dst, const uint4 (&src)[APT], int s) {
+      const bool tail = s * kBK + kBK > K;      // uniform
 #pragma unroll
-    for (int t = 0; t < TN; ++t) {
+      for (int j = 0; j < APT; ++j) {
+        const int piece = tid + j * kGemmThreads;
+        const int r = piece >> 3, c = piece & 7;
+        uint4 v = src[j];
+        if (tail && s * kBK + 16 * c >= K) v = make_uint4(0u, 0u, 0u, 0u);
+        dst[r * 8 + (c ^ ((r >> 1) & 7))] = v;
+      }
+    };
+    uint4 bq[R][4];
+    auto load_b = [&](int s, uint4 (&w)[4]) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        w[st] = *reinterpret_cast<const uint4*>(wrow + min(s * kBK + 64 * h + 16 * st, K - 16));
+    };
+
+    i32x16_t acc[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) acc[i] = i32x16_t{};
+
+    // prologue in the steady-state issue order (weights of step j, then
+    // activations of step j + 1), so the wait counts agree at the loop head
+    load_a(k0, av[0]);
+#pragma unroll
+    for (int j = 0; j < R - 1; ++j) {
+      load_b(min(k0 + j, klast), bq[j]);
+      load_a(min(k0 + j + 1, klast), av[j + 1]);
+    }
+    store_a(As0, av[0], k0);
+    __syncthreads();
+
+    auto step = [&](auto set_c, int kk) {
+      constexpr int S = decltype(set_c)::value;
+      constexpr int SB = (S + R - 1) % R;
+      load_b(min(kk + R - 1, klast), bq[SB]);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint4* Ab = ((kk - k0) & 1) ? As1 : As0;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const int k = kk * kBK + 64 * half + 16 * st;
-        bq[t][st] = (nok[t] && k < K) ? load_stream16(wrow[t] + k) : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
-
-  i32x16_t acc[TM][TN];
+        const i32x4_t b = bitcast<i32x4_t>(bq[S][st]);
+        const int c = 4 * h + st;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int t = 0; t < TN; ++t) acc[i][t] = i32x16_t{};
-
-  load_a(0);
-  load_b(0);
-  store_a(0);
-  __syncthreads();
-
-  for (int kk = 0; kk < nk; ++kk) {
-    const int buf = kk & 1;
-    uint4 bcur[TN][4];
-#pragma unroll
-    for (int t = 0; t < TN; ++t)
-#pragma unroll
-      for (int st = 0; st < 4; ++st) bcur[t][st] = bq[t][st];
-    if (kk + 1 < nk) {
-      load_a(kk + 1);
-      load_b(kk + 1);
-    }
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = (wm * TM + i) * 32 + col;
-        const i32x4_t a = *reinterpret_cast<const i32x4_t*>(&As[buf][r * ROW + 64 * half + 16 * st]);
-#pragma unroll
-        for (int t = 0; t < TN; ++t) {
-          const i32x4_t b = bitcast<i32x4_t>(bcur[t][st]);
-          acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[i][t], 0, 0, 0);
+        for (int i = 0; i < TM; ++i) {
+          const i32x4_t a = bitcast<i32x4_t>(Ab[(32 * i + col) * 8 + (c ^ swz)]);
+          acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[i], 0, 0, 0);
         }
       }
-    }
-    if (kk + 1 < nk) {
-      store_a(buf ^ 1);
+      store_a(((kk + 1 - k0) & 1) ? As1 : As0, av[(S + 1) % R], kk + 1);
+      load_a(min(kk + R, klast), av[S]);
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
+    };
+    int kk = k0;
+    while (sk_run_steps<0, R>(step, kk, k1)) {
     }
-  }
 
+    // ---- finish the tile: lane holds column n, rows 8*(r/4) + 4*h + r%4 of each 32-row block
+    bool write = true;
+    if (k0 != 0 || k1 != plan.ksteps) {
+      const int first = sk_owner(plan, static_cast<long long>(t) * plan.ksteps);
+      const int last = sk_owner(plan, static_cast<long long>(t + 1) * plan.ksteps - 1);
+      int* mine = ws + static_cast<size_t>(sk_slot(plan, p, t)) * (BM * kBN);
 #pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    if (!nok[t]) continue;
-    const int n = n0 + 32 * t + col;
-    const float ws = w_scale[n];
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+        for (int r = 0; r < 16; ++r) sk_store(mine + ((wv * TM + i) * 16 + r) * 64 + lane, acc[i][r]);
+      sk_drain_stores();
+      __syncthreads();
+      if (tid == 0) s_last = sk_arrive(&counters[t]) == last - first;
+      __syncthreads();
+      write = s_last != 0;
+      if (write) {
+        for (int q = first; q <= last; ++q) {
+          if (q == p) continue;
+          const int* other = ws + static_cast<size_t>(sk_slot(plan, q, t)) * (BM * kBN);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + (wm * TM + i) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (m < M) {
-          const size_t idx = static_cast<size_t>(m) * N + n;
-          store_out<OUTK>(Y, idx, static_cast<float>(acc[i][t][r]) * x_scale[m] * ws);
-          if (acc_out) acc_out[idx] = acc[i][t][r];
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][r] += sk_load(other + ((wv * TM + i) * 16 + r) * 64 + lane);
         }
+        if (tid == 0) sk_reset(&counters[t]);
       }
     }
+    if (write && nok) {
+      const float wsc = w_scale[n];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (m < M) {
+            const size_t idx = static_cast<size_t>(m) * N + n;
+            store_out<OUTK>(Y, idx, static_cast<float>(acc[i][r]) * x_scale[m] * wsc);
+            if (acc_out) acc_out[idx] = acc[i][r];
+          }
+        }
+    }
+    u += k1 - k0;
   }
 }
 
-template <int WM, int WN, int TM, int TN>
-void gemm_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
-            void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
-  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  dim3 grid(((N + BN - 1) / BN) * ((M + BM - 1) / BM));
-  if (y_dtype == QLIN_F32)
-    hipLaunchKernelGGL((sq_gemm_kernel<WM, WN, TM, TN, OUT_F32>), grid, dim3(kGemmThreads), 0, stream,
-                       Xq, xsc, Wq, wsc, M, N, K, Y, acc_out);
-  else
-    hipLaunchKernelGGL((sq_gemm_kernel<WM, WN, TM, TN, OUT_F16>), grid, dim3(kGemmThreads), 0, stream,
-                       Xq, xsc, Wq, wsc, M, N, K, Y, acc_out);
+template <int TM, int R, int OUTK>
+qlin_status gemm_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
+                   void* Y, int32_t* acc_out, hipStream_t stream) {
+  constexpr int BM = 32 * TM;
+  const size_t lds = static_cast<size_t>(2) * BM * 8 * sizeof(uint4);
+  static int occ = 0;                          // resident workgroups per CU
+  if (occ == 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, sq_gemm_sk_kernel<TM, R, OUTK>, kGemmThreads, lds) !=
+            hipSuccess || o <= 0)
+      o = 1;
+    occ = std::min(o, 2);
+  }
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + kBN - 1) / kBN;
+  const long long tiles = static_cast<long long>(tiles_m) * tiles_n;
+  SkPlan plan;
+  plan.ksteps = (K + kBK - 1) / kBK;
+  plan.units = tiles * plan.ksteps;
+  plan.P = static_cast<int>(std::min<long long>(static_cast<long long>(occ) * device_cus(), plan.units));
+  Workspace w;
+  const qlin_status s = get_workspace(static_cast<size_t>(2) * plan.P * BM * kBN * sizeof(int),
+                                      static_cast<size_t>(tiles), stream, "sq_int8_gemm", &w);
+  if (s != QLIN_OK) return s;
+  hipLaunchKernelGGL((sq_gemm_sk_kernel<TM, R, OUTK>), dim3(plan.P), dim3(kGemmThreads), lds, stream, Xq, xsc, Wq,
+                     wsc, M, N, K, tiles_n, plan, Y, acc_out, reinterpret_cast<int*>(w.partials), w.counters);
+  return QLIN_OK;
+}
+
+template <int TM, int R>
+qlin_status gemm_o(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
+                   void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
+  return y_dtype == QLIN_F32 ? gemm_t<TM, R, OUT_F32>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream)
+                             : gemm_t<TM, R, OUT_F16>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
 }
 
 }  // namespace
@@ -234,15 +290,11 @@ void sq_act_launch(const uint16_t* X, const float* inv_s, int M, int K, int8_t* 
   hipLaunchKernelGGL(sq_act_kernel, dim3(M), dim3(kActThreads), 0, stream, X, inv_s, K, Xq, x_scale);
 }
 
-void sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
-                    int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
-  // Largest tile that still gives every CU a workgroup; small batches use one
-  // 32-row tile with the four waves side by side along N.
-  auto wgs = [&](int bm, int bn) { return static_cast<long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  if (M <= 32) gemm_t<1, 4, 1, 1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-  else if (wgs(128, 128) >= 256) gemm_t<2, 2, 2, 2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-  else if (wgs(64, 128) >= 256) gemm_t<2, 2, 1, 2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-  else gemm_t<2, 2, 1, 1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
+                           int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
+  if (M <= 32) return gemm_o<1, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+  if (M <= 64) return gemm_o<2, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+  return gemm_o<4, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
 }
 
 }  // namespace qlin

@@ -10,15 +10,15 @@
 //     rows of the tile and 32 output columns, so every packed word is turned into
 //     fp16 once and feeds TM matrix instructions;
 //   * B operand: a lane unpacks one word (8 codes of its column) per
-//     v_mfma_f32_32x32x16_f16 into the exact fp16 integers q - z, in natural k
+//     v_mfma_f32_32x32x16_f16 into fp16 weights s * (q - z), in natural k
 //     order: a byte permute + an and-or place each code in the mantissa of
-//     1024.0 and one packed fp16 subtraction removes 1024 + z.  No rounding;
+//     1024.0, one packed fp16 subtraction removes 1024 + z (exact) and one packed
+//     multiply by the group's fp16 scale rounds the weight once to fp16, as the
+//     GPTQ kernels do, so the matrix cores accumulate across groups directly;
 //   * A operand: the activation tile of one 128-wide K step, converted to fp16
 //     (bf16 inputs exactly, for values in the fp16 normal range) and stored in
 //     LDS as 256-byte rows whose 16-byte chunks are XOR-swizzled by the row, so
 //     the 32 rows an MFMA reads land in distinct banks; double buffered;
-//   * each K step's fp32 products are scaled by the group's fp16 scale into the
-//     running fp32 result (one fused multiply-add per output and step);
 //   * packed words, the group scale/zero and the activations are fetched R - 1
 //     K steps ahead into R-deep register rings (every load unconditional, so the
 //     compiler's in-order wait counts never drain the rings): with a few waves
@@ -44,8 +44,9 @@ constexpr int kThreads = 256;   // 4 waves along N
 constexpr int kBN = 128;        // output columns per tile
 constexpr int kKS = 128;        // K per step (16 packed words per column)
 
-// Eight fp16 values q - z in natural k order from one packed word.
-__device__ __forceinline__ h8_t dequant_nat(uint32_t w, h2_t zz) {
+// Eight fp16 weights s * (q - z) in natural k order from one packed word: q - z
+// is exact, the product by the fp16 scale is rounded once to fp16.
+__device__ __forceinline__ h8_t dequant_nat(uint32_t w, h2_t zz, h2_t ss) {
   const uint32_t t = w >> 4;
   h8_t b;
 #pragma unroll
@@ -53,7 +54,7 @@ __device__ __forceinline__ h8_t dequant_nat(uint32_t w, h2_t zz) {
     // byte j of w holds codes 2j (low nibble) and 2j + 1; t's byte j has code 2j + 1 low
     const uint32_t sel = static_cast<uint32_t>(j) | (0x0Cu << 8) | (static_cast<uint32_t>(4 + j) << 16) | (0x0Cu << 24);
     const uint32_t pr = __builtin_amdgcn_perm(t, w, sel);
-    const h2_t d = bitcast<h2_t>(and_or(pr, 0x000F000Fu, 0x64006400u)) - zz;   // exact
+    const h2_t d = (bitcast<h2_t>(and_or(pr, 0x000F000Fu, 0x64006400u)) - zz) * ss;
     b[2 * j] = d[0];
     b[2 * j + 1] = d[1];
   }
@@ -65,15 +66,6 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
   const float lo = bitcast<float>(u << 16);
   const float hi = bitcast<float>(u & 0xFFFF0000u);
   return bitcast<uint32_t>(__builtin_amdgcn_cvt_pkrtz(lo, hi));
-}
-
-// Calls f(step index I, kk) for I = 0 .. R-1 while kk < k1; false once the range is done.
-template <int I, int R, class F>
-__device__ __forceinline__ bool run_steps(F& f, int& kk, int k1) {
-  f(std::integral_constant<int, I>{}, kk);
-  if (++kk >= k1) return false;
-  if constexpr (I + 1 < R) return run_steps<I + 1, R>(f, kk, k1);
-  else return true;
 }
 
 template <int TM, int R, bool XBF16, int OUTK>
@@ -127,6 +119,8 @@ __global__ __launch_bounds__(kThreads) void w4_gemm_sk_kernel(
         v[j] = *reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K + s * kKS + 8 * c);
       }
     };
+    // Rows past M are loaded from row M - 1 and left in place: a row of A only
+    // feeds the same row of the product, and those rows are never stored.
     auto store_a = [&](uint4* dst, const uint4 (&src)[APT]) {
 #pragma unroll
       for (int j = 0; j < APT; ++j) {
@@ -139,11 +133,6 @@ __global__ __launch_bounds__(kThreads) void w4_gemm_sk_kernel(
           v.z = bf16x2_to_f16x2(v.z);
           v.w = bf16x2_to_f16x2(v.w);
         }
-        const bool live = m0 + r < M;
-        v.x = live ? v.x : 0u;
-        v.y = live ? v.y : 0u;
-        v.z = live ? v.z : 0u;
-        v.w = live ? v.w : 0u;
         dst[r * 16 + (c ^ (r & 15))] = v;
       }
     };
@@ -164,10 +153,14 @@ __global__ __launch_bounds__(kThreads) void w4_gemm_sk_kernel(
 
     // ---- prologue
     const int klast = k1 - 1;
+    // prologue in the steady-state issue order (weights of step j, then
+    // activations of step j + 1), so the wait counts agree at the loop head
+    load_a(k0, av[0]);
 #pragma unroll
-    for (int j = 0; j < R - 1; ++j) load_b(min(k0 + j, klast), bq[j], bs[j], bz[j]);
-#pragma unroll
-    for (int j = 0; j < R; ++j) load_a(min(k0 + j, klast), av[j]);
+    for (int j = 0; j < R - 1; ++j) {
+      load_b(min(k0 + j, klast), bq[j], bs[j], bz[j]);
+      load_a(min(k0 + j + 1, klast), av[j + 1]);
+    }
     store_a(As0, av[0]);
     __syncthreads();
 
@@ -181,28 +174,22 @@ __global__ __launch_bounds__(kThreads) void w4_gemm_sk_kernel(
       const uint32_t z = (bz[S] >> (4 * (g & 7))) & 15u;
       const _Float16 zb = static_cast<_Float16>(1024.0f + static_cast<float>(z));
       const h2_t zz = {zb, zb};
-      f32x16_t part[TM];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) part[i] = f32x16_t{};
+      const _Float16 sh = bitcast<_Float16>(static_cast<uint16_t>(bs[S]));
+      const h2_t ss = {sh, sh};
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const uint4 q4 = bq[S][st >> 2];
         const uint32_t w = (st & 3) == 0 ? q4.x : (st & 3) == 1 ? q4.y : (st & 3) == 2 ? q4.z : q4.w;
-        const h8_t b = dequant_nat(w, zz);
+        const h8_t b = dequant_nat(w, zz, ss);
         const int c = 8 * (st >> 2) + 4 * h + (st & 3);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           const h8_t a = bitcast<h8_t>(Ab[(32 * i + col) * 16 + (c ^ swz)]);
-          part[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, part[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[i], 0, 0, 0);
         }
       }
-      const float sc = f16_bits_to_f32(static_cast<uint16_t>(bs[S]));
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = fmaf(sc, part[i][r], acc[i][r]);
       // the next step's activations (past the range end this rewrites the idle
-      // buffer), then the fetch three steps ahead into the set of step kk
+      // buffer), then the fetch R steps ahead into the set of step kk
       // (emptied at the end of the previous step)
       constexpr int S1 = (S + 1) % R;
       store_a(((kk + 1 - k0) & 1) ? As1 : As0, av[S1]);
@@ -212,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void w4_gemm_sk_kernel(
     };
 
     int kk = k0;
-    while (run_steps<0, R>(step, kk, k1)) {
+    while (sk_run_steps<0, R>(step, kk, k1)) {
     }
 
     // ---- finish the tile: lane holds column n, rows 8*(r/4) + 4*h + r%4 of each 32-row block
