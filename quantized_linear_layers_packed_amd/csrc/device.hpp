@@ -66,6 +66,36 @@ __device__ __forceinline__ int xcd_tile(int b, int T) {
   return base + slot;
 }
 
+// ---------------------------------------------------------------------------
+// Direct global -> LDS loads (gfx950 global_load_lds_dwordx4).  Each lane reads
+// 16 bytes at its own global address; the wave's 64 pieces land contiguously at
+// lds_wave_base + 16 * lane (the LDS address must be the same for the whole
+// wave).  These count in vmcnt like ordinary loads but write no VGPR, so a ring
+// of stages in LDS carries no loop state in registers.
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+__device__ __forceinline__ void dma16(const void* global_src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((global_void_ptr)(const_cast<void*>(global_src)), (lds_void_ptr)(lds_wave_base),
+                                   16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt untouched).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also wait for every outstanding direct-to-LDS load); the empty asm keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_raw() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -13,10 +13,9 @@
 // equal the host definition bit for bit.
 //
 // GEMM kernel: v_mfma_i32_32x32x32_i8, exact int32 accumulation
-// (|acc| <= K * 127^2 < 2^31 for K <= 131072).  The token tile of Xq is staged
-// in LDS per 128-wide K step (double buffered) and shared by the waves; each
-// wave streams its own weight rows from HBM into MFMA operand registers, R - 1
-// K steps ahead.  Epilogue: float(acc) * x_scale[m] * w_scale[n], rounded once.
+// (|acc| <= K * 127^2 < 2^31 for K <= 131072).  The token tile of Xq and the
+// weight rows stream from HBM straight into a multi-stage LDS ring several K
+// steps ahead.  Epilogue: float(acc) * x_scale[m] * w_scale[n], rounded once.
 
 #include <algorithm>
 
@@ -88,31 +87,30 @@ constexpr int kBK = 128;            // K bytes per step (4 MFMA steps of 32)
 // Tiles of BM = 32 TM rows x 128 columns; a wave owns all BM rows and 32
 // columns.  Within one 128-byte K step, MFMA step st and lane half h use bytes
 // 64h + 16st .. +15 of both operands (a fixed permutation of k, identical for A
-// and B), so each lane streams 64 contiguous bytes of its weight row per step.
-// Activation rows go to LDS as 128-byte rows whose 16-byte chunks are
-// XOR-swizzled by row / 2, so the 32 rows an MFMA reads fall in distinct banks.
-// Weights and activations are fetched R - 1 steps ahead into register rings,
-// with every load unconditional (clamped addresses) so that the compiler's
-// in-order wait counts never drain the rings.  The (tile, K step) space is
-// split evenly over the workgroups (stream-K); shared tiles are summed (int32,
-// exact) by the last workgroup to finish them.
-template <int TM, int R, int OUTK>
+// and B).  Both operands stream from HBM straight into an NS-stage LDS ring
+// (direct-to-LDS loads, NS - 1 steps ahead, no registers involved); each
+// 128-byte row is stored with its 16-byte chunks XOR-swizzled by row / 2, which
+// the direct loads realise by choosing which global chunk each lane fetches, so
+// the 32 rows an MFMA reads fall in distinct banks.  One explicit vmcnt wait and
+// one barrier per step.  The (tile, K step) space is split evenly over the
+// workgroups (stream-K); shared tiles are summed (int32, exact) by the last
+// workgroup to finish them.
+template <int TM, int NS, int OUTK>
 __global__ __launch_bounds__(kGemmThreads) void sq_gemm_sk_kernel(
-    const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
-    int M, int N, int K, int tiles_n, SkPlan plan, void* Y, int32_t* acc_out, int* ws, int* counters) {
-  // (no __restrict__: it would let the prefetch loads be sunk across the step
-  // barriers to their first use)
+    const int8_t* __restrict__ Xq, const float* __restrict__ x_scale, const int8_t* __restrict__ Wq,
+    const float* __restrict__ w_scale, int M, int N, int K, int tiles_n, SkPlan plan, void* __restrict__ Y,
+    int32_t* __restrict__ acc_out, int* __restrict__ ws, int* __restrict__ counters) {
   constexpr int BM = 32 * TM;
-  constexpr int APT = BM * 8 / kGemmThreads;   // 16-byte activation pieces per thread per step
-  static_assert(APT >= 1, "tile too small");
+  constexpr int A_PIECES = BM * 8, B_PIECES = kBN * 8;         // 16-byte pieces per stage
+  constexpr int STAGE = A_PIECES + B_PIECES;
+  constexpr int DMA_PER_STAGE = TM + 4;                         // direct loads per wave per stage
   extern __shared__ uint4 smem[];
   __shared__ int s_last;
-  uint4* const As0 = smem;
-  uint4* const As1 = smem + BM * 8;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int col = lane & 31, h = lane >> 5;
-  const int swz = (col >> 1) & 7;
+  const int swz = (col >> 1) & 7;                               // swizzle of every row this lane reads
+  const int lrow = lane >> 3, lpos = lane & 7;                  // this lane's piece in a direct load
 
   const int p = xcd_tile(blockIdx.x, gridDim.x);
   long long u = sk_begin(plan, p);
@@ -124,83 +122,72 @@ __global__ __launch_bounds__(kGemmThreads) void sq_gemm_sk_kernel(
     const int k1 = static_cast<int>(std::min<long long>(plan.ksteps, k0 + (u_end - u)));
     const int klast = k1 - 1;
     const int m0 = (t / tiles_n) * BM;
-    const int n = (t % tiles_n) * kBN + 32 * wv + col;
+    const int nt0 = (t % tiles_n) * kBN;
+    const int n = nt0 + 32 * wv + col;
     const bool nok = n < N;
-    const size_t nn = static_cast<size_t>(min(n, N - 1));
-    const int8_t* wrow = Wq + nn * K;
 
-    // Activation rows past M are read from row M - 1 and never stored.  When
-    // K % 128 == 64 the last step is half full: its addresses are clamped into
-    // the row and its activation chunks past K are zeroed at staging, so the
-    // weight bytes they meet contribute nothing.
-    uint4 av[R][APT];
-    auto load_a = [&](int s, uint4 (&v)[APT]) {
+    // Direct loads for ring position j (slot j % NS) of the data of step s =
+    // min(j, klast).  Wave wv loads A row blocks wv*TM .. and B row blocks wv*4 ..
+    // (8 rows of 128 bytes per instruction).  Rows past M / N read the last row
+    // (their results are never stored); positions past the range re-read its last
+    // step into slots no step of the range reads again; chunks past K (half step)
+    // read the row's last chunk and meet zeroed activations.
+    auto issue = [&](int j) {
+      const int s = min(j, klast);
+      uint4* slot = smem + static_cast<size_t>(j % NS) * STAGE;
 #pragma unroll
-      for (int j = 0; j < APT; ++j) {
-        const int piece = tid + j * kGemmThreads;
-        const int r = piece >> 3, c = piece & 7;
-        const int m = min(m0 + r, M - 1);
-        const int kb = min(s * kBK + 16 * c, K - 16);
-        v[j] = *reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(m) * K + kb);
+      for (int j = 0; j < TM; ++j) {
+        const int rb = wv * TM + j;
+        const int row = 8 * rb + lrow;
+        const int c = lpos ^ ((row >> 1) & 7);
+        const int m = min(m0 + row, M - 1);
+        dma16(Xq + static_cast<size_t>(m) * K + min(s * kBK + 16 * c, K - 16), slot + 64 * rb);
       }
-    };
-    auto store_a = [&](uint4* dst, const uint4 (&src)[APT], int s) {
-      const bool tail = s * kBK + kBK > K;      // uniform
 #pragma unroll
-      for (int j = 0; j < APT; ++j) {
-        const int piece = tid + j * kGemmThreads;
-        const int r = piece >> 3, c = piece & 7;
-        uint4 v = src[j];
-        if (tail && s * kBK + 16 * c >= K) v = make_uint4(0u, 0u, 0u, 0u);
-        dst[r * 8 + (c ^ ((r >> 1) & 7))] = v;
+      for (int j = 0; j < 4; ++j) {
+        const int rb = wv * 4 + j;
+        const int row = 8 * rb + lrow;
+        const int c = lpos ^ ((row >> 1) & 7);
+        const int nn = min(nt0 + row, N - 1);
+        dma16(Wq + static_cast<size_t>(nn) * K + min(s * kBK + 16 * c, K - 16), slot + A_PIECES + 64 * rb);
       }
-    };
-    uint4 bq[R][4];
-    auto load_b = [&](int s, uint4 (&w)[4]) {
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        w[st] = *reinterpret_cast<const uint4*>(wrow + min(s * kBK + 64 * h + 16 * st, K - 16));
     };
 
     i32x16_t acc[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) acc[i] = i32x16_t{};
 
-    // prologue in the steady-state issue order (weights of step j, then
-    // activations of step j + 1), so the wait counts agree at the loop head
-    load_a(k0, av[0]);
 #pragma unroll
-    for (int j = 0; j < R - 1; ++j) {
-      load_b(min(k0 + j, klast), bq[j]);
-      load_a(min(k0 + j + 1, klast), av[j + 1]);
-    }
-    store_a(As0, av[0], k0);
-    __syncthreads();
+    for (int j = 0; j < NS - 1; ++j) issue(k0 + j);
 
-    auto step = [&](auto set_c, int kk) {
-      constexpr int S = decltype(set_c)::value;
-      constexpr int SB = (S + R - 1) % R;
-      load_b(min(kk + R - 1, klast), bq[SB]);
-      __builtin_amdgcn_sched_barrier(0);
-      const uint4* Ab = ((kk - k0) & 1) ? As1 : As0;
+    for (int kk = k0; kk < k1; ++kk) {
+      wait_vmcnt<(NS - 2) * DMA_PER_STAGE>();                   // this wave's loads of step kk
+      barrier_raw();                                            // everyone's; step kk - 1 finished
+      const uint4* slot = smem + static_cast<size_t>(kk % NS) * STAGE;
+      if (kk * kBK + kBK > K) {                                 // half step: zero A chunks past K
+        uint4* a = const_cast<uint4*>(slot);
+        for (int q = tid; q < BM * 4; q += kGemmThreads) {
+          const int row = q >> 2, c = 4 + (q & 3);
+          a[row * 8 + (c ^ ((row >> 1) & 7))] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        __syncthreads();
+      }
+      issue(kk + NS - 1);
+      const uint4* As = slot;
+      const uint4* Bs = slot + A_PIECES + (32 * wv + col) * 8;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const i32x4_t b = bitcast<i32x4_t>(bq[S][st]);
         const int c = 4 * h + st;
+        const i32x4_t b = bitcast<i32x4_t>(Bs[c ^ swz]);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const i32x4_t a = bitcast<i32x4_t>(Ab[(32 * i + col) * 8 + (c ^ swz)]);
+          const i32x4_t a = bitcast<i32x4_t>(As[(32 * i + col) * 8 + (c ^ swz)]);
           acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[i], 0, 0, 0);
         }
       }
-      store_a(((kk + 1 - k0) & 1) ? As1 : As0, av[(S + 1) % R], kk + 1);
-      load_a(min(kk + R, klast), av[S]);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-    };
-    int kk = k0;
-    while (sk_run_steps<0, R>(step, kk, k1)) {
     }
+    wait_vmcnt<0>();                                            // loads past the range end
+    __syncthreads();
 
     // ---- finish the tile: lane holds column n, rows 8*(r/4) + 4*h + r%4 of each 32-row block
     bool write = true;
@@ -221,16 +208,26 @@ __global__ __launch_bounds__(kGemmThreads) void sq_gemm_sk_kernel(
         for (int q = first; q <= last; ++q) {
           if (q == p) continue;
           const int* other = ws + static_cast<size_t>(sk_slot(plan, q, t)) * (BM * kBN);
+          int part[TM][16];                     // issue all loads, then add (one wait)
 #pragma unroll
           for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][r] += sk_load(other + ((wv * TM + i) * 16 + r) * 64 + lane);
+            for (int r = 0; r < 16; ++r) part[i][r] = sk_load(other + ((wv * TM + i) * 16 + r) * 64 + lane);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][r] += part[i][r];
         }
         if (tid == 0) sk_reset(&counters[t]);
       }
     }
     if (write && nok) {
       const float wsc = w_scale[n];
+      float xsc[TM][16];                        // row scales first (clamped rows, no branches)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xsc[i][r] = x_scale[min(m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3), M - 1)];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -238,7 +235,7 @@ __global__ __launch_bounds__(kGemmThreads) void sq_gemm_sk_kernel(
           const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
           if (m < M) {
             const size_t idx = static_cast<size_t>(m) * N + n;
-            store_out<OUTK>(Y, idx, static_cast<float>(acc[i][r]) * x_scale[m] * wsc);
+            store_out<OUTK>(Y, idx, static_cast<float>(acc[i][r]) * xsc[i][r] * wsc);
             if (acc_out) acc_out[idx] = acc[i][r];
           }
         }
@@ -247,15 +244,17 @@ __global__ __launch_bounds__(kGemmThreads) void sq_gemm_sk_kernel(
   }
 }
 
-template <int TM, int R, int OUTK>
+template <int TM, int NS, int OUTK>
 qlin_status gemm_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
                    void* Y, int32_t* acc_out, hipStream_t stream) {
   constexpr int BM = 32 * TM;
-  const size_t lds = static_cast<size_t>(2) * BM * 8 * sizeof(uint4);
+  const size_t lds = static_cast<size_t>(NS) * (BM + kBN) * 8 * sizeof(uint4);
   static int occ = 0;                          // resident workgroups per CU
   if (occ == 0) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sq_gemm_sk_kernel<TM, NS, OUTK>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, sq_gemm_sk_kernel<TM, R, OUTK>, kGemmThreads, lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, sq_gemm_sk_kernel<TM, NS, OUTK>, kGemmThreads, lds) !=
             hipSuccess || o <= 0)
       o = 1;
     occ = std::min(o, 2);
@@ -271,16 +270,16 @@ qlin_status gemm_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const f
   const qlin_status s = get_workspace(static_cast<size_t>(2) * plan.P * BM * kBN * sizeof(int),
                                       static_cast<size_t>(tiles), stream, "sq_int8_gemm", &w);
   if (s != QLIN_OK) return s;
-  hipLaunchKernelGGL((sq_gemm_sk_kernel<TM, R, OUTK>), dim3(plan.P), dim3(kGemmThreads), lds, stream, Xq, xsc, Wq,
+  hipLaunchKernelGGL((sq_gemm_sk_kernel<TM, NS, OUTK>), dim3(plan.P), dim3(kGemmThreads), lds, stream, Xq, xsc, Wq,
                      wsc, M, N, K, tiles_n, plan, Y, acc_out, reinterpret_cast<int*>(w.partials), w.counters);
   return QLIN_OK;
 }
 
-template <int TM, int R>
+template <int TM, int NS>
 qlin_status gemm_o(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
                    void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
-  return y_dtype == QLIN_F32 ? gemm_t<TM, R, OUT_F32>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream)
-                             : gemm_t<TM, R, OUT_F16>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+  return y_dtype == QLIN_F32 ? gemm_t<TM, NS, OUT_F32>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream)
+                             : gemm_t<TM, NS, OUT_F16>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
 }
 
 }  // namespace
@@ -292,8 +291,9 @@ void sq_act_launch(const uint16_t* X, const float* inv_s, int M, int K, int8_t* 
 
 qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
                            int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
-  if (M <= 32) return gemm_o<1, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-  if (M <= 64) return gemm_o<2, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+  // ring depth within 160 KB of LDS: stage = (32 TM + 128) rows x 128 bytes
+  if (M <= 32) return gemm_o<1, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+  if (M <= 64) return gemm_o<2, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
   return gemm_o<4, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
 }
 

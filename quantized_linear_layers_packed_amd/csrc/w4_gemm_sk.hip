@@ -227,10 +227,15 @@ __global__ __launch_bounds__(kThreads) void w4_gemm_sk_kernel(
             for (int i = 0; i < TM; ++i) tot[i] += acc[i];
           } else {
             const float* other = ws + static_cast<size_t>(sk_slot(plan, q, t)) * (BM * kBN);
+            float part[TM][16];                 // issue all loads, then add (one wait)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) tot[i][r] += sk_load(other + ((wv * TM + i) * 16 + r) * 64 + lane);
+              for (int r = 0; r < 16; ++r) part[i][r] = sk_load(other + ((wv * TM + i) * 16 + r) * 64 + lane);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) tot[i][r] += part[i][r];
           }
         }
 #pragma unroll
