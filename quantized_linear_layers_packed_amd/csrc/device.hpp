@@ -136,23 +136,53 @@ __device__ __forceinline__ uint32_t and_or_v(uint32_t a, uint32_t m, uint32_t c)
   return r;
 }
 
+// Unpacked codes for the GEMV's fp16 dot products.  Register j of a word holds
+// the codes of k = j and k = j + 4 (the pairs the activation staging builds).
+//
+// fp16 activations: one shift and four and-ors.  Registers 0 and 2 take the
+// low nibble of each byte into mantissa bits 0..3 of 1024.0 (value 1024 + q),
+// registers 1 and 3 the high nibble into bits 4..7 (value 1024 + 16 q).  The
+// staging divides the activations paired with registers 1 and 3 by 16 (exact
+// in fp16 above 2^-10) so one dot-product chain gives
+//   acc = sum x q + 1024 sum_{0,2} x + 64 sum_{1,3} x,
+// and a chunk's sum x (q - z) = acc - (E + z S), E = 1024 (se + so),
+// S = se + 16 so with se / so the chunk's sums over registers 0, 2 / the scaled
+// 1, 3 (staging computes both).
 struct W4F16 {
-  static constexpr uint32_t MAGIC = 0x64006400u, MASK = 0x00F000F0u;
-  static constexpr float B_OVER_D = 64.0f, INV_D = 0.0625f;
+  static constexpr uint32_t MAGIC = 0x64006400u;
   __device__ __forceinline__ static void unpack(uint32_t w, uint32_t p[4]) {
-    const uint32_t mask = MASK;
-    p[0] = and_or(w << 4, mask, MAGIC);
-    p[1] = and_or(w, mask, MAGIC);
-    p[2] = and_or(w >> 4, mask, MAGIC);
-    p[3] = and_or(w >> 8, mask, MAGIC);
+    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u;
+    const uint32_t w8 = w >> 8;
+    p[0] = and_or(w, lo, MAGIC);
+    p[1] = and_or(w, hi, MAGIC);
+    p[2] = and_or(w8, lo, MAGIC);
+    p[3] = and_or(w8, hi, MAGIC);
   }
-  __device__ __forceinline__ static uint32_t code_of(uint16_t half) { return (half >> 4) & 15u; }
+  __device__ __forceinline__ static uint32_t code_of(int j, uint16_t half) {
+    return (j & 1) ? (half >> 4) & 15u : half & 15u;
+  }
   __device__ __forceinline__ static float dot(uint32_t a, uint32_t b, float c) { return dot2_f16(a, b, c); }
+  // scale the odd pairs by 1/16 and accumulate (se, so) with dot products by (1, 1)
+  __device__ __forceinline__ static void stage(uint32_t P[4], float2& es) {
+    const h2_t sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+    P[1] = bitcast<uint32_t>(bitcast<h2_t>(P[1]) * sixteenth);
+    P[3] = bitcast<uint32_t>(bitcast<h2_t>(P[3]) * sixteenth);
+    es.x = dot2_f16(P[0], 0x3C003C00u, es.x);
+    es.x = dot2_f16(P[2], 0x3C003C00u, es.x);
+    es.y = dot2_f16(P[1], 0x3C003C00u, es.y);
+    es.y = dot2_f16(P[3], 0x3C003C00u, es.y);
+  }
+  __device__ __forceinline__ static float2 sums(float2 es) {
+    return make_float2(1024.0f * (es.x + es.y), fmaf(16.0f, es.y, es.x));
+  }
+  __device__ __forceinline__ static float finish(float acc, float2 es, float z) { return acc - fmaf(z, es.y, es.x); }
 };
 
+// bf16 activations: every code goes to mantissa bits 3..6 of 128.0 (value
+// 128 + 8 q; a bf16 mantissa has no room for the high-nibble trick):
+//   sum x (q - z) = acc / 8 - (16 + z) sum x.
 struct W4BF16 {
   static constexpr uint32_t MAGIC = 0x43004300u, MASK = 0x00780078u;
-  static constexpr float B_OVER_D = 16.0f, INV_D = 0.125f;
   __device__ __forceinline__ static void unpack(uint32_t w, uint32_t p[4]) {
     const uint32_t mask = MASK;
     p[0] = and_or(w << 3, mask, MAGIC);
@@ -160,8 +190,16 @@ struct W4BF16 {
     p[2] = and_or(w >> 5, mask, MAGIC);
     p[3] = and_or(w >> 9, mask, MAGIC);
   }
-  __device__ __forceinline__ static uint32_t code_of(uint16_t half) { return (half >> 3) & 15u; }
+  __device__ __forceinline__ static uint32_t code_of(int, uint16_t half) { return (half >> 3) & 15u; }
   __device__ __forceinline__ static float dot(uint32_t a, uint32_t b, float c) { return dot2_bf16(a, b, c); }
+  __device__ __forceinline__ static void stage(uint32_t P[4], float2& es) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) es.x = dot2_bf16(P[j], 0x3F803F80u, es.x);
+  }
+  __device__ __forceinline__ static float2 sums(float2 es) { return make_float2(0.0f, es.x); }
+  __device__ __forceinline__ static float finish(float acc, float2 es, float z) {
+    return fmaf(acc, 0.125f, -(16.0f + z) * es.y);
+  }
 };
 
 // Activation pairs matching the unpack order above: from 8 consecutive 16-bit

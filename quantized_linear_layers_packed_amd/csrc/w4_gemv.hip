@@ -34,105 +34,138 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t v, int src) {
   return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(v)));
 }
 
-// One wavefront per output row; lane l reads chunks l, l + 64, ... so every load
-// instruction covers 1 KB of contiguous packed words.  Per row the wave loads
-// its scales and zero words once, coalesced (lane i holds scale i + 64t and
-// zero word i); each chunk then picks its group's values with a cross-lane
-// read instead of two more memory instructions.  The activation loads for the
-// LDS staging are issued before the weight loads (vector loads return in order)
-// so the staging overlaps the weight stream.
-template <int MT, int BPL, typename Codec, bool XBF16, int OUTK>
+// Sum over each group of LPR lanes (16, 32 or 64) with DPP: the group's total
+// ends up in its last lane.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  auto dpp = [](float x, int ctrl, int row_mask) -> float {
+    switch (ctrl) {   // the control must be a constant expression
+      case 0xB1: return bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(x), 0xB1, 0xF, 0xF, true));
+      case 0x4E: return bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(x), 0x4E, 0xF, 0xF, true));
+      case 0x141: return bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(x), 0x141, 0xF, 0xF, true));
+      case 0x140: return bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(x), 0x140, 0xF, 0xF, true));
+      case 0x142: return bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(x), 0x142, 0xA, 0xF, false));
+      default: return bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(x), 0x143, 0xC, 0xF, false));
+    }
+    (void)row_mask;
+  };
+  v += dpp(v, 0xB1, 0xF);      // quad_perm [1,0,3,2]: pairs
+  v += dpp(v, 0x4E, 0xF);      // quad_perm [2,3,0,1]: quads
+  v += dpp(v, 0x141, 0xF);     // row_half_mirror: groups of 8
+  v += dpp(v, 0x140, 0xF);     // row_mirror: rows of 16 (every lane of the row)
+  if constexpr (LPR >= 32) v += dpp(v, 0x142, 0xA);   // row_bcast:15 into rows 1 and 3
+  if constexpr (LPR >= 64) v += dpp(v, 0x143, 0xC);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// A wave serves RPW = 64 / LPR output rows; the LPR lanes of a row read chunks
+// l, l + LPR, ... so every load instruction covers LPR x 16 contiguous bytes
+// of each of its rows.  Per row the lanes load its scales and zero words once,
+// coalesced (lane i of the row holds scale i + LPR t and zero word i); each
+// chunk then picks its group's values with a cross-lane read instead of two
+// more memory instructions.  The activation loads for the LDS staging are
+// issued before the weight loads (vector loads return in order) so the staging
+// overlaps the weight stream.  Per chunk the staging stores the 16 activation
+// pairs and two sums (Codec::sums); a chunk's sum of x (q - z) is then
+// acc - (E + z S) with the chunk's (E, S), acc the dot products with the
+// unpacked codes.
+template <int MT, int LPR, int KS, int BPL, typename Codec, int OUTK>
 __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
     const uint16_t* __restrict__ X, int M, int K,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
-    const uint32_t* __restrict__ qzeros, int N, int G, void* __restrict__ Y) {
+    const uint32_t* __restrict__ qzeros, int N, int gshift, void* __restrict__ Y) {
+  constexpr int RPW = 64 / LPR;
+  static_assert(KS == 1 || LPR == 64, "K split across waves needs whole-wave rows");
   extern __shared__ uint4 smem[];
+  __shared__ float red[kWaves][MT];            // per-wave partial sums (K split)
   const int C = K >> 5;                        // chunks per row
   uint4* xl = smem;                            // [MT][4][C] activation pairs
-  float* xs = reinterpret_cast<float*>(smem + static_cast<size_t>(MT) * 4 * C);   // [MT][C]
+  float2* xs = reinterpret_cast<float2*>(smem + MT * 4 * C);   // [MT][C] (E, S)
 
-  const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int sub = lane / LPR, sl = lane % LPR;
+  const int wv = tid >> 6;
+  const int part = wv % KS;                    // this wave's share of the row's chunks
+  const int n = (blockIdx.x * (kWaves / KS) + wv / KS) * RPW + sub;
   const bool nok = n < N;
-  const int ng = K / G, nzw = (ng + 7) >> 3;
-  const int cshift = __builtin_ctz(static_cast<unsigned>(G >> 5));
+  const int ng = K >> gshift, nzw = (ng + 7) >> 3;
+  const int cshift = gshift - 5;               // chunk -> group
 
-  // ---- 1. activation loads for the staging (up to two 32-value items per thread)
-  const int items = M * C;
+  // ---- 1. activation loads for the staging: chunk tid of batch rows 0 and 1
+  //      (C <= 512 = threads, so each thread stages at most one chunk per row)
+  const bool stager = tid < C;
   uint4 xv[2][4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int it = threadIdx.x + q * kThreads;
-    if (it < items) {
-      const int m = it / C, c = it - m * C;
-      const uint4* src = reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K) + 4 * c;
+  for (int m = 0; m < 2; ++m) {
+    if (m < M && stager) {
+      const uint4* src = reinterpret_cast<const uint4*>(X + m * K) + 4 * tid;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[q][i] = src[i];
+      for (int i = 0; i < 4; ++i) xv[m][i] = src[i];
     }
   }
 
-  // ---- 2. weights, then this row's scales and zero words
-  const size_t nn = nok ? static_cast<size_t>(n) : 0;
+  // ---- 2. weights, then the row's scales and zero words (rows past N read row N - 1)
+  const size_t nn = static_cast<size_t>(min(n, N - 1));
   const uint4* qrow = reinterpret_cast<const uint4*>(qweight + nn * (K >> 3));
+  // chunk of block b: LPR (KS b + part) + sl (the KS waves of a row interleave
+  // their blocks of LPR chunks)
   uint4 w[BPL];
 #pragma unroll
   for (int b = 0; b < BPL; ++b) {
-    const int c = 64 * b + lane;
-    if (nok && c < C) w[b] = load_stream16(qrow + c);
+    const int c = LPR * (KS * b + part) + sl;
+    if (c < C) w[b] = load_stream16(qrow + c);
   }
-  // scale registers: lane i of register t holds the scale of group 64t + i
-  // (a row has at most one group per chunk, so BPL registers always suffice)
-  constexpr int SV = BPL;
+  // scale registers: lane i of the row, register t, holds the scale of group
+  // LPR t + i (a row has at most one group per chunk, so KS * BPL registers suffice)
+  constexpr int SV = KS * BPL;
   uint32_t sv[SV];
-  uint32_t zv = 0;
   const uint16_t* srow = scales + nn * ng;
 #pragma unroll
   for (int t = 0; t < SV; ++t) {
-    const int g = 64 * t + lane;
+    const int g = LPR * t + sl;
     sv[t] = 0u;
-    if (64 * t < ng && nok && g < ng) sv[t] = static_cast<uint32_t>(srow[g]);
+    if (LPR * t < ng && g < ng) sv[t] = static_cast<uint32_t>(srow[g]);
   }
-  if (nok && lane < nzw) zv = qzeros[nn * nzw + lane];
+  uint32_t zv = 0u;                            // nzw <= LPR for the shapes that pick LPR
+  if (sl < nzw) zv = qzeros[nn * nzw + sl];
 
   // ---- 3. finish staging the activations
-  for (int q = 0; q * kThreads < items; ++q) {
-    const int it = threadIdx.x + q * kThreads;
-    if (it < items) {
-      const int m = it / C, c = it - m * C;
+  if (stager) {
+    for (int m = 0; m < M; ++m) {
       uint4 v4[4];
-      if (q < 2) {
+      if (m < 2) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = xv[q & 1][i];
+        for (int i = 0; i < 4; ++i) v4[i] = xv[m & 1][i];
       } else {
-        const uint4* src = reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K) + 4 * c;
+        const uint4* src = reinterpret_cast<const uint4*>(X + m * K) + 4 * tid;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v4[i] = src[i];
       }
-      // sum of the 32 activations: dot products with (1, 1) pairs
-      const uint32_t ones = XBF16 ? 0x3F803F80u : 0x3C003C00u;
-      float sum = 0.0f;
+      float2 es = make_float2(0.0f, 0.0f);
+      uint4 pq[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t u[4] = {v4[i].x, v4[i].y, v4[i].z, v4[i].w};
         uint32_t P[4];
         pair_up(u, P);
-        xl[(static_cast<size_t>(m) * 4 + i) * C + c] = make_uint4(P[0], P[1], P[2], P[3]);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sum = Codec::dot(u[jj], ones, sum);
+        Codec::stage(P, es);
+        pq[i] = make_uint4(P[0], P[1], P[2], P[3]);
       }
-      xs[m * C + c] = sum;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xl[(m * 4 + i) * C + tid] = pq[i];
+      xs[m * C + tid] = Codec::sums(es);
     }
   }
-  __syncthreads();
-  if (!nok) return;
-
-  // ---- 4. compute
-  float res[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) res[m] = 0.0f;
+  // ---- 4. unpack the codes and look up the groups' scales and zero points
+  //      while the activation staging is still in flight (this needs only the
+  //      weights), then the dot products once the staged activations are visible
+  const int base = sub * LPR;                  // first lane of this row
+  uint32_t p[BPL][4][4];
+  float s[BPL], zf[BPL];
 #pragma unroll
   for (int b = 0; b < BPL; ++b) {
-    const int c = 64 * b + lane;
+    const int c = LPR * (KS * b + part) + sl;
     // cross-lane reads with every lane active (a read from a lane that is
     // inactive in a divergent branch returns 0): lanes past the row end read
     // the last group's values and discard them
@@ -140,81 +173,115 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
     uint32_t sbits = 0;
 #pragma unroll
     for (int t = 0; t < SV; ++t) {
-      if (64 * t < ng) {                             // uniform: registers holding real groups
-        const uint32_t v = lane_value(sv[t], g & 63);
-        if ((g >> 6) == t) sbits = v;
+      if (LPR * t < ng) {                            // uniform: registers holding real groups
+        const uint32_t v = lane_value(sv[t], base + g % LPR);
+        if (g / LPR == t) sbits = v;
       }
     }
-    const uint32_t zw = lane_value(zv, g >> 3);
+    const uint32_t zw = lane_value(zv, base + (g >> 3));
+    s[b] = f16_bits_to_f32(static_cast<uint16_t>(sbits));
+    zf[b] = static_cast<float>((zw >> (4 * (g & 7))) & 15u);
     if (c < C) {
-      const float s = f16_bits_to_f32(static_cast<uint16_t>(sbits));
-      const float zc = Codec::B_OVER_D + static_cast<float>((zw >> (4 * (g & 7))) & 15u);
-      uint32_t p[4][4];
-      Codec::unpack(w[b].x, p[0]);
-      Codec::unpack(w[b].y, p[1]);
-      Codec::unpack(w[b].z, p[2]);
-      Codec::unpack(w[b].w, p[3]);
+      Codec::unpack(w[b].x, p[b][0]);
+      Codec::unpack(w[b].y, p[b][1]);
+      Codec::unpack(w[b].z, p[b][2]);
+      Codec::unpack(w[b].w, p[b][3]);
+    }
+  }
+  __syncthreads();                             // staged activations visible
+
+  float res[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) res[m] = 0.0f;
+#pragma unroll
+  for (int b = 0; b < BPL; ++b) {
+    const int c = LPR * (KS * b + part) + sl;
+    if (c < C) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m < M) {
           float acc = 0.0f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const uint4 xp = xl[(static_cast<size_t>(m) * 4 + i) * C + c];
-            acc = Codec::dot(p[i][0], xp.x, acc);
-            acc = Codec::dot(p[i][1], xp.y, acc);
-            acc = Codec::dot(p[i][2], xp.z, acc);
-            acc = Codec::dot(p[i][3], xp.w, acc);
+            const uint4 xp = xl[(m * 4 + i) * C + c];
+            acc = Codec::dot(p[b][i][0], xp.x, acc);
+            acc = Codec::dot(p[b][i][1], xp.y, acc);
+            acc = Codec::dot(p[b][i][2], xp.z, acc);
+            acc = Codec::dot(p[b][i][3], xp.w, acc);
           }
-          const float t = fmaf(acc, Codec::INV_D, -zc * xs[m * C + c]);
-          res[m] = fmaf(s, t, res[m]);
+          res[m] = fmaf(s[b], Codec::finish(acc, xs[m * C + c], zf[b]), res[m]);
         }
       }
     }
   }
-  // ---- 5. reduce over the wave and store
+  // ---- 5. reduce over each row's lanes (the row's last lane holds the sum),
+  //      then over the KS waves of the row in a fixed order, and store
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     if (m < M) {
-      const float v = wave_sum(res[m]);
-      if (lane == 0) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, v);
+      const float v = group_sum<LPR>(res[m]);
+      if constexpr (KS == 1) {
+        if (sl == LPR - 1 && nok) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, v);
+      } else {
+        if (lane == 63) red[wv][m] = v;
+      }
+    }
+  }
+  if constexpr (KS > 1) {
+    __syncthreads();
+    if (part == 0 && lane == 63 && nok) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < M) {
+          float v = red[wv][m];
+#pragma unroll
+          for (int q = 1; q < KS; ++q) v += red[wv + q][m];
+          store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, v);
+        }
+      }
     }
   }
 }
 
-template <int MT, int BPL, typename Codec, bool XBF16, int OUTK>
+template <int MT, int LPR, int KS, int BPL, typename Codec, int OUTK>
 void launch_t(const W4Args& a, hipStream_t stream) {
+  constexpr int RPW = 64 / LPR;
+  constexpr int ROWS = kWaves / KS * RPW;      // output rows per workgroup
   const int C = a.K >> 5;
-  const size_t lds = static_cast<size_t>(MT) * 4 * C * 16 + static_cast<size_t>(MT) * C * 4;
-  const int grid = (a.N + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL((w4_gemv_kernel<MT, BPL, Codec, XBF16, OUTK>), dim3(grid), dim3(kThreads), lds, stream,
-                     static_cast<const uint16_t*>(a.X), a.M, a.K, a.qweight, a.scales, a.qzeros, a.N, a.G, a.Y);
+  const size_t lds = static_cast<size_t>(MT) * 4 * C * 16 + static_cast<size_t>(MT) * C * 8;
+  const int grid = (a.N + ROWS - 1) / ROWS;
+  const int gshift = __builtin_ctz(static_cast<unsigned>(a.G));
+  hipLaunchKernelGGL((w4_gemv_kernel<MT, LPR, KS, BPL, Codec, OUTK>), dim3(grid), dim3(kThreads), lds, stream,
+                     static_cast<const uint16_t*>(a.X), a.M, a.K, a.qweight, a.scales, a.qzeros, a.N, gshift, a.Y);
 }
 
-template <int MT, int BPL>
+template <int MT, int LPR, int KS, int BPL>
 void launch_b(const W4Args& a, hipStream_t stream) {
   const bool bf = a.x_dtype == QLIN_BF16;
   const int ok = a.y_dtype == QLIN_F16 ? OUT_F16 : (a.y_dtype == QLIN_BF16 ? OUT_BF16 : OUT_F32);
   if (!bf) {
-    if (ok == OUT_F16) launch_t<MT, BPL, W4F16, false, OUT_F16>(a, stream);
-    else if (ok == OUT_BF16) launch_t<MT, BPL, W4F16, false, OUT_BF16>(a, stream);
-    else launch_t<MT, BPL, W4F16, false, OUT_F32>(a, stream);
+    if (ok == OUT_F16) launch_t<MT, LPR, KS, BPL, W4F16, OUT_F16>(a, stream);
+    else if (ok == OUT_BF16) launch_t<MT, LPR, KS, BPL, W4F16, OUT_BF16>(a, stream);
+    else launch_t<MT, LPR, KS, BPL, W4F16, OUT_F32>(a, stream);
   } else {
-    if (ok == OUT_F16) launch_t<MT, BPL, W4BF16, true, OUT_F16>(a, stream);
-    else if (ok == OUT_BF16) launch_t<MT, BPL, W4BF16, true, OUT_BF16>(a, stream);
-    else launch_t<MT, BPL, W4BF16, true, OUT_F32>(a, stream);
+    if (ok == OUT_F16) launch_t<MT, LPR, KS, BPL, W4BF16, OUT_F16>(a, stream);
+    else if (ok == OUT_BF16) launch_t<MT, LPR, KS, BPL, W4BF16, OUT_BF16>(a, stream);
+    else launch_t<MT, LPR, KS, BPL, W4BF16, OUT_F32>(a, stream);
   }
 }
 
 template <int MT>
 void launch_m(const W4Args& a, hipStream_t stream) {
-  // blocks of 64 chunks per row (one per lane); the whole row is held in flight
+  // One row per wave, 64 lanes; rows with more than two blocks of 64 chunks are
+  // split over KS waves (at most 4 blocks per wave, so the unpacked codes of the
+  // wave fit in registers and the per-wave tail after the activations arrive
+  // stays short).  Rows per wave and fewer lanes per row were measured slower.
   const int blocks = ((a.K >> 5) + 63) / 64;
-  if (blocks <= 1) launch_b<MT, 1>(a, stream);
-  else if (blocks <= 2) launch_b<MT, 2>(a, stream);
-  else if (blocks <= 4) launch_b<MT, 4>(a, stream);
-  else if (blocks <= 6) launch_b<MT, 6>(a, stream);
-  else launch_b<MT, 8>(a, stream);
+  if (blocks <= 1) launch_b<MT, 64, 1, 1>(a, stream);
+  else if (blocks <= 2) launch_b<MT, 64, 1, 2>(a, stream);
+  else if (blocks <= 4) launch_b<MT, 64, 2, 2>(a, stream);
+  else if (blocks <= 6) launch_b<MT, 64, 2, 3>(a, stream);
+  else launch_b<MT, 64, 2, 4>(a, stream);
 }
 
 // Debug: codes recovered from the same and-or unpack the GEMV uses (the pair
@@ -229,8 +296,8 @@ __global__ void w4_unpack_kernel(const uint32_t* __restrict__ qweight, const uin
     uint8_t* dst = codes + i * 8;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      dst[j] = static_cast<uint8_t>(W4F16::code_of(static_cast<uint16_t>(p[j])));
-      dst[j + 4] = static_cast<uint8_t>(W4F16::code_of(static_cast<uint16_t>(p[j] >> 16)));
+      dst[j] = static_cast<uint8_t>(W4F16::code_of(j, static_cast<uint16_t>(p[j])));
+      dst[j + 4] = static_cast<uint8_t>(W4F16::code_of(j, static_cast<uint16_t>(p[j] >> 16)));
     }
   }
   const int ng = K / G, nzw = (ng + 7) >> 3;
@@ -253,7 +320,7 @@ void w4_unpack_launch(const uint32_t* qweight, const uint32_t* qzeros, int N, in
 size_t w4_gemv_lds_bytes(int M, int K) {
   const size_t MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
   const size_t C = static_cast<size_t>(K) / 32;
-  return MT * 4 * C * 16 + MT * C * 4;
+  return MT * 4 * C * 16 + MT * C * 8;
 }
 
 bool w4_gemv_supported(int M, int K, int G) {
