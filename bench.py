@@ -14,9 +14,9 @@ The same run also times, each on its own workload (field "paths"):
 and the CPU oracle on a bounded sample ("cpu_baseline").
 
 Timing uses HIP events on the stream the kernels run on: one event pair around
-the K timed steps gives ms_per_step; a second pass with an event pair around
-every launch gives each kernel's average duration, from which the roofline
-figures are derived.
+the K timed steps (replayed as a HIP graph) gives ms_per_step; each kernel's
+average duration comes from a graph holding only that kernel's launches over the
+weight rotation, timed the same way, and gives the roofline figures.
 """
 from __future__ import annotations
 
@@ -68,30 +68,21 @@ def copies_for(bytes_per_set):
     return max(2, -(-ROTATE_BYTES // max(1, bytes_per_set)))
 
 
-def time_steps(torch, step_fns, steps, warmup, copies):
-    """Time ``steps`` steps; return (ms per step, per-launch average ms list).
-
-    step_fns: callables; step i runs every callable with argument i (i selects
-    the weight copy).  The timed steps replay a HIP graph holding one full
-    rotation (``copies`` steps), so host launch overhead stays out of the
-    measurement.  Per-launch durations come from an eager pass with an event
-    pair around every launch, queued behind a GPU sleep so that the host is
-    ahead of the device and the events bracket only the kernels."""
-    for i in range(warmup):
-        for f in step_fns:
-            f(i)
-    torch.cuda.synchronize()
+def _graph(torch, body):
+    """Capture body() into a HIP graph on a side stream; return the graph."""
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
         with torch.cuda.graph(graph, stream=cap):
-            for i in range(copies):
-                for f in step_fns:
-                    f(i)
+            body()
     torch.cuda.current_stream().wait_stream(cap)
     torch.cuda.synchronize()
-    reps = max(1, -(-steps // copies))
+    return graph
+
+
+def _replay_ms(torch, graph, reps):
+    """Average time of one replay, with events on the replaying stream."""
     graph.replay()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
@@ -101,24 +92,36 @@ def time_steps(torch, step_fns, steps, warmup, copies):
         graph.replay()
     e1.record(s)
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / (reps * copies)
-    del graph
-    # per-launch durations
-    n = min(steps, 4 * copies)
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in step_fns] for _ in range(n)]
-    try:
-        torch.cuda._sleep(200_000_000)
-    except Exception:  # pragma: no cover - sleep kernel unavailable
-        pass
-    for i in range(n):
-        for j, f in enumerate(step_fns):
-            evs[i][j][0].record(s)
+    return e0.elapsed_time(e1) / reps
+
+
+def time_steps(torch, step_fns, steps, warmup, copies):
+    """Time ``steps`` steps; return (ms per step, per-kernel average ms list).
+
+    step_fns: callables; step i runs every callable with argument i (i selects
+    the weight copy).  The timed steps replay a HIP graph holding one full
+    rotation (``copies`` steps), so host launch overhead stays out of the
+    measurement.  Each kernel's average duration comes from a graph of that
+    kernel alone over the same rotation, launched back to back (the events
+    bracket ``copies`` launches on the stream they run on)."""
+    for i in range(warmup):
+        for f in step_fns:
             f(i)
-            evs[i][j][1].record(s)
     torch.cuda.synchronize()
-    per = [float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(n)]))
-           for j in range(len(step_fns))]
+
+    def whole():
+        for i in range(copies):
+            for f in step_fns:
+                f(i)
+    graph = _graph(torch, whole)
+    reps = max(1, -(-steps // copies))
+    ms_step = _replay_ms(torch, graph, reps) / copies
+    del graph
+    per = []
+    for f in step_fns:
+        g = _graph(torch, lambda f=f: [f(i) for i in range(copies)])
+        per.append(_replay_ms(torch, g, reps) / copies)
+        del g
     return ms_step, per
 
 
