@@ -40,8 +40,6 @@ namespace qlin {
 
 namespace {
 
-constexpr int kThreads = 256;   // 4 waves along N
-constexpr int kBN = 128;        // output columns per tile
 constexpr int kKS = 128;        // K per step (16 packed words per column)
 
 // Eight fp16 weights s * (q - z) in natural k order from one packed word: q - z
@@ -68,12 +66,14 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
   return bitcast<uint32_t>(__builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
-template <int TM, int R, bool XBF16, int OUTK>
-__global__ __launch_bounds__(kThreads) void w4_gemm_sk_kernel(
+template <int TM, int NW, int R, bool XBF16, int OUTK>
+__global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
     const uint16_t* X, int M, int K, const uint32_t* qweight, const uint16_t* scales,
     const uint32_t* qzeros, int N, int gsh, int tiles_n, SkPlan plan, void* Y, float* ws, int* counters) {
   // (no __restrict__: with it the prefetch loads count as invariant and get sunk
   // across the step barriers to their first use, which defeats the prefetch)
+  constexpr int kThreads = 64 * NW;           // NW waves side by side along N
+  constexpr int kBN = 32 * NW;                // output columns per tile
   constexpr int BM = 32 * TM;
   constexpr int APT = BM * 16 / kThreads;   // 16-byte activation pieces per thread per step
   static_assert(APT >= 1, "tile too small");
@@ -218,28 +218,26 @@ __global__ __launch_bounds__(kThreads) void w4_gemm_sk_kernel(
       __syncthreads();
       write = s_last != 0;
       if (write) {
-        f32x16_t tot[TM];
+        // K-order sum, one 32-row block at a time: (partials before this
+        // workgroup's) + own + (partials after), each batch of loads issued at once
 #pragma unroll
-        for (int i = 0; i < TM; ++i) tot[i] = f32x16_t{};
-        for (int q = first; q <= last; ++q) {
-          if (q == p) {
+        for (int i = 0; i < TM; ++i) {
+          f32x16_t tot = f32x16_t{};
+          for (int q = first; q <= last; ++q) {
+            if (q == p) {
+              tot += acc[i];
+            } else {
+              const float* other = ws + static_cast<size_t>(sk_slot(plan, q, t)) * (BM * kBN) +
+                                   ((wv * TM + i) * 16) * 64 + lane;
+              float part[16];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) tot[i] += acc[i];
-          } else {
-            const float* other = ws + static_cast<size_t>(sk_slot(plan, q, t)) * (BM * kBN);
-            float part[TM][16];                 // issue all loads, then add (one wait)
+              for (int r = 0; r < 16; ++r) part[r] = sk_load(other + r * 64);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) part[i][r] = sk_load(other + ((wv * TM + i) * 16 + r) * 64 + lane);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) tot[i][r] += part[i][r];
+              for (int r = 0; r < 16; ++r) tot[r] += part[r];
+            }
           }
+          acc[i] = tot;
         }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) acc[i] = tot[i];
         if (tid == 0) sk_reset(&counters[t]);
       }
     }
@@ -256,54 +254,54 @@ __global__ __launch_bounds__(kThreads) void w4_gemm_sk_kernel(
   }
 }
 
-template <int TM, int R, bool XBF16, int OUTK>
+template <int TM, int NW, int R, bool XBF16, int OUTK>
 qlin_status launch_sk(const W4Args& a, hipStream_t stream) {
-  constexpr int BM = 32 * TM;
+  constexpr int BM = 32 * TM, BN = 32 * NW;
   const size_t lds = static_cast<size_t>(2) * BM * 16 * sizeof(uint4);
   static int occ = 0;                          // resident workgroups per CU (register / LDS bound)
   if (occ == 0) {
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, w4_gemm_sk_kernel<TM, R, XBF16, OUTK>, kThreads, lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, w4_gemm_sk_kernel<TM, NW, R, XBF16, OUTK>, 64 * NW, lds) !=
             hipSuccess || o <= 0)
       o = 1;
     occ = std::min(o, 2);
   }
   const int tiles_m = (a.M + BM - 1) / BM;
-  const int tiles_n = (a.N + kBN - 1) / kBN;
+  const int tiles_n = (a.N + BN - 1) / BN;
   const long long tiles = static_cast<long long>(tiles_m) * tiles_n;
   SkPlan plan;
   plan.ksteps = a.K / kKS;
   plan.units = tiles * plan.ksteps;
   plan.P = static_cast<int>(std::min<long long>(static_cast<long long>(occ) * device_cus(), plan.units));
   Workspace w;
-  const qlin_status s = get_workspace(static_cast<size_t>(2) * plan.P * BM * kBN * sizeof(float),
+  const qlin_status s = get_workspace(static_cast<size_t>(2) * plan.P * BM * BN * sizeof(float),
                                       static_cast<size_t>(tiles), stream, "qlin_w4_forward", &w);
   if (s != QLIN_OK) return s;
   const int gsh = a.G == 256 ? 1 : 0;
-  hipLaunchKernelGGL((w4_gemm_sk_kernel<TM, R, XBF16, OUTK>), dim3(plan.P), dim3(kThreads), lds, stream,
+  hipLaunchKernelGGL((w4_gemm_sk_kernel<TM, NW, R, XBF16, OUTK>), dim3(plan.P), dim3(64 * NW), lds, stream,
                      static_cast<const uint16_t*>(a.X), a.M, a.K, a.qweight, a.scales, a.qzeros, a.N, gsh, tiles_n,
                      plan, a.Y, w.partials, w.counters);
   return QLIN_OK;
 }
 
-template <int TM, int R, bool XBF16>
+template <int TM, int NW, int R, bool XBF16>
 qlin_status launch_o(const W4Args& a, hipStream_t stream) {
-  if (a.y_dtype == QLIN_F16) return launch_sk<TM, R, XBF16, OUT_F16>(a, stream);
-  if (a.y_dtype == QLIN_BF16) return launch_sk<TM, R, XBF16, OUT_BF16>(a, stream);
-  return launch_sk<TM, R, XBF16, OUT_F32>(a, stream);
+  if (a.y_dtype == QLIN_F16) return launch_sk<TM, NW, R, XBF16, OUT_F16>(a, stream);
+  if (a.y_dtype == QLIN_BF16) return launch_sk<TM, NW, R, XBF16, OUT_BF16>(a, stream);
+  return launch_sk<TM, NW, R, XBF16, OUT_F32>(a, stream);
 }
 
-template <int TM, int R>
+template <int TM, int NW, int R>
 qlin_status launch_x(const W4Args& a, hipStream_t stream) {
-  return a.x_dtype == QLIN_BF16 ? launch_o<TM, R, true>(a, stream) : launch_o<TM, R, false>(a, stream);
+  return a.x_dtype == QLIN_BF16 ? launch_o<TM, NW, R, true>(a, stream) : launch_o<TM, NW, R, false>(a, stream);
 }
 
 }  // namespace
 
 qlin_status w4_gemm_sk_launch(const W4Args& a, hipStream_t stream) {
-  if (a.M <= 32) return launch_x<1, 6>(a, stream);
-  if (a.M <= 64) return launch_x<2, 4>(a, stream);
-  return launch_x<4, 4>(a, stream);
+  if (a.M <= 32) return launch_x<1, 4, 6>(a, stream);
+  if (a.M <= 64) return launch_x<2, 4, 4>(a, stream);
+  return launch_x<4, 8, 3>(a, stream);
 }
 
 }  // namespace qlin
