@@ -299,8 +299,8 @@ qlin_status launch_x(const W4Args& a, hipStream_t stream) {
 }  // namespace
 
 qlin_status w4_gemm_sk_launch(const W4Args& a, hipStream_t stream) {
-  if (a.M <= 32) return launch_x<1, 4, 6>(a, stream);
-  if (a.M <= 64) return launch_x<2, 4, 4>(a, stream);
+  if (a.M <= 32) return launch_x<1, 8, 6>(a, stream);
+  if (a.M <= 64) return launch_x<2, 8, 4>(a, stream);
   return launch_x<4, 8, 3>(a, stream);
 }
 
