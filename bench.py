@@ -271,12 +271,21 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "w4_gemv_w4_llama7b_m1_counters.t
 COPY_BYTES = 256 << 20
 
 
+def code_text(src):
+    """C++ source with comments removed and whitespace runs collapsed: what the
+    compiler sees, so that editing a comment does not invalidate a measurement."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def source_hash(paths=GEMV_SOURCES):
     import hashlib
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

@@ -91,8 +91,18 @@ qlin_status qlin_w4_pack(const float* W, int N, int K, int G,
 /* Y = X . W_hat^T on the GPU.
  *   X  device, [M][K], x_dtype QLIN_F16 or QLIN_BF16
  *   Y  device, [M][N], y_dtype QLIN_F16, QLIN_BF16 or QLIN_F32
- * Accumulation is fp32.  M <= 16 runs a fused unpack-dequant GEMV; larger M runs
- * an MFMA GEMM on exact integer codes with a per-group fp32 rescale.
+ * Accumulation is fp32.  Small batches (M <= 16, K <= 16384, and the batch's
+ * staged activations within 64 KB of LDS) run a fused unpack-dequant GEMV on
+ * exact codes.  Otherwise an fp16 MFMA GEMM runs: for G = 128 or 256 on
+ * weights S * (q - z) rounded once to fp16, split over the device's compute
+ * units (stream-K); for G = 32 or 64 on exact integer codes with a per-group
+ * fp32 rescale.  The GEMM computes with fp16 activations: bf16 X must lie in
+ * the fp16 range (|x| <= 65504; below 2^-14 the subnormal step limits precision).
+ * The stream-K GEMM uses a workspace the library allocates per device on first
+ * use of a larger shape and keeps until the process ends; calls that reach it
+ * on one device must not run concurrently, and a call that would have to grow
+ * it while `stream` is being captured returns EUNSUPPORTED (make one uncaptured
+ * call of the largest shape first).
  * Requirements: M, N, K > 0; G % 32 == 0; K % G == 0.  EUNSUPPORTED for other G. */
 qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
                             const uint32_t* qweight, const uint16_t* scales,
@@ -191,7 +201,10 @@ qlin_status sq_smooth_quant_act(const uint16_t* X, const float* inv_s, int M, in
 /* GPU: acc[m][n] = sum_k Xq[m][k] * Wq[n][k] (int32, exact);
  * Y[m][n] = y_dtype(float(acc) * x_scale[m] * w_scale[n]).
  * Y device [M][N] with y_dtype QLIN_F16 or QLIN_F32; acc_out, if not NULL,
- * receives acc (int32 [M][N], device).  Requirements: K % 64 == 0, K <= 131072. */
+ * receives acc (int32 [M][N], device).  Requirements: K % 64 == 0, K <= 131072.
+ * The K range of a tile may be split over several workgroups (stream-K) through
+ * the same per-device workspace as the W4 GEMM, with the same rules: calls on one
+ * device must not overlap, and growing it during graph capture is refused. */
 qlin_status sq_int8_gemm(const int8_t* Xq, const float* x_scale,
                          const int8_t* Wq, const float* w_scale,
                          int M, int N, int K, void* Y, int y_dtype,

@@ -6,9 +6,10 @@
 // At larger batch the weight-only layer becomes compute bound and the dequant
 // work is what erodes the gain (GPTQ bulletin, "İddia ve Gerçeklik").  Layout of
 // the work:
-//   * one workgroup = 4 waves side by side along N; a wave owns all BM = 32 TM
-//     rows of the tile and 32 output columns, so every packed word is turned into
-//     fp16 once and feeds TM matrix instructions;
+//   * one workgroup = NW = 8 waves side by side along N (tiles of BM = 32 TM
+//     rows x 256 columns); a wave owns all BM rows of the tile and 32 output
+//     columns, so every packed word is turned into fp16 once and feeds TM matrix
+//     instructions, and eight waves per CU hide each other's dequant work;
 //   * B operand: a lane unpacks one word (8 codes of its column) per
 //     v_mfma_f32_32x32x16_f16 into fp16 weights s * (q - z), in natural k
 //     order: a byte permute + an and-or place each code in the mantissa of

@@ -8,15 +8,20 @@
 // operations:
 //   * the activations of the whole batch are staged once per workgroup in LDS,
 //     already arranged as the (x_j, x_{j+4}) pairs the code unpack produces,
-//     together with per-chunk sums sum(x) (a chunk = 32 codes = one uint4);
-//   * each wavefront owns whole output rows; its lanes stride over the row's
-//     chunks (64 lanes x 16 B contiguous per load instruction);
-//   * codes become exact 16-bit floats B + D q by an and-or into the mantissa,
-//     and v_dot2 accumulates x * (B + D q) in fp32; the group's zero point and
-//     the magic offset B fold into one fused multiply-add with sum(x):
-//       sum x (q - z) = acc / D - (B / D + z) * sum(x);
-//   * the per-group fp16 scale multiplies that chunk result in fp32, and a
-//     64-lane shuffle reduction finishes the row.
+//     together with two per-chunk sums (a chunk = 32 codes = one uint4);
+//   * each wavefront owns whole output rows (or, for long rows, one of KS
+//     contiguous K parts of a row); its lanes stride over the row's chunks
+//     (64 lanes x 16 B contiguous per load instruction), and the whole part is
+//     loaded before any arithmetic;
+//   * codes become exact 16-bit floats by and-or into the mantissa of 1024:
+//     the low nibble of a byte gives 1024 + q, the high nibble 1024 + 16 q
+//     without a shift (the activations paired with those registers are staged
+//     pre-divided by 16), and v_dot2 accumulates against the pairs in fp32;
+//     the magic offsets and the group's zero point then fold into one fused
+//     multiply-add with the chunk's sums;
+//   * the per-group fp16 scale multiplies that chunk result in fp32; a DPP
+//     row reduction (and, for split rows, a fixed-order sum of the parts in
+//     LDS) finishes the row.
 
 #include "common.hpp"
 #include "device.hpp"
