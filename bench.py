@@ -47,6 +47,9 @@ def parse():
                    help="summarize rocprofv3 csv output under DIR (trace/, fetch/, write/) and exit")
     p.add_argument("--calibrate", action="store_true",
                    help="first run a plain 256 MiB device copy (known traffic) 5 times, for counter scaling")
+    p.add_argument("--sweep", choices=("batch", "outliers"),
+                   help="instead of the headline: batch crossover sweep M = 1..2048 (W4A16 vs W8A8 vs "
+                        "dense fp16), or SpQR outlier-fraction sweep 0-4%% at M = 1 and 4")
     return p.parse_args()
 
 
@@ -230,6 +233,171 @@ def sq_step_fns(qlin, layers):
 
 
 # ---------------------------------------------------------------------------
+# sweeps (separate runs, not part of the headline line)
+
+SWEEP_M = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048)
+SWEEP_FRACS = (0.0, 0.0025, 0.005, 0.01, 0.02, 0.03, 0.04)
+
+
+def graph_step_ms(torch, fns, copies, steps):
+    """Average time of one step (every callable of ``fns`` with the step's copy
+    index) over a HIP graph of one full weight rotation, replayed ``steps`` /
+    ``copies`` times after a few eager warm-up steps."""
+    for i in range(min(copies, 3)):
+        for f in fns:
+            f(i)
+    torch.cuda.synchronize()
+    g = _graph(torch, lambda: [f(i) for i in range(copies) for f in fns])
+    ms = _replay_ms(torch, g, max(1, -(-steps // copies))) / copies
+    del g
+    return ms
+
+
+def dense_f16_weights(torch, layers_w):
+    """fp16 copies of the weights, rotated like the packed forms."""
+    base = [torch.from_numpy(W.astype(np.float16)).cuda() for W in layers_w]
+    per_set = sum(t.numel() * 2 for t in base)
+    R = copies_for(per_set)
+    return [base] + [[t.clone() for t in base] for _ in range(R - 1)]
+
+
+def sweep_batch(torch, qlin, synth, steps):
+    """W4A16 (GEMV up to M=16, MFMA GEMM above) vs SmoothQuant W8A8 (activation
+    kernel + int8 GEMM) vs dense fp16 (torch.matmul, the vendor GEMM) on the
+    Llama-7B-shaped layers, for M = 1 .. 2048.  Same fp16 activations for all
+    three (N(0,1), 1% of channels x100, the SmoothQuant workload's recipe)."""
+    shapes = synth.WORKLOADS["w4_llama7b"]["layers"]
+    Mmax = max(SWEEP_M)
+    Ws = [synth.layer_weight("w4_llama7b", li) for li in range(len(shapes))]
+    Xs = []
+    for li, (N, K) in enumerate(shapes):
+        ch = synth.outlier_channels(K, 0.01, f"sweep/L{li}/channels")
+        Xs.append(synth.x_f16(Mmax, K, f"sweep/L{li}/X", ch, 100.0))
+    Xd = [to_dev(torch, x) for x in Xs]
+    Yd = [torch.empty((Mmax, N), dtype=torch.float16, device="cuda") for N, _ in shapes]
+
+    w4 = [[to_dev(torch, a) for a in qlin.qlin_w4_pack(W, 128)] for W in Ws]
+    w4_bytes = sum(t.numel() * t.element_size() for l in w4 for t in l)
+    w4 = [w4] + [[[t.clone() for t in l] for l in w4] for _ in range(copies_for(w4_bytes) - 1)]
+
+    sq, inv = [], []
+    for W, X in zip(Ws, Xs):
+        s_, inv_ = qlin.sq_compute_smoothing(qlin.sq_act_absmax(X[:512]), W, 0.85)
+        Wq, ws = qlin.sq_pack_weight(W, s_)
+        sq.append([to_dev(torch, Wq), to_dev(torch, ws)])
+        inv.append(to_dev(torch, inv_))
+    sq_bytes = sum(t.numel() * t.element_size() for l in sq for t in l)
+    sq = [sq] + [[[t.clone() for t in l] for l in sq] for _ in range(copies_for(sq_bytes) - 1)]
+    Xq = [torch.empty((Mmax, K), dtype=torch.int8, device="cuda") for _, K in shapes]
+    xs = [torch.empty((Mmax,), dtype=torch.float32, device="cuda") for _ in shapes]
+
+    f16 = dense_f16_weights(torch, Ws)
+    f16_bytes = sum(t.numel() * 2 for t in f16[0])
+    del Ws
+
+    rows = []
+    for M in SWEEP_M:
+        def w4_fns():
+            out = []
+            for li, (N, K) in enumerate(shapes):
+                def f(i, li=li, N=N, K=K):
+                    qw, sc, qz = w4[i % len(w4)][li]
+                    qlin.qlin_w4_forward(Xd[li][:M], qlin.QLIN_F16, M, K, qw, sc, qz, N, 128, Yd[li][:M],
+                                         qlin.QLIN_F16)
+                out.append(f)
+            return out
+
+        def sq_fns():
+            out = []
+            for li, (N, K) in enumerate(shapes):
+                def f(i, li=li, N=N, K=K):
+                    Wq, ws = sq[i % len(sq)][li]
+                    qlin.sq_smooth_quant_act(Xd[li][:M], inv[li], M, K, Xq[li][:M], xs[li][:M])
+                    qlin.sq_int8_gemm(Xq[li][:M], xs[li][:M], Wq, ws, M, N, K, Yd[li][:M], qlin.QLIN_F16, None)
+                out.append(f)
+            return out
+
+        def f16_fns():
+            out = []
+            for li in range(len(shapes)):
+                def f(i, li=li):
+                    torch.matmul(Xd[li][:M], f16[i % len(f16)][li].t(), out=Yd[li][:M])
+                out.append(f)
+            return out
+
+        flops = sum(2.0 * M * N * K for N, K in shapes)
+        io = sum(M * K * 2 + M * N * 2 for N, K in shapes)
+        rec = {"M": M}
+        for name, fns, copies, wb, peak in (("w4a16", w4_fns(), len(w4), w4_bytes, MFMA_PEAK_TFLOPS["f16"]),
+                                            ("w8a8", sq_fns(), len(sq), sq_bytes, MFMA_PEAK_TFLOPS["i8"]),
+                                            ("f16", f16_fns(), len(f16), f16_bytes, MFMA_PEAK_TFLOPS["f16"])):
+            ms = graph_step_ms(torch, fns, copies, steps)
+            floor_us = max((wb + io) / (HBM_PEAK_GBS * 1e9), flops / (peak * 1e12)) * 1e6
+            rec[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+                         "GB/s": round((wb + io) / (ms * 1e-3) / 1e9, 1), "roofline_us": round(floor_us, 2)}
+        rec["fastest"] = min(("w4a16", "w8a8", "f16"), key=lambda k: rec[k]["us"])
+        print(json.dumps(rec), flush=True)
+        rows.append(rec)
+    return {"sweep": "batch", "layers": [f"{N}x{K}" for N, K in shapes], "weight_bytes":
+            {"w4a16": w4_bytes, "w8a8": sq_bytes, "f16": f16_bytes}, "rows": rows}
+
+
+def sweep_outliers(torch, qlin, synth, steps):
+    """SpQR forward on the 33B-shaped layers at M = 1 and 4 for outlier fractions
+    0 .. 4%, against the dense fp16 product of the same layers (torch.matmul).
+    The share of time spent on the CSR part is (t(p) - t(0)) / t(p): the dense
+    3-bit part costs the same whatever the fraction."""
+    cfg = synth.WORKLOADS["spqr_33b"]
+    shapes = cfg["layers"]
+    Ms = (1, 4)
+    Xd = {M: [to_dev(torch, synth.activations("spqr_33b", li, M)) for li in range(len(shapes))] for M in Ms}
+    Yd = {M: [torch.empty((M, N), dtype=torch.float16, device="cuda") for N, _ in shapes] for M in Ms}
+    Ws = []
+    for li in range(len(shapes)):
+        Ws.append(synth.layer_weight("spqr_33b", li))
+        print(json.dumps({"generated_layer": li}), flush=True)
+    f16 = dense_f16_weights(torch, Ws)
+    base = {}
+    for M in Ms:
+        def f(i, M=M):
+            for li in range(len(shapes)):
+                torch.matmul(Xd[M][li], f16[i % len(f16)][li].t(), out=Yd[M][li])
+        base[M] = graph_step_ms(torch, [f], len(f16), steps)
+    del f16
+    torch.cuda.empty_cache()
+
+    rows = []
+    t0 = {}
+    for p in SWEEP_FRACS:
+        packed, nnz, wb = [], [], 0
+        for W in Ws:
+            st = qlin.spqr_pack(W, p)
+            packed.append([to_dev(torch, st[k]) for k in ("codes", "stats1", "stats2", "row_ptr", "col_idx", "val")])
+            nnz.append(len(st["val"]))
+            wb += sum(t.numel() * t.element_size() for t in packed[-1])
+        R = copies_for(wb)
+        sets = [packed] + [[[t.clone() for t in l] for l in packed] for _ in range(R - 1)]
+        for M in Ms:
+            def f(i, M=M):
+                for li, (N, K) in enumerate(shapes):
+                    c, s1, s2, rp, ci, v = sets[i % R][li]
+                    qlin.spqr_forward(Xd[M][li], M, K, c, s1, s2, rp, ci, v, nnz[li], N, Yd[M][li], qlin.QLIN_F16)
+            ms = graph_step_ms(torch, [f], R, steps)
+            if p == 0.0:
+                t0[M] = ms
+            io = sum(M * K * 2 + M * N * 2 for N, K in shapes)
+            rec = {"outlier_frac": p, "M": M, "nnz": sum(nnz), "bits_per_param": round(8.0 * wb / sum(N * K for N, K in shapes), 3),
+                   "us": round(ms * 1e3, 2), "GB/s": round((wb + io) / (ms * 1e-3) / 1e9, 1),
+                   "csr_time_share": round(max(0.0, (ms - t0[M]) / ms), 3),
+                   "f16_us": round(base[M] * 1e3, 2), "speedup_vs_f16": round(base[M] / ms, 2)}
+            print(json.dumps(rec), flush=True)
+            rows.append(rec)
+        del sets, packed
+        torch.cuda.empty_cache()
+    return {"sweep": "outliers", "layers": [f"{N}x{K}" for N, K in shapes], "rows": rows}
+
+
+# ---------------------------------------------------------------------------
 
 def cpu_baseline(synth):
     """The oracle, untouched, on one forward step of the headline workload."""
@@ -388,6 +556,13 @@ def main():
             qlin.qlin_stream_copy(dst, src, nb)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.sweep == "batch":
+        print(json.dumps(sweep_batch(torch, qlin, synth, max(20, args.steps // 4))), flush=True)
+        return
+    if args.sweep == "outliers":
+        print(json.dumps(sweep_outliers(torch, qlin, synth, max(20, args.steps // 4))), flush=True)
+        return
 
     # ---- headline: W4 GEMV, Llama-7B-shaped layers, M = 1
     layers = w4_layers(torch, qlin, synth, "w4_llama7b", 1)

@@ -67,7 +67,7 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
   return bitcast<uint32_t>(__builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
-template <int TM, int NW, int R, bool XBF16, int OUTK>
+template <int TM, int NW, int R, int RV, bool XBF16, int OUTK>
 __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
     const uint16_t* X, int M, int K, const uint32_t* qweight, const uint16_t* scales,
     const uint32_t* qzeros, int N, int gsh, int tiles_n, SkPlan plan, void* Y, float* ws, int* counters) {
@@ -203,7 +203,9 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
     while (sk_run_steps<0, R>(step, kk, k1)) {
     }
 
-    // ---- finish the tile: lane holds column n, rows 8*(r/4) + 4*h + r%4 of each 32-row block
+    // ---- finish the tile: lane holds column n, rows 8*(r/4) + 4*h + r%4 of each
+    // 32-row block; registers r >= RV hold rows past M only (RV < 16 when M is
+    // small) and are neither stored nor summed
     bool write = true;
     if (k0 != 0 || k1 != plan.ksteps) {
       const int first = sk_owner(plan, static_cast<long long>(t) * plan.ksteps);
@@ -212,30 +214,36 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sk_store(mine + ((wv * TM + i) * 16 + r) * 64 + lane, acc[i][r]);
+        for (int r = 0; r < RV; ++r) sk_store(mine + ((wv * TM + i) * 16 + r) * 64 + lane, acc[i][r]);
       sk_drain_stores();
       __syncthreads();
       if (tid == 0) s_last = sk_arrive(&counters[t]) == last - first;
       __syncthreads();
       write = s_last != 0;
       if (write) {
-        // K-order sum, one 32-row block at a time: (partials before this
-        // workgroup's) + own + (partials after), each batch of loads issued at once
+        // K-order sum of every contributor's stored partial (this workgroup's
+        // included), QC partials per batch with all their loads in flight at
+        // once: the latency is paid once per batch, not once per partial
+        constexpr int QC = 64 / RV;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           f32x16_t tot = f32x16_t{};
-          for (int q = first; q <= last; ++q) {
-            if (q == p) {
-              tot += acc[i];
-            } else {
-              const float* other = ws + static_cast<size_t>(sk_slot(plan, q, t)) * (BM * kBN) +
-                                   ((wv * TM + i) * 16) * 64 + lane;
-              float part[16];
+          for (int q0 = first; q0 <= last; q0 += QC) {
+            float part[QC][RV];
 #pragma unroll
-              for (int r = 0; r < 16; ++r) part[r] = sk_load(other + r * 64);
+            for (int j = 0; j < QC; ++j) {
+              const int q = min(q0 + j, last);
+              const float* src = ws + static_cast<size_t>(sk_slot(plan, q, t)) * (BM * kBN) +
+                                 ((wv * TM + i) * 16) * 64 + lane;
 #pragma unroll
-              for (int r = 0; r < 16; ++r) tot[r] += part[r];
+              for (int r = 0; r < RV; ++r) part[j][r] = sk_load(src + r * 64);
             }
+#pragma unroll
+            for (int j = 0; j < QC; ++j)
+              if (q0 + j <= last) {
+#pragma unroll
+                for (int r = 0; r < RV; ++r) tot[r] += part[j][r];
+              }
           }
           acc[i] = tot;
         }
@@ -255,14 +263,14 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
   }
 }
 
-template <int TM, int NW, int R, bool XBF16, int OUTK>
+template <int TM, int NW, int R, int RV, bool XBF16, int OUTK>
 qlin_status launch_sk(const W4Args& a, hipStream_t stream) {
   constexpr int BM = 32 * TM, BN = 32 * NW;
   const size_t lds = static_cast<size_t>(2) * BM * 16 * sizeof(uint4);
   static int occ = 0;                          // resident workgroups per CU (register / LDS bound)
   if (occ == 0) {
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, w4_gemm_sk_kernel<TM, NW, R, XBF16, OUTK>, 64 * NW, lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, w4_gemm_sk_kernel<TM, NW, R, RV, XBF16, OUTK>, 64 * NW, lds) !=
             hipSuccess || o <= 0)
       o = 1;
     occ = std::min(o, 2);
@@ -279,30 +287,35 @@ qlin_status launch_sk(const W4Args& a, hipStream_t stream) {
                                       static_cast<size_t>(tiles), stream, "qlin_w4_forward", &w);
   if (s != QLIN_OK) return s;
   const int gsh = a.G == 256 ? 1 : 0;
-  hipLaunchKernelGGL((w4_gemm_sk_kernel<TM, NW, R, XBF16, OUTK>), dim3(plan.P), dim3(64 * NW), lds, stream,
+  hipLaunchKernelGGL((w4_gemm_sk_kernel<TM, NW, R, RV, XBF16, OUTK>), dim3(plan.P), dim3(64 * NW), lds, stream,
                      static_cast<const uint16_t*>(a.X), a.M, a.K, a.qweight, a.scales, a.qzeros, a.N, gsh, tiles_n,
                      plan, a.Y, w.partials, w.counters);
   return QLIN_OK;
 }
 
-template <int TM, int NW, int R, bool XBF16>
+template <int TM, int NW, int R, int RV, bool XBF16>
 qlin_status launch_o(const W4Args& a, hipStream_t stream) {
-  if (a.y_dtype == QLIN_F16) return launch_sk<TM, NW, R, XBF16, OUT_F16>(a, stream);
-  if (a.y_dtype == QLIN_BF16) return launch_sk<TM, NW, R, XBF16, OUT_BF16>(a, stream);
-  return launch_sk<TM, NW, R, XBF16, OUT_F32>(a, stream);
+  if (a.y_dtype == QLIN_F16) return launch_sk<TM, NW, R, RV, XBF16, OUT_F16>(a, stream);
+  if (a.y_dtype == QLIN_BF16) return launch_sk<TM, NW, R, RV, XBF16, OUT_BF16>(a, stream);
+  return launch_sk<TM, NW, R, RV, XBF16, OUT_F32>(a, stream);
 }
 
-template <int TM, int NW, int R>
+template <int TM, int NW, int R, int RV>
 qlin_status launch_x(const W4Args& a, hipStream_t stream) {
-  return a.x_dtype == QLIN_BF16 ? launch_o<TM, NW, R, true>(a, stream) : launch_o<TM, NW, R, false>(a, stream);
+  return a.x_dtype == QLIN_BF16 ? launch_o<TM, NW, R, RV, true>(a, stream)
+                                : launch_o<TM, NW, R, RV, false>(a, stream);
 }
 
 }  // namespace
 
 qlin_status w4_gemm_sk_launch(const W4Args& a, hipStream_t stream) {
-  if (a.M <= 32) return launch_x<1, 8, 6>(a, stream);
-  if (a.M <= 64) return launch_x<2, 8, 4>(a, stream);
-  return launch_x<4, 8, 3>(a, stream);
+  // RV: accumulator registers per 32-row block that can hold rows below M
+  // (register r holds rows 8 (r / 4) + 4 h + r % 4, h the lane half)
+  if (a.M <= 8) return launch_x<1, 8, 6, 4>(a, stream);
+  if (a.M <= 16) return launch_x<1, 8, 6, 8>(a, stream);
+  if (a.M <= 32) return launch_x<1, 8, 6, 16>(a, stream);
+  if (a.M <= 64) return launch_x<2, 8, 4, 16>(a, stream);
+  return launch_x<4, 8, 3, 16>(a, stream);
 }
 
 }  // namespace qlin

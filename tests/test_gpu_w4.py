@@ -155,3 +155,18 @@ def test_small_batch_beyond_the_gemv_range_uses_the_gemm():
         say(f"w4 long-K N={N} K={K} M={M}")
         X = synth.x_f16(M, K, f"gpu/w4/longkx{M}")
         check_close(gpu_w4(X, F16, packed, N, K, 128, F32), ow4.forward(X, *st, K, 128), f"M={M}")
+
+
+def test_gemm_small_batches_with_split_tiles():
+    """Batches of 2..24 rows on layers whose activations exceed the GEMV's LDS
+    staging run the MFMA GEMM with few output tiles, so every tile's K range is
+    split over many workgroups; the fix-up then sums only the accumulator
+    registers that can hold rows below M."""
+    for (N, K, G) in ((512, 8192, 128), (300, 6144, 256)):
+        W = synth.normal_f32((N, K), 0.02, f"gpu/w4/smallm{N}")
+        packed = dev_pack(W, G)
+        st = ow4.encode(W, G)
+        for M in (2, 5, 8, 9, 16, 17, 24):
+            say(f"w4 small-batch gemm N={N} K={K} G={G} M={M}")
+            X = synth.x_f16(M, K, f"gpu/w4/smallmx{M}")
+            check_close(gpu_w4(X, F16, packed, N, K, G, F32), ow4.forward(X, *st, K, G), f"M={M}")
