@@ -211,6 +211,51 @@ qlin_status sq_int8_gemm(const int8_t* Xq, const float* x_scale,
                          int32_t* acc_out, hipStream_t stream);
 
 /* ======================================================================== */
+/* Second-order encoders (host, offline): same storage, same forward calls   */
+/* ======================================================================== */
+/* The GPTQ bulletin ("İddia ve Gerçeklik") quantizes column by column with a
+ * second-order error model: the inverse Hessian comes from the covariance of
+ * the layer inputs, a Cholesky decomposition keeps it stable, and each
+ * column's rounding error is pushed onto the columns not yet quantized.  The
+ * SpQR bulletin ("İddia ve Gerçeklik") picks its outliers by Hessian-based
+ * sensitivity.  All three calls are deterministic host functions; inputs and
+ * outputs are host arrays owned by the caller; nothing is enqueued. */
+
+/* H = (2 / n) X^T X in fp64 (host, [K][K], symmetric) from n calibration rows
+ * X (fp32 [n][K], host), each entry summed over the rows in order.
+ * EINVAL if n <= 0, K <= 0 or a pointer is NULL.  Cost O(n K^2). */
+qlin_status qlin_hessian(const float* X, int n, int K, double* H);
+
+/* Error-feedback (GPTQ-style) encode of fp32 W [N][K] into the storage of
+ * qlin_w4_pack, given the undamped Hessian H (fp64 [K][K], finite, symmetric).
+ * Damping: H + lam I with lam = damp * mean(diag H) (damp >= 0, 0.01 typical;
+ * H = I when that mean is 0).  U = upper Cholesky factor of (H + lam I)^-1.
+ * Columns j = 0 .. K-1 in order: a group's scale and zero are the
+ * round-to-nearest ones (qlin_w4_pack's rule) of its current weights rounded to
+ * fp32, computed at its first column; column j's code is that rule's code of its
+ * current weight rounded to fp32; then, in fp64, e = (w_j - S (q - z)) / U[j][j]
+ * and every later column k moves by -e U[j][k].  H proportional to I reproduces
+ * qlin_w4_pack bit for bit.  EINVAL for bad sizes (as qlin_w4_sizes), NULL
+ * pointers, damp < 0, a non-symmetric or non-finite H, or H + lam I not
+ * positive definite.  Host memory: about 3 K^2 doubles; time O(K^3 + N K^2). */
+qlin_status qlin_w4_pack_gptq(const float* W, int N, int K, int G, const double* H, double damp,
+                              uint32_t* qweight, uint16_t* scales, uint32_t* qzeros);
+
+/* SpQR encode (outputs and sizes as spqr_pack) whose floor(p N K) outliers are
+ * the weights of largest sensitivity, ties to the lower row-major index.  The
+ * sensitivity of a weight is the drop of its group's (16 consecutive k of one
+ * row) weighted 3-bit quantization error, sum_k c_k (w_k - w_hat_k)^2 with
+ * c_k = diag(H + lam I) (damping as above) and real-valued min/max statistics
+ * (s = (hi - lo) / 7, z = -lo / s; s = 1, z = -lo if hi == lo), when the weight
+ * leaves the group and the other 15 are re-quantized without it; fp64, summed in
+ * index order.  The rest of the encoding is spqr_pack's.  Errors as spqr_pack,
+ * plus EINVAL for damp < 0 or a non-symmetric or non-finite H. */
+qlin_status spqr_pack_hessian(const float* W, int N, int K, double outlier_frac, const double* H, double damp,
+                              uint32_t* codes, uint32_t* stats1, uint16_t* stats2,
+                              int32_t* row_ptr, int32_t* col_idx, uint16_t* vals,
+                              int64_t nnz_cap, int64_t* nnz_out);
+
+/* ======================================================================== */
 /* Measurement aid                                                           */
 /* ======================================================================== */
 /* Plain streaming read of `bytes` (multiple of 16) from device buffer `buf`

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "common.hpp"
+#include "host_pack.hpp"
 
 using namespace qlin;
 
@@ -74,26 +75,45 @@ inline Level2 spqr_level2(const float* v) {
   return r;
 }
 
-// Mask of the n_out entries first in the order (-|w|, row-major index).
-std::vector<uint8_t> spqr_outlier_mask(const float* W, size_t total, int64_t n_out) {
+}  // namespace
+
+namespace qlin {
+
+// Mask of the n entries first in the order (-key, index).
+template <typename T>
+std::vector<uint8_t> top_n_mask(const T* key, size_t total, int64_t n) {
   std::vector<uint8_t> mask(total, 0);
-  if (n_out <= 0) return mask;
-  if (static_cast<size_t>(n_out) >= total) { std::fill(mask.begin(), mask.end(), 1); return mask; }
-  std::vector<float> mag(total);
-  for (size_t i = 0; i < total; ++i) mag[i] = std::fabs(W[i]);
-  std::vector<float> tmp(mag);
-  // threshold t = the n_out-th largest magnitude
-  std::nth_element(tmp.begin(), tmp.begin() + (n_out - 1), tmp.end(), std::greater<float>());
-  const float t = tmp[n_out - 1];
+  if (n <= 0) return mask;
+  if (static_cast<size_t>(n) >= total) { std::fill(mask.begin(), mask.end(), 1); return mask; }
+  std::vector<T> tmp(key, key + total);
+  // threshold t = the n-th largest key
+  std::nth_element(tmp.begin(), tmp.begin() + (n - 1), tmp.end(), std::greater<T>());
+  const T t = tmp[n - 1];
   tmp.clear(); tmp.shrink_to_fit();
   int64_t taken = 0;
-  for (size_t i = 0; i < total; ++i) if (mag[i] > t) { mask[i] = 1; ++taken; }
-  for (size_t i = 0; i < total && taken < n_out; ++i)
-    if (mag[i] == t) { mask[i] = 1; ++taken; }
+  for (size_t i = 0; i < total; ++i) if (key[i] > t) { mask[i] = 1; ++taken; }
+  for (size_t i = 0; i < total && taken < n; ++i)
+    if (key[i] == t) { mask[i] = 1; ++taken; }
   return mask;
 }
+template std::vector<uint8_t> top_n_mask<float>(const float*, size_t, int64_t);
+template std::vector<uint8_t> top_n_mask<double>(const double*, size_t, int64_t);
 
-}  // namespace
+void w4_group_stats(const float* w, int G, uint16_t* S, float* s, float* z) {
+  float lo = 0.0f, hi = 0.0f;
+  for (int i = 0; i < G; ++i) { lo = std::min(lo, w[i]); hi = std::max(hi, w[i]); }
+  uint16_t Sh = host_f32_to_f16((hi - lo) / 15.0f);
+  if ((Sh & 0x7FFFu) == 0) Sh = 0x3C00u;
+  *S = Sh;
+  *s = host_f16_to_f32(Sh);
+  *z = clampf(rne(-lo / *s), 0.0f, 15.0f);
+}
+
+uint32_t w4_code(float w, float s, float z) {
+  return static_cast<uint32_t>(clampf(rne(w / s) + z, 0.0f, 15.0f));
+}
+
+}  // namespace qlin
 
 extern "C" {
 
@@ -126,14 +146,11 @@ qlin_status qlin_w4_pack(const float* W, int N, int K, int G,
     std::fill(zrow, zrow + nzw, 0u);
     for (int g = 0; g < ng; ++g) {
       const float* w = row + static_cast<size_t>(g) * G;
-      float lo = 0.0f, hi = 0.0f;
-      for (int i = 0; i < G; ++i) { lo = std::min(lo, w[i]); hi = std::max(hi, w[i]); }
-      uint16_t S = host_f32_to_f16((hi - lo) / 15.0f);
-      if ((S & 0x7FFFu) == 0) S = 0x3C00u;
-      const float s = host_f16_to_f32(S);
-      const float z = clampf(rne(-lo / s), 0.0f, 15.0f);
+      uint16_t S;
+      float s, z;
+      w4_group_stats(w, G, &S, &s, &z);
       for (int i = 0; i < G; ++i) {
-        const uint32_t code = static_cast<uint32_t>(clampf(rne(w[i] / s) + z, 0.0f, 15.0f));
+        const uint32_t code = w4_code(w[i], s, z);
         const int k = g * G + i;
         qrow[k / 8] |= code << (4 * (k % 8));
       }
@@ -175,8 +192,21 @@ qlin_status spqr_pack(const float* W, int N, int K, double p,
   if (nnz_cap < n_out) return fail(QLIN_EINVAL, "spqr_pack: nnz_cap smaller than the outlier count");
 
   const size_t total = static_cast<size_t>(N) * K;
-  std::vector<uint8_t> mask = spqr_outlier_mask(W, total, n_out);
+  std::vector<float> mag(total);
+  for (size_t i = 0; i < total; ++i) mag[i] = std::fabs(W[i]);
+  const std::vector<uint8_t> mask = top_n_mask(mag.data(), total, n_out);
+  mag.clear(); mag.shrink_to_fit();
+  spqr_encode_masked(W, N, K, mask.data(), codes, stats1, stats2, row_ptr, col_idx, vals, nnz_out);
+  return QLIN_OK;
+}
 
+}  // extern "C"
+
+namespace qlin {
+
+void spqr_encode_masked(const float* W, int N, int K, const uint8_t* mask,
+                        uint32_t* codes, uint32_t* stats1, uint16_t* stats2,
+                        int32_t* row_ptr, int32_t* col_idx, uint16_t* vals, int64_t* nnz_out) {
   // CSR, rows = output channels, columns ascending
   int64_t nz = 0;
   row_ptr[0] = 0;
@@ -235,8 +265,11 @@ qlin_status spqr_pack(const float* W, int N, int K, double p,
     for (int c = 0; c < K / 32; ++c) spqr_pack_chunk(&q[32 * c], &q[32 * c + 16], crow + 3 * c);
   }
   if (nnz_out) *nnz_out = nz;
-  return QLIN_OK;
 }
+
+}  // namespace qlin
+
+extern "C" {
 
 // ===========================================================================
 // SmoothQuant (host side)

@@ -44,6 +44,7 @@ EXPORTS = (
     "spqr_sizes", "spqr_pack", "spqr_forward", "spqr_unpack",
     "sq_act_absmax", "sq_compute_smoothing", "sq_pack_weight", "sq_smooth_quant_act", "sq_int8_gemm",
     "qlin_stream_read", "qlin_stream_copy",
+    "qlin_hessian", "qlin_w4_pack_gptq", "spqr_pack_hessian",
 )
 
 _vp, _i, _i64, _sz, _d = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.c_double
@@ -66,6 +67,9 @@ _sigs = {
     "sq_int8_gemm": ([_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp], _i),
     "qlin_stream_read": ([_vp, _sz, _i, _i, _i, _vp, _vp], _i),
     "qlin_stream_copy": ([_vp, _vp, _sz, _vp], _i),
+    "qlin_hessian": ([_vp, _i, _i, _vp], _i),
+    "qlin_w4_pack_gptq": ([_vp, _i, _i, _i, _vp, _d, _vp, _vp, _vp], _i),
+    "spqr_pack_hessian": ([_vp, _i, _i, _d, _vp, _d, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp], _i),
 }
 for _name, (_args, _res) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -147,6 +151,28 @@ def qlin_w4_pack(W: np.ndarray, G: int = 128):
     return qw, sc.view(np.float16), qz
 
 
+def qlin_hessian(X: np.ndarray):
+    """H = (2/n) X^T X in fp64 from calibration rows X [n][K] (converted to fp32)."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    n, K = X.shape
+    H = np.zeros((K, K), np.float64)
+    _check(_lib.qlin_hessian(_ptr(X), n, K, _ptr(H)))
+    return H
+
+
+def qlin_w4_pack_gptq(W: np.ndarray, G: int, H: np.ndarray, damp: float = 0.01):
+    """Second-order (error-feedback) encode into the same storage as qlin_w4_pack."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    H = np.ascontiguousarray(H, dtype=np.float64)
+    N, K = W.shape
+    qlin_w4_sizes(N, K, G)
+    qw = np.zeros((N, K // 8), np.uint32)
+    sc = np.zeros((N, K // G), np.uint16)
+    qz = np.zeros((N, (K // G + 7) // 8), np.uint32)
+    _check(_lib.qlin_w4_pack_gptq(_ptr(W), N, K, G, _ptr(H), damp, _ptr(qw), _ptr(sc), _ptr(qz)))
+    return qw, sc.view(np.float16), qz
+
+
 def qlin_w4_forward(X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype, stream=None):
     _check(_lib.qlin_w4_forward(_ptr(X), x_dtype, M, K, _ptr(qweight), _ptr(scales), _ptr(qzeros),
                                 N, G, _ptr(Y), y_dtype, _stream(stream)))
@@ -178,6 +204,26 @@ def spqr_pack(W: np.ndarray, outlier_frac: float = 0.01):
     out = C.c_int64()
     _check(_lib.spqr_pack(_ptr(W), N, K, outlier_frac, _ptr(codes), _ptr(s1), _ptr(s2), _ptr(rp),
                           _ptr(ci), _ptr(vals), nnz, C.byref(out)))
+    n = out.value
+    return dict(codes=codes, stats1=s1, stats2=s2.view(np.float16), row_ptr=rp,
+                col_idx=ci[:n].copy(), val=vals[:n].view(np.float16).copy())
+
+
+def spqr_pack_hessian(W: np.ndarray, outlier_frac: float, H: np.ndarray, damp: float = 0.01):
+    """SpQR storage with outliers chosen by Hessian-weighted sensitivity (H fp64 [K][K])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    H = np.ascontiguousarray(H, dtype=np.float64)
+    N, K = W.shape
+    _, _, _, nnz = spqr_sizes(N, K, outlier_frac)
+    codes = np.zeros((N, K // 32, 3), np.uint32)
+    s1 = np.zeros((N, K // 256, 3), np.uint32)
+    s2 = np.zeros((N, K // 256, 4), np.uint16)
+    rp = np.zeros(N + 1, np.int32)
+    ci = np.zeros(max(nnz, 1), np.int32)
+    vals = np.zeros(max(nnz, 1), np.uint16)
+    out = C.c_int64()
+    _check(_lib.spqr_pack_hessian(_ptr(W), N, K, outlier_frac, _ptr(H), damp, _ptr(codes), _ptr(s1), _ptr(s2),
+                                  _ptr(rp), _ptr(ci), _ptr(vals), nnz, C.byref(out)))
     n = out.value
     return dict(codes=codes, stats1=s1, stats2=s2.view(np.float16), row_ptr=rp,
                 col_idx=ci[:n].copy(), val=vals[:n].view(np.float16).copy())
