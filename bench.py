@@ -47,9 +47,10 @@ def parse():
                    help="summarize rocprofv3 csv output under DIR (trace/, fetch/, write/) and exit")
     p.add_argument("--calibrate", action="store_true",
                    help="first run a plain 256 MiB device copy (known traffic) 5 times, for counter scaling")
-    p.add_argument("--sweep", choices=("batch", "outliers"),
+    p.add_argument("--sweep", choices=("batch", "outliers", "actorder"),
                    help="instead of the headline: batch crossover sweep M = 1..2048 (W4A16 vs W8A8 vs "
-                        "dense fp16), or SpQR outlier-fraction sweep 0-4%% at M = 1 and 4")
+                        "dense fp16), SpQR outlier-fraction sweep 0-4%% at M = 1 and 4, or the act-order "
+                        "penalty (gathered activations vs static groups) at M = 1, 8, 64")
     return p.parse_args()
 
 
@@ -397,6 +398,45 @@ def sweep_outliers(torch, qlin, synth, steps):
     return {"sweep": "outliers", "layers": [f"{N}x{K}" for N, K in shapes], "rows": rows}
 
 
+def sweep_actorder(torch, qlin, synth, steps):
+    """Act-order storage without static groups needs the activations gathered
+    through perm before the regular kernels (qlin_w4_forward_perm); with static
+    groups the storage is natural (qlin_w4_forward).  Same Llama-7B-shaped
+    layers and weight bytes; the timing does not depend on the values, so the
+    weights are the round-to-nearest encode and perm a seeded permutation."""
+    shapes = synth.WORKLOADS["w4_llama7b"]["layers"]
+    Ms = (1, 8, 64)
+    packed = [[to_dev(torch, a) for a in qlin.qlin_w4_pack(synth.layer_weight("w4_llama7b", li), 128)]
+              for li in range(len(shapes))]
+    wb = sum(t.numel() * t.element_size() for l in packed for t in l)
+    sets = [packed] + [[[t.clone() for t in l] for l in packed] for _ in range(copies_for(wb) - 1)]
+    perms = [to_dev(torch, synth.rng(f"actorder/perm{li}").permutation(K).astype(np.int32))
+             for li, (_, K) in enumerate(shapes)]
+    rows = []
+    for M in Ms:
+        Xd = [to_dev(torch, synth.x_f16(M, K, f"actorder/X{li}")) for li, (_, K) in enumerate(shapes)]
+        Xp = [torch.empty_like(x) for x in Xd]
+        Yd = [torch.empty((M, N), dtype=torch.float16, device="cuda") for N, _ in shapes]
+
+        def natural(i):
+            for li, (N, K) in enumerate(shapes):
+                qw, sc, qz = sets[i % len(sets)][li]
+                qlin.qlin_w4_forward(Xd[li], qlin.QLIN_F16, M, K, qw, sc, qz, N, 128, Yd[li], qlin.QLIN_F16)
+
+        def gathered(i):
+            for li, (N, K) in enumerate(shapes):
+                qw, sc, qz = sets[i % len(sets)][li]
+                qlin.qlin_w4_forward_perm(Xd[li], qlin.QLIN_F16, M, K, perms[li], Xp[li], qw, sc, qz, N, 128,
+                                          Yd[li], qlin.QLIN_F16)
+        t_nat = graph_step_ms(torch, [natural], len(sets), steps)
+        t_gat = graph_step_ms(torch, [gathered], len(sets), steps)
+        rec = {"M": M, "static_groups_us": round(t_nat * 1e3, 2), "act_order_gather_us": round(t_gat * 1e3, 2),
+               "penalty_us": round((t_gat - t_nat) * 1e3, 2), "penalty_frac": round(t_gat / t_nat - 1.0, 3)}
+        print(json.dumps(rec), flush=True)
+        rows.append(rec)
+    return {"sweep": "actorder", "layers": [f"{N}x{K}" for N, K in shapes], "rows": rows}
+
+
 # ---------------------------------------------------------------------------
 
 def cpu_baseline(synth):
@@ -559,6 +599,9 @@ def main():
 
     if args.sweep == "batch":
         print(json.dumps(sweep_batch(torch, qlin, synth, max(20, args.steps // 4))), flush=True)
+        return
+    if args.sweep == "actorder":
+        print(json.dumps(sweep_actorder(torch, qlin, synth, max(20, args.steps // 4))), flush=True)
         return
     if args.sweep == "outliers":
         print(json.dumps(sweep_outliers(torch, qlin, synth, max(20, args.steps // 4))), flush=True)

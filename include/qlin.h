@@ -109,6 +109,24 @@ qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
                             const uint32_t* qzeros, int N, int G,
                             void* Y, int y_dtype, hipStream_t stream);
 
+/* Forward of act-order storage (qlin_w4_pack_gptq_actorder without static
+ * groups): the stored columns are in quantization order and stored column t is
+ * input column perm[t], so Y = X[:, perm] . W_hat^T.  The GPTQ bulletin
+ * ("Kod ve Entegrasyon Haritası") notes that act-order makes the groups
+ * irregular at run time; here a gather
+ * Xp[m][t] = X[m][perm[t]] runs first (one extra small kernel on `stream`), then
+ * qlin_w4_forward's kernels on Xp.
+ *   perm device int32 [K], a permutation of 0 .. K-1 (entries are clamped into
+ *        range, so a non-permutation gives a meaningless result, never a fault)
+ *   Xp   device scratch [M][K] of x_dtype, overwritten, 16-byte aligned, must
+ *        not overlap X
+ * Other arguments, requirements and errors as qlin_w4_forward (EINVAL for a
+ * NULL perm or Xp, or Xp overlapping X). */
+qlin_status qlin_w4_forward_perm(const void* X, int x_dtype, int M, int K, const int32_t* perm, void* Xp,
+                                 const uint32_t* qweight, const uint16_t* scales,
+                                 const uint32_t* qzeros, int N, int G,
+                                 void* Y, int y_dtype, hipStream_t stream);
+
 /* Debug: unpack codes (uint8 [N][K]) and zeros (uint8 [N][K/G]) on the GPU with
  * the same unpack routine the forward kernels use. */
 qlin_status qlin_w4_unpack(const uint32_t* qweight, const uint32_t* qzeros,
@@ -240,6 +258,23 @@ qlin_status qlin_hessian(const float* X, int n, int K, double* H);
  * positive definite.  Host memory: about 3 K^2 doubles; time O(K^3 + N K^2). */
 qlin_status qlin_w4_pack_gptq(const float* W, int N, int K, int G, const double* H, double damp,
                               uint32_t* qweight, uint16_t* scales, uint32_t* qzeros);
+
+/* Act-order variant of qlin_w4_pack_gptq: columns are quantized in decreasing
+ * order of diag(H), ties to the lower index (GPTQ bulletin, "Kod ve
+ * Entegrasyon Haritası": act-order, and its advice to keep groups static).
+ *   static_groups != 0: groups stay the natural runs of G columns, with the
+ *     round-to-nearest statistics of the original weights (qlin_w4_pack's
+ *     scales and zeros, bit for bit); storage in natural order, perm = identity;
+ *     run it with qlin_w4_forward.
+ *   static_groups == 0: groups are G consecutive columns of the quantization
+ *     order (qlin_w4_pack_gptq applied to W[:, order] with H[order][:, order]);
+ *     storage in that order, perm[t] = order[t]; run it with
+ *     qlin_w4_forward_perm.
+ * perm: host int32 [K] output.  Errors as qlin_w4_pack_gptq (EINVAL for a NULL
+ * perm). */
+qlin_status qlin_w4_pack_gptq_actorder(const float* W, int N, int K, int G, const double* H, double damp,
+                                       int static_groups, uint32_t* qweight, uint16_t* scales, uint32_t* qzeros,
+                                       int32_t* perm);
 
 /* SpQR encode (outputs and sizes as spqr_pack) whose floor(p N K) outliers are
  * the weights of largest sensitivity, ties to the lower row-major index.  The

@@ -31,6 +31,14 @@ G4. Columns are quantized in natural order.  When column j starts a group of
     later column k of the row moves by -e_j * U[j, k].  Rows are independent.
 G5. H proportional to I makes U diagonal: no feedback, and the codes, scales
     and zeros equal round-to-nearest's bit for bit.
+A1. Act-order: columns are quantized in decreasing order of diag(H) (ties to
+    the lower index).  With static groups, every group keeps its natural columns
+    k .. k+G-1 and its round-to-nearest statistics are taken from the original
+    weights before any error feedback; the storage stays in natural order.
+    Without static groups, groups are G consecutive columns of the quantization
+    order, i.e. plain G4 applied to W[:, order] with H[order][:, order]; the
+    storage holds the columns in that order and the forward reads the
+    activations through it: Y = X[:, order] . W_stored^T.
 S1. SpQR sensitivity of weight (n, k): how much the row's output error on the
     calibration inputs falls when that weight leaves the dense part.  The
     error of a group of 16 weights (one row, 16 consecutive k) is
@@ -150,6 +158,60 @@ def _group_error(w, c):
         d = wk - s * (q - z)
         err += ck * (d * d)
     return err
+
+
+def act_order(H) -> np.ndarray:
+    """A1: column order by decreasing diag(H), ties to the lower index (int64 [K])."""
+    return np.argsort(-np.diag(np.asarray(H, dtype=np.float64)), kind="stable")
+
+
+def quantize_w4_actorder(W, H, G: int = 128, damp: float = 0.01, static_groups: bool = True):
+    """A1.  Returns (q, S, z, perm): with static groups q/S/z are in natural
+    column order and perm is the identity; otherwise they are in the stored
+    (quantization) order and perm[t] is the original column of stored column t."""
+    W = np.asarray(W, dtype=F32)
+    N, K = W.shape
+    H = np.asarray(H, dtype=np.float64)
+    order = act_order(H)
+    if not static_groups:
+        q, S, z = quantize_w4(W[:, order], H[np.ix_(order, order)], G, damp)
+        return q, S, z, order.astype(np.int32)
+    if K % G:
+        raise ValueError("K must be a multiple of the group size")
+    S = np.zeros((N, K // G), dtype=np.float16)
+    s = np.zeros((N, K // G), dtype=F32)
+    z = np.zeros((N, K // G), dtype=F32)
+    for n in range(N):
+        for g in range(K // G):
+            S[n, g], s[n, g], z[n, g] = _group_rule(W[n, g * G:(g + 1) * G])
+    U = inverse_cholesky_upper(H[np.ix_(order, order)], damp)
+    Wc = W[:, order].astype(np.float64)
+    q = np.zeros((N, K), dtype=np.uint8)
+    for t in range(K):
+        j = int(order[t])
+        g = j // G
+        w32 = Wc[:, t].astype(F32)
+        qj = np.clip(np.rint(w32 / s[:, g]) + z[:, g], F32(0.0), F32(15.0))
+        q[:, j] = qj.astype(np.uint8)
+        w_hat = s[:, g].astype(np.float64) * (qj.astype(np.float64) - z[:, g].astype(np.float64))
+        e = (Wc[:, t] - w_hat) / U[t, t]
+        Wc[:, t + 1:] -= np.outer(e, U[t, t + 1:])
+    return q, S, z.astype(np.uint8), np.arange(K, dtype=np.int32)
+
+
+def encode_w4_actorder(W, H, G: int = 128, damp: float = 0.01, static_groups: bool = True):
+    """(qweight, scales, qzeros, perm) storage of the act-order encode."""
+    from . import w4 as ow4
+    q, S, z, perm = quantize_w4_actorder(W, H, G, damp, static_groups)
+    return (*ow4.pack(q, S, z), perm)
+
+
+def forward_perm(X, qweight, scales, qzeros, perm, K: int, G: int = 128):
+    """Y = X[:, perm] . W_stored^T in fp64 (the stored columns in quantization order)."""
+    from . import w4 as ow4
+    from .metrics import x_to_f64
+    Xd = x_to_f64(X)
+    return Xd[:, np.asarray(perm, dtype=np.int64)] @ ow4.dequantize(qweight, scales, qzeros, K, G).T
 
 
 def spqr_sensitivity(W, H, damp: float = 0.01) -> np.ndarray:

@@ -25,16 +25,12 @@ qlin_status need_aligned(const char* fn, const char* name, const void* p) {
     if (_s != QLIN_OK) return _s;           \
   } while (0)
 
-}  // namespace
-
-extern "C" {
-
-qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
-                            const uint32_t* qweight, const uint16_t* scales,
-                            const uint32_t* qzeros, int N, int G,
-                            void* Y, int y_dtype, hipStream_t stream) {
-  static const char* fn = "qlin_w4_forward";
-  clear_error();
+// Validation and kernel choice of the W4 forward; with perm != NULL the
+// activations are first gathered into Xp (act-order storage).
+qlin_status w4_forward_checked(const char* fn, const void* X, int x_dtype, int M, int K,
+                               const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int N, int G,
+                               void* Y, int y_dtype, hipStream_t stream, bool gather, const int32_t* perm,
+                               void* Xp) {
   if (M <= 0 || N <= 0 || K <= 0 || G <= 0) return fail(QLIN_EINVAL, std::string(fn) + ": M, N, K, G must be positive");
   if (!X || !qweight || !scales || !qzeros || !Y) return fail(QLIN_EINVAL, std::string(fn) + ": NULL pointer");
   if (x_dtype != QLIN_F16 && x_dtype != QLIN_BF16) return fail(QLIN_EINVAL, std::string(fn) + ": x_dtype must be F16 or BF16");
@@ -48,6 +44,16 @@ qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
   QLIN_TRY(need_aligned(fn, "scales", scales));
   QLIN_TRY(need_aligned(fn, "qzeros", qzeros));
   QLIN_TRY(need_aligned(fn, "Y", Y));
+  if (gather) {
+    if (!perm || !Xp) return fail(QLIN_EINVAL, std::string(fn) + ": NULL perm or Xp");
+    QLIN_TRY(need_aligned(fn, "Xp", Xp));
+    const char* x0 = static_cast<const char*>(X);
+    const char* p0 = static_cast<const char*>(Xp);
+    const size_t bytes = static_cast<size_t>(M) * K * 2;
+    if (p0 < x0 + bytes && x0 < p0 + bytes) return fail(QLIN_EINVAL, std::string(fn) + ": Xp overlaps X");
+    permute_cols_launch(X, perm, M, K, Xp, stream);
+    X = Xp;
+  }
   W4Args a{X, x_dtype, M, K, N, G, qweight, scales, qzeros, Y, y_dtype};
   if (w4_gemv_supported(M, K, G)) {
     w4_gemv_launch(a, stream);
@@ -57,6 +63,28 @@ qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
     w4_gemm_launch(a, stream);
   }
   return check_launch(fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
+                            const uint32_t* qweight, const uint16_t* scales,
+                            const uint32_t* qzeros, int N, int G,
+                            void* Y, int y_dtype, hipStream_t stream) {
+  clear_error();
+  return w4_forward_checked("qlin_w4_forward", X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype, stream,
+                            false, nullptr, nullptr);
+}
+
+qlin_status qlin_w4_forward_perm(const void* X, int x_dtype, int M, int K, const int32_t* perm, void* Xp,
+                                 const uint32_t* qweight, const uint16_t* scales,
+                                 const uint32_t* qzeros, int N, int G,
+                                 void* Y, int y_dtype, hipStream_t stream) {
+  clear_error();
+  return w4_forward_checked("qlin_w4_forward_perm", X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype,
+                            stream, true, perm, Xp);
 }
 
 qlin_status qlin_w4_unpack(const uint32_t* qweight, const uint32_t* qzeros, int N, int K, int G,

@@ -156,6 +156,106 @@ double group_error(const double* w, const double* c, int n) {
 constexpr int kBlock = 128;     // columns per deferred-update block
 constexpr int kRowBatch = 32;   // rows per worker batch (U streams once per batch)
 
+// Shared GPTQ core.  Columns are quantized in the order `order` (natural order
+// unless act_order: decreasing diag(H), ties to the lower index).  Groups:
+//   * static_groups: natural groups of G columns, with round-to-nearest
+//     statistics of the original weights; storage in natural order;
+//   * otherwise: G consecutive columns of the quantization order, statistics of
+//     the current weights at the group's first column; storage in quantization
+//     order (column t of the storage is original column order[t]).
+qlin_status gptq_encode(const char* fn, const float* W, int N, int K, int G, const double* H, double damp,
+                        bool act_order, bool static_groups, uint32_t* qweight, uint16_t* scales,
+                        uint32_t* qzeros, int32_t* perm) {
+  qlin_status st = qlin_w4_sizes(N, K, G, nullptr, nullptr, nullptr);
+  if (st != QLIN_OK) return st;
+  if (!W || !H || !qweight || !scales || !qzeros) return fail(QLIN_EINVAL, std::string(fn) + ": NULL pointer");
+  if (!(damp >= 0.0) || !std::isfinite(damp)) return fail(QLIN_EINVAL, std::string(fn) + ": damp must be >= 0");
+  if (!finite_and_symmetric(H, K)) return fail(QLIN_EINVAL, std::string(fn) + ": H must be finite and symmetric");
+
+  std::vector<int> order(K);
+  for (int k = 0; k < K; ++k) order[k] = k;
+  if (act_order)
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+      return H[static_cast<size_t>(a) * K + a] > H[static_cast<size_t>(b) * K + b];
+    });
+  if (perm)
+    for (int t = 0; t < K; ++t) perm[t] = static_groups ? t : order[t];
+
+  // U = upper Cholesky factor of (Hp + lam I)^-1 with Hp = H in quantization order
+  std::vector<double> Hp(static_cast<size_t>(K) * K);
+  for (int a = 0; a < K; ++a)
+    for (int b = 0; b < K; ++b) Hp[static_cast<size_t>(a) * K + b] = H[static_cast<size_t>(order[a]) * K + order[b]];
+  std::vector<double> A = damped(Hp.data(), K, damp);
+  Hp.clear();
+  Hp.shrink_to_fit();
+  if (!spd_inverse(A, K) || !cholesky_lower(A, K))
+    return fail(QLIN_EINVAL, std::string(fn) + ": H + lam I is not positive definite (raise damp)");
+  std::vector<double> U(static_cast<size_t>(K) * K, 0.0);
+  for (int i = 0; i < K; ++i)
+    for (int j = 0; j <= i; ++j) U[static_cast<size_t>(j) * K + i] = A[static_cast<size_t>(i) * K + j];
+  A.clear();
+  A.shrink_to_fit();
+
+  const int ng = K / G, nzw = (ng + 7) / 8;
+  const int nbatch = (N + kRowBatch - 1) / kRowBatch;
+  parallel_for(nbatch, static_cast<int64_t>(kRowBatch) * K * K / 2, [&](int64_t b) {
+    const int r0 = static_cast<int>(b) * kRowBatch, nr = std::min(kRowBatch, N - r0);
+    // current weights of the batch, in quantization order
+    std::vector<double> Wc(static_cast<size_t>(nr) * K);
+    for (int r = 0; r < nr; ++r)
+      for (int t = 0; t < K; ++t) Wc[static_cast<size_t>(r) * K + t] = W[static_cast<size_t>(r0 + r) * K + order[t]];
+    std::vector<double> E(static_cast<size_t>(nr) * kBlock);     // scaled errors of the current block
+    std::vector<float> s(static_cast<size_t>(nr) * ng), z(static_cast<size_t>(nr) * ng), g32(G);
+    for (int r = 0; r < nr; ++r) {
+      std::fill(qweight + static_cast<size_t>(r0 + r) * (K / 8), qweight + static_cast<size_t>(r0 + r + 1) * (K / 8), 0u);
+      std::fill(qzeros + static_cast<size_t>(r0 + r) * nzw, qzeros + static_cast<size_t>(r0 + r + 1) * nzw, 0u);
+    }
+    auto set_group = [&](int r, int g, const float* w) {
+      uint16_t S;
+      w4_group_stats(w, G, &S, &s[static_cast<size_t>(r) * ng + g], &z[static_cast<size_t>(r) * ng + g]);
+      scales[static_cast<size_t>(r0 + r) * ng + g] = S;
+      qzeros[static_cast<size_t>(r0 + r) * nzw + g / 8] |=
+          static_cast<uint32_t>(z[static_cast<size_t>(r) * ng + g]) << (4 * (g % 8));
+    };
+    if (static_groups)
+      for (int r = 0; r < nr; ++r)
+        for (int g = 0; g < ng; ++g) set_group(r, g, W + static_cast<size_t>(r0 + r) * K + static_cast<size_t>(g) * G);
+    for (int j0 = 0; j0 < K; j0 += kBlock) {
+      const int j1 = std::min(K, j0 + kBlock);
+      for (int j = j0; j < j1; ++j) {
+        const double* uj = &U[static_cast<size_t>(j) * K];
+        const int pos = static_groups ? order[j] : j;     // storage column of quantization step j
+        const int g = pos / G;
+        for (int r = 0; r < nr; ++r) {
+          double* w = &Wc[static_cast<size_t>(r) * K];
+          if (!static_groups && j % G == 0) {
+            for (int i = 0; i < G; ++i) g32[i] = static_cast<float>(w[j + i]);
+            set_group(r, g, g32.data());
+          }
+          const float sr = s[static_cast<size_t>(r) * ng + g], zr = z[static_cast<size_t>(r) * ng + g];
+          const uint32_t q = w4_code(static_cast<float>(w[j]), sr, zr);
+          qweight[static_cast<size_t>(r0 + r) * (K / 8) + pos / 8] |= q << (4 * (pos % 8));
+          const double w_hat = static_cast<double>(sr) * (static_cast<double>(q) - static_cast<double>(zr));
+          const double e = (w[j] - w_hat) / uj[j];
+          E[static_cast<size_t>(r) * kBlock + (j - j0)] = e;
+          for (int k = j + 1; k < j1; ++k) w[k] -= e * uj[k];      // inside the block: now
+        }
+      }
+      // later blocks: the block's updates, applied in column order
+      for (int r = 0; r < nr; ++r) {
+        double* w = &Wc[static_cast<size_t>(r) * K];
+        const double* e = &E[static_cast<size_t>(r) * kBlock];
+        for (int j = j0; j < j1; ++j) {
+          const double* uj = &U[static_cast<size_t>(j) * K];
+          const double ej = e[j - j0];
+          for (int k = j1; k < K; ++k) w[k] -= ej * uj[k];
+        }
+      }
+    }
+  });
+  return QLIN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,70 +285,16 @@ qlin_status qlin_hessian(const float* X, int n, int K, double* H) {
 
 qlin_status qlin_w4_pack_gptq(const float* W, int N, int K, int G, const double* H, double damp,
                               uint32_t* qweight, uint16_t* scales, uint32_t* qzeros) {
-  qlin_status st = qlin_w4_sizes(N, K, G, nullptr, nullptr, nullptr);
-  if (st != QLIN_OK) return st;
-  if (!W || !H || !qweight || !scales || !qzeros) return fail(QLIN_EINVAL, "qlin_w4_pack_gptq: NULL pointer");
-  if (!(damp >= 0.0) || !std::isfinite(damp)) return fail(QLIN_EINVAL, "qlin_w4_pack_gptq: damp must be >= 0");
-  if (!finite_and_symmetric(H, K)) return fail(QLIN_EINVAL, "qlin_w4_pack_gptq: H must be finite and symmetric");
+  return gptq_encode("qlin_w4_pack_gptq", W, N, K, G, H, damp, /*act_order=*/false, /*static_groups=*/false,
+                     qweight, scales, qzeros, nullptr);
+}
 
-  // U = upper Cholesky factor of (H + lam I)^-1: the transpose of its lower factor
-  std::vector<double> A = damped(H, K, damp);
-  if (!spd_inverse(A, K) || !cholesky_lower(A, K))
-    return fail(QLIN_EINVAL, "qlin_w4_pack_gptq: H + lam I is not positive definite (raise damp)");
-  std::vector<double> U(static_cast<size_t>(K) * K, 0.0);
-  for (int i = 0; i < K; ++i)
-    for (int j = 0; j <= i; ++j) U[static_cast<size_t>(j) * K + i] = A[static_cast<size_t>(i) * K + j];
-  A.clear();
-  A.shrink_to_fit();
-
-  const int ng = K / G, nzw = (ng + 7) / 8;
-  const int nbatch = (N + kRowBatch - 1) / kRowBatch;
-  parallel_for(nbatch, static_cast<int64_t>(kRowBatch) * K * K / 2, [&](int64_t b) {
-    const int r0 = static_cast<int>(b) * kRowBatch, nr = std::min(kRowBatch, N - r0);
-    std::vector<double> Wc(static_cast<size_t>(nr) * K);
-    for (int r = 0; r < nr; ++r)
-      for (int k = 0; k < K; ++k) Wc[static_cast<size_t>(r) * K + k] = W[static_cast<size_t>(r0 + r) * K + k];
-    std::vector<double> E(static_cast<size_t>(nr) * kBlock);     // scaled errors of the current block
-    std::vector<float> s(nr), z(nr), g32(G);
-    for (int r = 0; r < nr; ++r) {
-      std::fill(qweight + static_cast<size_t>(r0 + r) * (K / 8), qweight + static_cast<size_t>(r0 + r + 1) * (K / 8), 0u);
-      std::fill(qzeros + static_cast<size_t>(r0 + r) * nzw, qzeros + static_cast<size_t>(r0 + r + 1) * nzw, 0u);
-    }
-    for (int j0 = 0; j0 < K; j0 += kBlock) {
-      const int j1 = std::min(K, j0 + kBlock);
-      for (int j = j0; j < j1; ++j) {
-        const double* uj = &U[static_cast<size_t>(j) * K];
-        for (int r = 0; r < nr; ++r) {
-          double* w = &Wc[static_cast<size_t>(r) * K];
-          if (j % G == 0) {
-            for (int i = 0; i < G; ++i) g32[i] = static_cast<float>(w[j + i]);
-            uint16_t S;
-            w4_group_stats(g32.data(), G, &S, &s[r], &z[r]);
-            const int g = j / G;
-            scales[static_cast<size_t>(r0 + r) * ng + g] = S;
-            qzeros[static_cast<size_t>(r0 + r) * nzw + g / 8] |= static_cast<uint32_t>(z[r]) << (4 * (g % 8));
-          }
-          const uint32_t q = w4_code(static_cast<float>(w[j]), s[r], z[r]);
-          qweight[static_cast<size_t>(r0 + r) * (K / 8) + j / 8] |= q << (4 * (j % 8));
-          const double w_hat = static_cast<double>(s[r]) * (static_cast<double>(q) - static_cast<double>(z[r]));
-          const double e = (w[j] - w_hat) / uj[j];
-          E[static_cast<size_t>(r) * kBlock + (j - j0)] = e;
-          for (int k = j + 1; k < j1; ++k) w[k] -= e * uj[k];      // inside the block: now
-        }
-      }
-      // later blocks: the block's updates, applied in column order
-      for (int r = 0; r < nr; ++r) {
-        double* w = &Wc[static_cast<size_t>(r) * K];
-        const double* e = &E[static_cast<size_t>(r) * kBlock];
-        for (int j = j0; j < j1; ++j) {
-          const double* uj = &U[static_cast<size_t>(j) * K];
-          const double ej = e[j - j0];
-          for (int k = j1; k < K; ++k) w[k] -= ej * uj[k];
-        }
-      }
-    }
-  });
-  return QLIN_OK;
+qlin_status qlin_w4_pack_gptq_actorder(const float* W, int N, int K, int G, const double* H, double damp,
+                                       int static_groups, uint32_t* qweight, uint16_t* scales, uint32_t* qzeros,
+                                       int32_t* perm) {
+  if (!perm) return fail(QLIN_EINVAL, "qlin_w4_pack_gptq_actorder: NULL pointer");
+  return gptq_encode("qlin_w4_pack_gptq_actorder", W, N, K, G, H, damp, /*act_order=*/true, static_groups != 0,
+                     qweight, scales, qzeros, perm);
 }
 
 qlin_status spqr_pack_hessian(const float* W, int N, int K, double p, const double* H, double damp,

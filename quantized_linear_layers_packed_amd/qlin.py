@@ -45,6 +45,7 @@ EXPORTS = (
     "sq_act_absmax", "sq_compute_smoothing", "sq_pack_weight", "sq_smooth_quant_act", "sq_int8_gemm",
     "qlin_stream_read", "qlin_stream_copy",
     "qlin_hessian", "qlin_w4_pack_gptq", "spqr_pack_hessian",
+    "qlin_w4_pack_gptq_actorder", "qlin_w4_forward_perm",
 )
 
 _vp, _i, _i64, _sz, _d = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.c_double
@@ -70,6 +71,8 @@ _sigs = {
     "qlin_hessian": ([_vp, _i, _i, _vp], _i),
     "qlin_w4_pack_gptq": ([_vp, _i, _i, _i, _vp, _d, _vp, _vp, _vp], _i),
     "spqr_pack_hessian": ([_vp, _i, _i, _d, _vp, _d, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp], _i),
+    "qlin_w4_pack_gptq_actorder": ([_vp, _i, _i, _i, _vp, _d, _i, _vp, _vp, _vp, _vp], _i),
+    "qlin_w4_forward_perm": ([_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _vp], _i),
 }
 for _name, (_args, _res) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -171,6 +174,27 @@ def qlin_w4_pack_gptq(W: np.ndarray, G: int, H: np.ndarray, damp: float = 0.01):
     qz = np.zeros((N, (K // G + 7) // 8), np.uint32)
     _check(_lib.qlin_w4_pack_gptq(_ptr(W), N, K, G, _ptr(H), damp, _ptr(qw), _ptr(sc), _ptr(qz)))
     return qw, sc.view(np.float16), qz
+
+
+def qlin_w4_pack_gptq_actorder(W: np.ndarray, G: int, H: np.ndarray, damp: float = 0.01,
+                               static_groups: bool = True):
+    """Act-order second-order encode; returns (qweight, scales, qzeros, perm)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    H = np.ascontiguousarray(H, dtype=np.float64)
+    N, K = W.shape
+    qlin_w4_sizes(N, K, G)
+    qw = np.zeros((N, K // 8), np.uint32)
+    sc = np.zeros((N, K // G), np.uint16)
+    qz = np.zeros((N, (K // G + 7) // 8), np.uint32)
+    perm = np.zeros(K, np.int32)
+    _check(_lib.qlin_w4_pack_gptq_actorder(_ptr(W), N, K, G, _ptr(H), damp, int(bool(static_groups)), _ptr(qw),
+                                           _ptr(sc), _ptr(qz), _ptr(perm)))
+    return qw, sc.view(np.float16), qz, perm
+
+
+def qlin_w4_forward_perm(X, x_dtype, M, K, perm, Xp, qweight, scales, qzeros, N, G, Y, y_dtype, stream=None):
+    _check(_lib.qlin_w4_forward_perm(_ptr(X), x_dtype, M, K, _ptr(perm), _ptr(Xp), _ptr(qweight), _ptr(scales),
+                                     _ptr(qzeros), N, G, _ptr(Y), y_dtype, _stream(stream)))
 
 
 def qlin_w4_forward(X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype, stream=None):

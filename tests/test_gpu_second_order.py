@@ -70,3 +70,37 @@ def test_sensitivity_spqr_encode_through_the_fused_kernel():
         qlin.spqr_forward(dev(X), M, K, d["codes"], d["stats1"], d["stats2"], d["row_ptr"],
                           d["col_idx"], d["val"], nnz, N, Y, F32)
         check_close(host(Y).astype(np.float64), ospqr.forward(X, st, K), f"spqr M={M}")
+
+
+@pytest.mark.parametrize("G", [128, 64])
+def test_act_order_forward_through_the_gather(G):
+    """Act-order storage without static groups runs through qlin_w4_forward_perm
+    (gather of X by perm, then the regular kernels): parity with the oracle's
+    X[:, perm] . W_stored^T at GEMV and GEMM batch sizes; with static groups the
+    storage is natural and runs through qlin_w4_forward; an identity perm gives
+    qlin_w4_forward's result bit for bit."""
+    from oracle import gptq as ogptq
+    torch = torch_cuda()
+    N, K = 640, 2048
+    g = np.random.default_rng(15)
+    W = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Xc = (_calibration(256, K, 16).astype(np.float32) * np.exp(g.standard_normal(K) * 0.7)).astype(np.float16)
+    H = qlin.qlin_hessian(Xc.astype(np.float32))
+    dyn = qlin.qlin_w4_pack_gptq_actorder(W, G, H, static_groups=False)
+    sta = qlin.qlin_w4_pack_gptq_actorder(W, G, H, static_groups=True)
+    qw, sc, qz, perm = (dev(a) for a in dyn)
+    ident = dev(np.arange(K, dtype=np.int32))
+    for M in (1, 8, 64):
+        say(f"act-order W4 N={N} K={K} G={G} M={M}")
+        X = Xc[:M]
+        Xd = dev(X)
+        Xp = empty((M, K), torch.float16)
+        Y = empty((M, N), torch.float32)
+        qlin.qlin_w4_forward_perm(Xd, F16, M, K, perm, Xp, qw, sc, qz, N, G, Y, F32)
+        check_close(host(Y).astype(np.float64), ogptq.forward_perm(X, *dyn, K, G), f"dynamic groups M={M}")
+        check_close(_w4_gpu(X, sta[:3], N, K, G), ow4.forward(X, *sta[:3], K, G), f"static groups M={M}")
+        Y1 = empty((M, N), torch.float32)
+        qlin.qlin_w4_forward_perm(Xd, F16, M, K, ident, Xp, qw, sc, qz, N, G, Y1, F32)
+        Y2 = empty((M, N), torch.float32)
+        qlin.qlin_w4_forward(Xd, F16, M, K, qw, sc, qz, N, G, Y2, F32)
+        assert np.array_equal(host(Y1), host(Y2))

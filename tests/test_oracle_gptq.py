@@ -169,3 +169,90 @@ def test_sensitivity_outliers_keep_the_storage_rules():
         assert np.array_equal(np.asarray(st[k]).view(np.uint8), np.asarray(ref[k]).view(np.uint8)), k
     rows = np.repeat(np.arange(16), np.diff(st["row_ptr"]))
     assert np.array_equal(np.flatnonzero(mask), rows * 512 + st["col_idx"])
+
+
+def _energy_x(n, K, seed):
+    """Correlated inputs whose channels carry very different energies (the case
+    act-order is for)."""
+    g = np.random.default_rng(seed)
+    A = g.standard_normal((K, K)) * (3.0 / np.sqrt(K)) + np.eye(K)
+    gain = np.exp(g.standard_normal(K) * 0.7)
+    return ((g.standard_normal((n, K)) @ A) * gain).astype(F32)
+
+
+@pytest.mark.parametrize("static_groups", [True, False])
+def test_act_order_with_a_flat_diagonal_is_the_natural_order(static_groups):
+    """diag(H) constant: the order is the natural one (ties to the lower index),
+    so both act-order variants equal the natural-order encode."""
+    N, K, G = 16, 256, 64
+    W = _weights(N, K, 20)
+    X = _correlated_x(300, K, 21)
+    X /= np.sqrt(np.mean(X.astype(np.float64) ** 2, axis=0))[None, :].astype(F32)   # unit-energy columns
+    H = gptq.hessian(X)
+    H[np.diag_indices(K)] = 2.0                         # flat diagonal, same correlations
+    q, S, z, perm = gptq.quantize_w4_actorder(W, H, G, static_groups=static_groups)
+    assert np.array_equal(perm, np.arange(K))
+    q0, S0, z0 = gptq.quantize_w4(W, H, G)
+    if static_groups:
+        # natural order, but statistics from the original weights
+        assert np.array_equal(S.view(np.uint16), w4.quantize_rtn(W, G)[1].view(np.uint16))
+    else:
+        assert np.array_equal(q, q0) and np.array_equal(S.view(np.uint16), S0.view(np.uint16))
+        assert np.array_equal(z, z0)
+
+
+def test_static_groups_keep_round_to_nearest_statistics_and_match_brute_force():
+    """Static groups: scales and zeros are round-to-nearest's bit for bit; the
+    codes equal a brute-force Optimal Brain Surgeon pass in act-order that
+    re-inverts the damped H on the not-yet-quantized columns at every step."""
+    N, K, G = 4, 128, 32
+    W = _weights(N, K, 22)
+    H = gptq.hessian(_energy_x(300, K, 23))
+    q, S, z, perm = gptq.quantize_w4_actorder(W, H, G, static_groups=True)
+    q0, S0, z0 = w4.quantize_rtn(W, G)
+    assert np.array_equal(S.view(np.uint16), S0.view(np.uint16)) and np.array_equal(z, z0)
+    order = np.argsort(-np.diag(H), kind="stable")
+    assert np.all(np.diff(np.diag(H)[order]) <= 0)
+    Hd = gptq.damped(H[np.ix_(order, order)])
+    s0 = S0.astype(F32)
+    q_ref = np.zeros((N, K), np.uint8)
+    for n in range(N):
+        w = W[n, order].astype(np.float64)
+        for t in range(K):
+            j = order[t]
+            s, zz = s0[n, j // G], F32(z0[n, j // G])
+            qj = np.clip(np.rint(F32(w[t]) / s) + zz, F32(0), F32(15))
+            q_ref[n, j] = np.uint8(qj)
+            Finv = np.linalg.inv(Hd[t:, t:])
+            w[t:] -= (w[t] - np.float64(s) * (np.float64(qj) - np.float64(zz))) * Finv[:, 0] / Finv[0, 0]
+    assert np.array_equal(q, q_ref)
+
+
+def test_act_order_forward_reads_the_activations_through_perm():
+    """Closed form: X[:, perm] . W_stored^T = X . W_natural^T with the stored
+    columns scattered back to their input columns."""
+    N, K, G = 24, 256, 128
+    W = _weights(N, K, 24)
+    X = _energy_x(64, K, 25)
+    st = gptq.encode_w4_actorder(W, gptq.hessian(X), G, static_groups=False)
+    perm = st[3]
+    assert sorted(perm.tolist()) == list(range(K))
+    Wst = w4.dequantize(*st[:3], K, G)
+    Wnat = np.empty_like(Wst)
+    Wnat[:, perm] = Wst
+    Xh = X.astype(np.float16)
+    assert np.allclose(gptq.forward_perm(Xh, *st, K, G), Xh.astype(np.float64) @ Wnat.T, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("static_groups", [True, False])
+def test_act_order_reduces_the_error_where_channel_energies_differ(static_groups):
+    N, K, G = 48, 512, 128
+    W = _weights(N, K, 26)
+    X = _energy_x(600, K, 27)
+    H = gptq.hessian(X)
+    ex = X.astype(np.float64) @ W.astype(np.float64).T
+    e_nat = np.linalg.norm(w4.forward(X.astype(np.float16), *gptq.encode_w4(W, H, G), K, G) - ex)
+    st = gptq.encode_w4_actorder(W, H, G, static_groups=static_groups)
+    Y = gptq.forward_perm(X.astype(np.float16), *st, K, G)
+    e_act = np.linalg.norm(Y - ex)
+    assert e_act < 0.9 * e_nat, (e_act, e_nat)

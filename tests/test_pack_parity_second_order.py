@@ -81,3 +81,16 @@ def test_second_order_calls_reject_bad_arguments():
         qlin.qlin_w4_pack_gptq(W, 128, H, damp=-1.0)
     with pytest.raises(qlin.QlinError):
         qlin.qlin_hessian(np.zeros((0, 8), F32))
+
+
+@pytest.mark.parametrize("static_groups", [True, False])
+@pytest.mark.parametrize("N,K,G", [(40, 512, 128), (33, 256, 32), (64, 1024, 256)])
+def test_act_order_storage_identical(N, K, G, static_groups):
+    g = np.random.default_rng(N + K + G)
+    W = (g.standard_normal((N, K)) * 0.02).astype(F32)
+    X = _correlated_x(256, K, K + 1) * np.exp(g.standard_normal(K) * 0.7).astype(F32)
+    H = gptq.hessian(X)
+    lib = qlin.qlin_w4_pack_gptq_actorder(W, G, H, static_groups=static_groups)
+    ref = gptq.encode_w4_actorder(W, H, G, static_groups=static_groups)
+    for a, b in zip(lib, ref):
+        assert _same(a, b)
