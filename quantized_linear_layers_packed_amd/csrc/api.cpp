@@ -55,8 +55,12 @@ qlin_status w4_forward_checked(const char* fn, const void* X, int x_dtype, int M
     X = Xp;
   }
   W4Args a{X, x_dtype, M, K, N, G, qweight, scales, qzeros, Y, y_dtype};
-  if (w4_gemv_supported(M, K, G)) {
+  // M = 1 (and M <= 3 while the activations fit its LDS staging): the GEMV;
+  // M = 4 .. 16: the small-batch MFMA kernel; larger: the GEMMs.
+  if (w4_gemv_supported(M, K, G) && (M <= 3 || !w4_skinny_supported(M, K, G))) {
     w4_gemv_launch(a, stream);
+  } else if (w4_skinny_supported(M, K, G)) {
+    w4_skinny_launch(a, stream);
   } else if (G >= 128) {
     QLIN_TRY(w4_gemm_sk_launch(a, stream));
   } else {

@@ -29,6 +29,10 @@ void w4_gemv_launch(const W4Args& a, hipStream_t stream);
 // (uses the library workspace), one-group-per-step kernel for 32 / 64.
 qlin_status w4_gemm_sk_launch(const W4Args& a, hipStream_t stream);
 void w4_gemm_launch(const W4Args& a, hipStream_t stream);
+// Small batches (M <= 16, G = 128 / 256): 16 columns per workgroup, K split
+// over its waves, fp16 MFMA, no workspace.
+bool w4_skinny_supported(int M, int K, int G);
+void w4_skinny_launch(const W4Args& a, hipStream_t stream);
 // Xp[m][t] = X[m][perm[t]] for 16-bit activations (act-order storage).
 void permute_cols_launch(const void* X, const int32_t* perm, int M, int K, void* Xp, hipStream_t stream);
 void w4_unpack_launch(const uint32_t* qweight, const uint32_t* qzeros, int N, int K, int G,

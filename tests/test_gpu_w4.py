@@ -96,14 +96,28 @@ def test_gemv_ragged_shapes_and_dtypes(G, x_dtype, K):
         assert np.array_equal(yb, f32_to_bf16_bits(y32)), "bf16 store is not RNE of the fp32 result"
 
 
-def test_gemv_batch_rows_are_independent():
+def test_batch_rows_are_independent():
+    """A row's result does not depend on the other rows of its batch, bit for
+    bit within each kernel: the GEMV (M <= 3), the small-batch kernel
+    (M = 4..16) and the stream-K GEMM (M = 17..32 share one split plan); across
+    kernels the results agree within tolerance."""
     W = synth.normal_f32((256, 1024), 0.02, "gpu/w4/indep")
     packed = dev_pack(W, 128)
-    X = synth.x_f16(16, 1024, "gpu/w4/indepx")
-    full = gpu_w4(X, F16, packed, 256, 1024, 128, F32)
-    for m in (0, 5, 15):
-        one = gpu_w4(X[m:m + 1], F16, packed, 256, 1024, 128, F32)
-        assert np.array_equal(one[0], full[m])
+    X = synth.x_f16(32, 1024, "gpu/w4/indepx")
+
+    def run(rows):
+        return gpu_w4(np.ascontiguousarray(X[rows]), F16, packed, 256, 1024, 128, F32)
+
+    full3 = run(list(range(3)))
+    for m in range(3):
+        assert np.array_equal(run([m])[0], full3[m])
+    full16 = run(list(range(16)))
+    for m in (0, 5, 12):
+        assert np.array_equal(run(list(range(m, m + 4)))[0], full16[m])
+    full32 = run(list(range(32)))
+    assert np.array_equal(run(list(range(17)))[:17], full32[:17])
+    check_close(full3, full16[:3], "GEMV vs small-batch kernel")
+    check_close(full16, full32[:16], "small-batch kernel vs GEMM")
 
 
 @pytest.mark.parametrize("x_dtype", [BF16, F16])
@@ -157,16 +171,18 @@ def test_small_batch_beyond_the_gemv_range_uses_the_gemm():
         check_close(gpu_w4(X, F16, packed, N, K, 128, F32), ow4.forward(X, *st, K, 128), f"M={M}")
 
 
-def test_gemm_small_batches_with_split_tiles():
+@pytest.mark.parametrize("x_dtype", [F16, BF16])
+def test_small_batches_through_the_mfma_kernels(x_dtype):
     """Batches of 2..24 rows on layers whose activations exceed the GEMV's LDS
-    staging run the MFMA GEMM with few output tiles, so every tile's K range is
-    split over many workgroups; the fix-up then sums only the accumulator
-    registers that can hold rows below M."""
+    staging: 4..16 rows run the small-batch kernel (K split over the waves of a
+    workgroup, 16 columns each, ragged N), 17 and more the stream-K GEMM with
+    few output tiles, so every tile's K range is split over many workgroups and
+    the fix-up sums only the accumulator registers that can hold rows below M."""
     for (N, K, G) in ((512, 8192, 128), (300, 6144, 256)):
         W = synth.normal_f32((N, K), 0.02, f"gpu/w4/smallm{N}")
         packed = dev_pack(W, G)
         st = ow4.encode(W, G)
-        for M in (2, 5, 8, 9, 16, 17, 24):
-            say(f"w4 small-batch gemm N={N} K={K} G={G} M={M}")
-            X = synth.x_f16(M, K, f"gpu/w4/smallmx{M}")
-            check_close(gpu_w4(X, F16, packed, N, K, G, F32), ow4.forward(X, *st, K, G), f"M={M}")
+        for M in (2, 4, 5, 8, 9, 16, 17, 24):
+            say(f"w4 small-batch N={N} K={K} G={G} M={M} x={x_dtype}")
+            X = (synth.x_bf16_bits if x_dtype == BF16 else synth.x_f16)(M, K, f"gpu/w4/smallmx{M}")
+            check_close(gpu_w4(X, x_dtype, packed, N, K, G, F32), ow4.forward(X, *st, K, G), f"M={M}")
