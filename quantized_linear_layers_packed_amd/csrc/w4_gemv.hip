@@ -280,7 +280,8 @@ void launch_m(const W4Args& a, hipStream_t stream) {
   // One row per wave, 64 lanes; rows with more than two blocks of 64 chunks are
   // split over KS waves (at most 4 blocks per wave, so the unpacked codes of the
   // wave fit in registers and the per-wave tail after the activations arrive
-  // stays short).  Rows per wave and fewer lanes per row were measured slower.
+  // stays short).  Rows per wave, fewer lanes per row and 16-wave workgroups
+  // were measured slower.
   const int blocks = ((a.K >> 5) + 63) / 64;
   if (blocks <= 1) launch_b<MT, 64, 1, 1>(a, stream);
   else if (blocks <= 2) launch_b<MT, 64, 1, 2>(a, stream);
