@@ -7,8 +7,9 @@
 // warns that mixing the irregular sparse part with dense blocks costs register
 // pressure and divergence.  Here both parts feed ONE fp32 accumulator per
 // (row, batch entry) in the same pass:
-//   * 16 lanes share an output row (4 rows per wavefront); lane j of a row reads
-//     the 32-code chunks j, j+16, ... (three 32-bit words each);
+//   * a row is served by one wave (two for long rows, each taking half of its
+//     chunks); lane j of a wave reads the 32-code chunks j, j+64, ... of its
+//     part (three 32-bit words each);
 //   * the chunk layout places two codes of the same group in field i of the low
 //     and high 16-bit halves of a word, so one shift + and-or yields an fp16 pair
 //     1024 + 8c exactly, ready for v_dot2 against activation pairs staged in LDS
@@ -16,11 +17,13 @@
 //   * the two first-level statistics of the chunk's groups are decoded from
 //     their 3-bit codes and the block's fp16 second-level values
 //     (s_hat = SS_s (c_s - ZS_s), z_hat = SS_z (c_z - ZS_z)) in fp32;
-//   * then the same 16 lanes walk the row's CSR segment (entry e goes to lane
-//     e mod 16), gather x from LDS and add x * v into the same accumulators,
-//     before the one 16-lane reduction that produces Y.  No second pass, no
-//     atomics.
+//   * then the same lanes walk the row's CSR segment (entry e goes to lane
+//     e mod 64 of one of the row's waves), gather x from LDS and add x * v into
+//     the same accumulators, before one DPP reduction per row (and a
+//     fixed-order sum of its waves' parts).  No second pass, no atomics.
 // Activations are staged in K-slices when M*K does not fit the LDS budget.
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "device.hpp"
@@ -90,49 +93,76 @@ __device__ __forceinline__ uint32_t half_of(const uint32_t u[16], int o) {
   return (u[o >> 1] >> (16 * (o & 1))) & 0xFFFFu;
 }
 
-// One wavefront per output row.  Lane l reads chunks l, l + 64, ... of the
-// current K slice (12 bytes each, 768 contiguous bytes per load instruction).
-// Everything the wave needs from HBM for the slice is requested up front: its
-// chunks, the statistics of the slice's blocks (written to a per-wave LDS area
-// as [stats1 w0, w1, w2, stats2 w0] + [stats2 w1] so that a chunk fetches them
-// with two LDS reads) and, on the first slice, up to 4 CSR entries per lane.
-// After the dense chunks, the row's CSR entries that fall in the slice add into
-// the same accumulators; one 64-lane reduction per row and batch entry.
-template <int MT, int BPL, int OUTK>
+// Sum over the 64 lanes of a wave with DPP row operations and row broadcasts;
+// the total ends up in lane 63.
+__device__ __forceinline__ float row_sum64(float v) {
+  auto dpp = [](float x, auto ctrl_c) -> float {
+    constexpr int C = decltype(ctrl_c)::value;
+    constexpr int RM = C == 0x142 ? 0xA : C == 0x143 ? 0xC : 0xF;
+    constexpr bool BC = C != 0x142 && C != 0x143;
+    return bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(x), C, RM, 0xF, BC));
+  };
+  v += dpp(v, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]: pairs
+  v += dpp(v, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]: quads
+  v += dpp(v, std::integral_constant<int, 0x141>{});   // row_half_mirror: groups of 8
+  v += dpp(v, std::integral_constant<int, 0x140>{});   // row_mirror: rows of 16
+  v += dpp(v, std::integral_constant<int, 0x142>{});   // row_bcast:15 into rows 1 and 3
+  v += dpp(v, std::integral_constant<int, 0x143>{});   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// A row is served by KSW waves, each taking a contiguous run of the slice's
+// chunks (a multiple of 8 chunks, so a wave's statistic blocks are its own);
+// lane l of a wave reads its chunks l, l + 64, ... (12 bytes each, 768
+// contiguous bytes per load instruction).  Per slice, in this order:
+//   1. the activation loads for the LDS staging (one 32-value piece per
+//      thread; vector loads return in order, so these arrive first),
+//   2. everything the wave needs from HBM: its chunks, the statistics of its
+//      blocks and, on the first slice, up to 4 CSR entries per lane,
+//   3. the staging (pairs in the unpack order + two per-chunk sums) and the
+//      wave's statistics into LDS,
+//   4. the code unpack, while other waves' staging may still be in flight,
+//   5. after the barrier, the dot products, then the row's CSR entries of the
+//      slice into the same accumulators.
+// One DPP reduction per row and batch entry; the KSW parts are added in a
+// fixed order through LDS.  All loads are unconditional (clamped addresses).
+template <int MT, int KSW, int BPL, int OUTK>
 __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
-    const uint16_t* __restrict__ X, int M, int K, int KS,
-    const uint32_t* __restrict__ codes, const uint32_t* __restrict__ stats1,
-    const uint16_t* __restrict__ stats2, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ col_idx, const uint16_t* __restrict__ vals,
-    int N, void* __restrict__ Y) {
+    const uint16_t* X, int M, int K, int KS,
+    const uint32_t* codes, const uint32_t* stats1,
+    const uint16_t* stats2, const int32_t* row_ptr,
+    const int32_t* col_idx, const uint16_t* vals,
+    int N, void* Y) {
   constexpr int kCsr = 4;                             // CSR entries per lane held in registers
   extern __shared__ uint4 smem[];
+  __shared__ float red[kWaves][MT];
   const int CS = KS >> 5;                             // chunks per slice
   const int BS = KS >> 8;                             // statistic blocks per slice
   uint4* xl = smem;                                   // [MT][4][CS] pair quads
   float* xs = reinterpret_cast<float*>(smem + static_cast<size_t>(MT) * 4 * CS);   // [MT][2*CS]
-  const int wv = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int part = wv % KSW;
   uint4* st4 = reinterpret_cast<uint4*>(xs + static_cast<size_t>(MT) * 2 * CS) + static_cast<size_t>(wv) * BS;
   uint32_t* st1 = reinterpret_cast<uint32_t*>(reinterpret_cast<uint4*>(xs + static_cast<size_t>(MT) * 2 * CS) +
                                               static_cast<size_t>(kWaves) * BS) + static_cast<size_t>(wv) * BS;
 
-  const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * kWaves + wv;
+  const int n = blockIdx.x * (kWaves / KSW) + wv / KSW;
   const bool nok = n < N;
-  const int nb = K >> 8;
-  const size_t nrow = nok ? static_cast<size_t>(n) : 0;
-  const uint32_t* crow = codes + nrow * (K >> 5) * 3;
+  const int C = K >> 5, nb = K >> 8;
+  const size_t nrow = static_cast<size_t>(min(n, N - 1));
+  const uint32_t* crow = codes + nrow * C * 3;
   const uint32_t* s1row = stats1 + nrow * nb * 3;
   const uint2* s2row = reinterpret_cast<const uint2*>(stats2) + nrow * nb;
   const int e0 = nok ? row_ptr[n] : 0;
   const int e1 = nok ? row_ptr[n + 1] : 0;
 
-  // CSR entries of this row held by this lane: e0 + lane + 64 i
+  // CSR entries of this row held by this lane: e0 + 64 (KSW i + part) + lane
   int ccol[kCsr];
   float cval[kCsr];
 #pragma unroll
   for (int i = 0; i < kCsr; ++i) {
-    const int e = e0 + lane + 64 * i;
+    const int e = e0 + 64 * (KSW * i + part) + lane;
     ccol[i] = -1;
     cval[i] = 0.0f;
     if (e < e1) {
@@ -149,67 +179,88 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
     const int ks = min(KS, K - k0);
     const int cs = ks >> 5, bs = ks >> 8;
     const int cbase = k0 >> 5, bbase = k0 >> 8;
-    // ---- weight and statistics loads of this slice
+    const int cp = ((cs + KSW - 1) / KSW + 7) & ~7;   // chunks per part, a multiple of 8
+    const int c0 = part * cp, c1 = min(cs, c0 + cp);
+    const int b0 = c0 >> 3, b1 = min(bs, (c1 + 7) >> 3);
+
+    // ---- 1. first staging piece of this thread (item it = tid; clamped)
+    const int items = M * cs;
+    uint4 xv[4];
+    {
+      const int it = min(tid, items - 1);
+      const int m = it / cs, c = it - m * cs;
+      const uint4* src = reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K + k0) + 4 * c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xv[i] = src[i];
+    }
+    // ---- 2. this wave's chunks and statistics (clamped into the row)
     uint3 w[BPL];
 #pragma unroll
     for (int b = 0; b < BPL; ++b) {
-      const int c = 64 * b + lane;
-      if (nok && c < cs) w[b] = *reinterpret_cast<const uint3*>(crow + 3 * (cbase + c));
+      const int c = min(c0 + 64 * b + lane, cs - 1);
+      w[b] = *reinterpret_cast<const uint3*>(crow + 3 * (cbase + c));
     }
     uint3 s1[2];
     uint2 s2[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int blk = 64 * t + lane;
-      if (nok && blk < bs) {
-        s1[t] = *reinterpret_cast<const uint3*>(s1row + 3 * (bbase + blk));
-        s2[t] = s2row[bbase + blk];
-      }
+      const int blk = min(b0 + 64 * t + lane, bs - 1);
+      s1[t] = *reinterpret_cast<const uint3*>(s1row + 3 * (bbase + blk));
+      s2[t] = s2row[bbase + blk];
     }
-    // ---- stage the activation slice as pairs + per-group sums; this row's statistics
+    // ---- 3. staging (the previous slice's readers are done after this barrier)
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int blk = 64 * t + lane;
-      if (nok && blk < bs) {
+      const int blk = b0 + 64 * t + lane;
+      if (blk < b1) {
         st4[blk] = make_uint4(s1[t].x, s1[t].y, s1[t].z, s2[t].x);
         st1[blk] = s2[t].y;
       }
     }
-    for (int it = threadIdx.x; it < M * cs; it += kThreads) {
+    for (int it = tid; it < items; it += kThreads) {
       const int m = it / cs, c = it - m * cs;
-      const uint4* src = reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K + k0) + 4 * c;
       uint32_t u[16];
+      if (it == tid) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v = src[i];
-        u[4 * i] = v.x; u[4 * i + 1] = v.y; u[4 * i + 2] = v.z; u[4 * i + 3] = v.w;
+        for (int i = 0; i < 4; ++i) {
+          u[4 * i] = xv[i].x; u[4 * i + 1] = xv[i].y; u[4 * i + 2] = xv[i].z; u[4 * i + 3] = xv[i].w;
+        }
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K + k0) + 4 * c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = src[i];
+          u[4 * i] = v.x; u[4 * i + 1] = v.y; u[4 * i + 2] = v.z; u[4 * i + 3] = v.w;
+        }
       }
       uint32_t P[16];
 #pragma unroll
-      for (int p = 0; p < 16; ++p) P[p] = half_of(u, pair_lo(p)) | (half_of(u, pair_hi(p)) << 16);
+      for (int q = 0; q < 16; ++q) P[q] = half_of(u, pair_lo(q)) | (half_of(u, pair_hi(q)) << 16);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         xl[(static_cast<size_t>(m) * 4 + q) * CS + c] = make_uint4(P[4 * q], P[4 * q + 1], P[4 * q + 2], P[4 * q + 3]);
       // group sums by dot products with (1, 1): pairs 0..7 hold group 2c, 8..15 group 2c+1
       float sa = 0.0f, sb = 0.0f;
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        sa = dot2_f16(P[p], 0x3C003C00u, sa);
-        sb = dot2_f16(P[8 + p], 0x3C003C00u, sb);
+      for (int q = 0; q < 8; ++q) {
+        sa = dot2_f16(P[q], 0x3C003C00u, sa);
+        sb = dot2_f16(P[8 + q], 0x3C003C00u, sb);
       }
       xs[m * 2 * CS + 2 * c] = sa;
       xs[m * 2 * CS + 2 * c + 1] = sb;
     }
+    // ---- 4. unpack this wave's chunks while the staging completes
+    uint32_t pk[BPL][16];
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) unpack_chunk(w[b].x, w[b].y, w[b].z, pk[b]);
     __syncthreads();
-    if (!nok) continue;
 
-    // ---- dense 3-bit part
-    const int nfull = cs >> 6;                         // blocks of 64 chunks with every lane busy
+    // ---- 5. dense 3-bit part
 #pragma unroll
     for (int b = 0; b < BPL; ++b) {
-      const int c = 64 * b + lane;
-      if (b < nfull || (b == nfull && c < cs)) {
+      const int c = c0 + 64 * b + lane;
+      if (nok && c < c1) {
         const int blk = c >> 3, j = c & 7;             // block within the slice; chunk within the block
         const uint4 sb4 = st4[blk];
         const uint32_t szw = st1[blk];
@@ -225,8 +276,6 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
         const float zA = SSz * (static_cast<float>((f >> 3) & 7u) - ZSz);
         const float sB = SSs * (static_cast<float>((f >> 6) & 7u) - ZSs);
         const float zB = SSz * (static_cast<float>((f >> 9) & 7u) - ZSz);
-        uint32_t p[16];
-        unpack_chunk(w[b].x, w[b].y, w[b].z, p);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m < M) {
@@ -235,15 +284,15 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
             for (int q = 0; q < 4; ++q) {
               const uint4 xp = xl[(static_cast<size_t>(m) * 4 + q) * CS + c];
               if (q < 2) {
-                aA = dot2_f16(p[4 * q], xp.x, aA);
-                aA = dot2_f16(p[4 * q + 1], xp.y, aA);
-                aA = dot2_f16(p[4 * q + 2], xp.z, aA);
-                aA = dot2_f16(p[4 * q + 3], xp.w, aA);
+                aA = dot2_f16(pk[b][4 * q], xp.x, aA);
+                aA = dot2_f16(pk[b][4 * q + 1], xp.y, aA);
+                aA = dot2_f16(pk[b][4 * q + 2], xp.z, aA);
+                aA = dot2_f16(pk[b][4 * q + 3], xp.w, aA);
               } else {
-                aB = dot2_f16(p[4 * q], xp.x, aB);
-                aB = dot2_f16(p[4 * q + 1], xp.y, aB);
-                aB = dot2_f16(p[4 * q + 2], xp.z, aB);
-                aB = dot2_f16(p[4 * q + 3], xp.w, aB);
+                aB = dot2_f16(pk[b][4 * q], xp.x, aB);
+                aB = dot2_f16(pk[b][4 * q + 1], xp.y, aB);
+                aB = dot2_f16(pk[b][4 * q + 2], xp.z, aB);
+                aB = dot2_f16(pk[b][4 * q + 3], xp.w, aB);
               }
             }
             // sum x (c - z_hat) = acc / 8 - (128 + z_hat) * sum(x)
@@ -272,33 +321,55 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
         }
       }
     };
+    if (nok) {
 #pragma unroll
-    for (int i = 0; i < kCsr; ++i)
-      if (ccol[i] >= 0) outlier(ccol[i], cval[i]);
-    for (int e = e0 + lane + 64 * kCsr; e < e1; e += 64) outlier(col_idx[e], f16_bits_to_f32(vals[e]));
+      for (int i = 0; i < kCsr; ++i)
+        if (ccol[i] >= 0) outlier(ccol[i], cval[i]);
+      for (int e = e0 + 64 * (KSW * kCsr + part) + lane; e < e1; e += 64 * KSW)
+        outlier(col_idx[e], f16_bits_to_f32(vals[e]));
+    }
   }
 
-  // ---- 64-lane reduction and store
+  // ---- reduction over the row's lanes, then over its KSW waves in a fixed order
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     if (m < M) {
-      const float r = wave_sum(res[m]);
-      if (nok && lane == 0) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, r);
+      const float r = row_sum64(res[m]);
+      if constexpr (KSW == 1) {
+        if (nok && lane == 63) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, r);
+      } else {
+        if (lane == 63) red[wv][m] = r;
+      }
+    }
+  }
+  if constexpr (KSW > 1) {
+    __syncthreads();
+    if (part == 0 && lane == 63 && nok) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < M) {
+          float v = red[wv][m];
+#pragma unroll
+          for (int q = 1; q < KSW; ++q) v += red[wv + q][m];
+          store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, v);
+        }
+      }
     }
   }
 }
 
-template <int MT, int BPL>
+template <int MT, int KSW, int BPL>
 void launch_k(const SpqrArgs& a, int KS, hipStream_t stream) {
   const int CS = KS / 32, BS = KS / 256;
   const size_t lds = static_cast<size_t>(MT) * 4 * CS * 16 + static_cast<size_t>(MT) * 2 * CS * 4 +
                      static_cast<size_t>(kWaves) * BS * 20;
-  const int grid = (a.N + kWaves - 1) / kWaves;
+  const int rows = kWaves / KSW;
+  const int grid = (a.N + rows - 1) / rows;
   if (a.y_dtype == QLIN_F32)
-    hipLaunchKernelGGL((spqr_gemv_kernel<MT, BPL, OUT_F32>), dim3(grid), dim3(kThreads), lds, stream,
+    hipLaunchKernelGGL((spqr_gemv_kernel<MT, KSW, BPL, OUT_F32>), dim3(grid), dim3(kThreads), lds, stream,
                        a.X, a.M, a.K, KS, a.codes, a.stats1, a.stats2, a.row_ptr, a.col_idx, a.vals, a.N, a.Y);
   else
-    hipLaunchKernelGGL((spqr_gemv_kernel<MT, BPL, OUT_F16>), dim3(grid), dim3(kThreads), lds, stream,
+    hipLaunchKernelGGL((spqr_gemv_kernel<MT, KSW, BPL, OUT_F16>), dim3(grid), dim3(kThreads), lds, stream,
                        a.X, a.M, a.K, KS, a.codes, a.stats1, a.stats2, a.row_ptr, a.col_idx, a.vals, a.N, a.Y);
 }
 
@@ -306,19 +377,20 @@ template <int MT>
 void launch_m(const SpqrArgs& a, hipStream_t stream) {
   // K slice (multiple of 256): staged activations (2.25 bytes per value and batch
   // row) plus the waves' statistics (20 bytes per 256 values and wave) within
-  // the LDS budget; at most 16 chunk loads per lane (32768 values) and at most
-  // 128 statistic blocks per slice (two per lane)
+  // the LDS budget, at most 32768 values (so a wave's part of a slice has at
+  // most 128 statistic blocks, two per lane, for any split below)
   const double per_k = 2.25 * MT + 20.0 * kWaves / 256.0;
   int KS = static_cast<int>(static_cast<double>(kLdsBudget) / per_k);
   if (KS > 32768) KS = 32768;
   KS = KS / 256 * 256;
   if (KS < 256) KS = 256;
   if (KS > a.K) KS = a.K;
-  const int blocks = (KS / 32 + 63) / 64;
-  if (blocks <= 4) launch_k<MT, 4>(a, KS, stream);
-  else if (blocks <= 8) launch_k<MT, 8>(a, KS, stream);
-  else if (blocks <= 12) launch_k<MT, 12>(a, KS, stream);
-  else launch_k<MT, 16>(a, KS, stream);
+  // split a row over KSW waves so that each wave has at most 4 chunks per lane
+  // (its unpacked codes then stay in registers)
+  const int cs = KS / 32;
+  if (cs <= 256) launch_k<MT, 1, 4>(a, KS, stream);
+  else if (cs <= 512) launch_k<MT, 2, 4>(a, KS, stream);
+  else launch_k<MT, 4, 4>(a, KS, stream);
 }
 
 // Debug: dense codes and first-level statistic codes via the forward's routines.
