@@ -72,6 +72,22 @@ def test_llama7b_gemv_full_layer(layer):
     check_close(Y, ow4.forward(X, *ow4.encode(W, 128), K, 128), f"{N}x{K}")
 
 
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_llama7b_small_batches_full_layer(layer):
+    """The Llama-7B-shaped layers at the batch sizes of the crossover sweep that
+    run the GEMV with two rows (M = 2) and the small-batch MFMA kernel (M = 8,
+    16): all output columns against the oracle."""
+    N, K = synth.WORKLOADS["w4_llama7b"]["layers"][layer]
+    W = synth.layer_weight("w4_llama7b", layer)
+    st = ow4.encode(W, 128)
+    packed = dev_pack(W, 128)
+    del W
+    for M in (2, 8, 16):
+        say(f"w4_llama7b layer {layer} {N}x{K} M={M}")
+        X = synth.x_f16(M, K, f"gpu/w4/l7b{layer}x{M}")
+        check_close(gpu_w4(X, F16, packed, N, K, 128, F16), ow4.forward(X, *st, K, 128), f"{N}x{K} M={M}")
+
+
 @pytest.mark.parametrize("K", [3 * 256, 4096 + 512])
 @pytest.mark.parametrize("G", [32, 64, 128, 256])
 @pytest.mark.parametrize("x_dtype", [F16, BF16])
