@@ -248,17 +248,18 @@ template <int TM, int NS, int OUTK>
 qlin_status gemm_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
                    void* Y, int32_t* acc_out, hipStream_t stream) {
   constexpr int BM = 32 * TM;
-  const size_t lds = static_cast<size_t>(NS) * (BM + kBN) * 8 * sizeof(uint4);
-  static int occ = 0;                          // resident workgroups per CU
-  if (occ == 0) {
+  constexpr size_t lds = static_cast<size_t>(NS) * (BM + kBN) * 8 * sizeof(uint4);
+  // resident workgroups per CU, queried once per process (thread-safe
+  // initialisation of a function-local static), after raising the dynamic LDS limit
+  static const int occ = [] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sq_gemm_sk_kernel<TM, NS, OUTK>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, sq_gemm_sk_kernel<TM, NS, OUTK>, kGemmThreads, lds) !=
             hipSuccess || o <= 0)
       o = 1;
-    occ = std::min(o, 2);
-  }
+    return std::min(o, 2);
+  }();
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + kBN - 1) / kBN;
   const long long tiles = static_cast<long long>(tiles_m) * tiles_n;

@@ -266,15 +266,16 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
 template <int TM, int NW, int R, int RV, bool XBF16, int OUTK>
 qlin_status launch_sk(const W4Args& a, hipStream_t stream) {
   constexpr int BM = 32 * TM, BN = 32 * NW;
-  const size_t lds = static_cast<size_t>(2) * BM * 16 * sizeof(uint4);
-  static int occ = 0;                          // resident workgroups per CU (register / LDS bound)
-  if (occ == 0) {
+  constexpr size_t lds = static_cast<size_t>(2) * BM * 16 * sizeof(uint4);
+  // resident workgroups per CU (register / LDS bound), queried once per
+  // process (thread-safe initialisation of a function-local static)
+  static const int occ = [] {
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, w4_gemm_sk_kernel<TM, NW, R, RV, XBF16, OUTK>, 64 * NW, lds) !=
             hipSuccess || o <= 0)
       o = 1;
-    occ = std::min(o, 2);
-  }
+    return std::min(o, 2);
+  }();
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles_n = (a.N + BN - 1) / BN;
   const long long tiles = static_cast<long long>(tiles_m) * tiles_n;
