@@ -1,0 +1,103 @@
+"""Repeatability and graph capture through the C ABI (GPU).
+
+Every forward is deterministic: the split-K GEMMs add their partial tiles in K
+order whatever the arrival order of the workgroups, and their arrival counters
+return to zero at the end of each call.  So a call repeated gives the same bits,
+and a HIP graph that captured the calls gives, at every replay, the bits of
+the eager calls (the workspace exists before capture, counters are never
+cleared inside the graph)."""
+import numpy as np
+import pytest
+
+import synth
+from quantized_linear_layers_packed_amd import qlin
+from tests.gpu_util import dev, empty, host, say, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+F16, BF16, F32 = qlin.QLIN_F16, qlin.QLIN_BF16, qlin.QLIN_F32
+
+
+def _calls():
+    """Device inputs and a list of (name, callable writing its output, output tensor)."""
+    torch = torch_cuda()
+    out = []
+    # W4: GEMV (M=1), small-batch kernel (M=8), stream-K GEMM (M=96, bf16 in)
+    W = synth.normal_f32((1536, 2048), 0.02, "gpu/graph/w4")
+    qw, sc, qz = (dev(a) for a in qlin.qlin_w4_pack(W, 128))
+    for M, xd in ((1, F16), (8, F16), (96, BF16)):
+        X = dev((synth.x_bf16_bits if xd == BF16 else synth.x_f16)(M, 2048, f"gpu/graph/x{M}"))
+        Y = empty((M, 1536), torch.float32)
+        out.append((f"w4 M={M}", lambda X=X, Y=Y, M=M, xd=xd: qlin.qlin_w4_forward(X, xd, M, 2048, qw, sc, qz, 1536,
+                                                                                  128, Y, F32), Y))
+    # SpQR M=1 and 4
+    Ws = synth.student_t3_f32((512, 2048), 0.02, "gpu/graph/spqr")
+    st = qlin.spqr_pack(Ws, 0.01)
+    d = {k: dev(np.ascontiguousarray(v)) for k, v in st.items()}
+    nnz = len(st["val"])
+    for M in (1, 4):
+        X = dev(synth.x_f16(M, 2048, f"gpu/graph/sx{M}"))
+        Y = empty((M, 512), torch.float32)
+        out.append((f"spqr M={M}", lambda X=X, Y=Y, M=M: qlin.spqr_forward(
+            X, M, 2048, d["codes"], d["stats1"], d["stats2"], d["row_ptr"], d["col_idx"], d["val"], nnz, 512, Y, F32),
+            Y))
+    # W8A8: activation kernel + int8 GEMM (stream-K), M=200
+    Wf = synth.normal_f32((1024, 2048), 0.02, "gpu/graph/sq")
+    Xc = synth.x_f16(200, 2048, "gpu/graph/sqx")
+    s, inv = qlin.sq_compute_smoothing(qlin.sq_act_absmax(Xc), Wf, 0.85)
+    Wq, ws = qlin.sq_pack_weight(Wf, s)
+    Wq, ws, inv, X = dev(Wq), dev(ws), dev(inv), dev(Xc)
+    Xq = empty((200, 2048), torch.int8)
+    xs = empty((200,), torch.float32)
+    Y = empty((200, 1024), torch.float32)
+    acc = empty((200, 1024), torch.int32)
+
+    def sq():
+        qlin.sq_smooth_quant_act(X, inv, 200, 2048, Xq, xs)
+        qlin.sq_int8_gemm(Xq, xs, Wq, ws, 200, 1024, 2048, Y, F32, acc)
+    out.append(("w8a8 M=200", sq, Y))
+    out.append(("w8a8 acc", lambda: None, acc))
+    return out, (qw, sc, qz, d, Wq)
+
+
+def test_repeated_calls_give_identical_bits():
+    calls, _keep = _calls()
+    first = []
+    for name, f, y in calls:
+        f()
+        first.append(host(y).copy())
+    for rep in range(3):
+        for (name, f, y), ref in zip(calls, first):
+            f()
+            assert np.array_equal(host(y), ref), f"{name}: repetition {rep} differs"
+    say("  repeated calls: bit-identical")
+
+
+def test_graph_replays_match_eager_calls():
+    torch = torch_cuda()
+    calls, _keep = _calls()
+    eager = []
+    for name, f, y in calls:
+        f()
+        eager.append(host(y).copy())
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for name, f, y in calls:
+                f()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for name, f, y in calls:
+            y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (name, f, y), ref in zip(calls, eager):
+            assert np.array_equal(host(y), ref), f"{name}: replay {rep} differs from the eager call"
+        # eager work between replays (the same calls, outside the graph)
+        for name, f, y in calls:
+            f()
+        torch.cuda.synchronize()
+    say("  graph replays: bit-identical to eager calls")
