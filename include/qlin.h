@@ -255,7 +255,9 @@ qlin_status qlin_hessian(const float* X, int n, int K, double* H);
  * and every later column k moves by -e U[j][k].  H proportional to I reproduces
  * qlin_w4_pack bit for bit.  EINVAL for bad sizes (as qlin_w4_sizes), NULL
  * pointers, damp < 0, a non-symmetric or non-finite H, or H + lam I not
- * positive definite.  Host memory: about 3 K^2 doubles; time O(K^3 + N K^2). */
+ * positive definite.  Host memory: about 3 K^2 doubles; time O(K^3 + N K^2)
+ * (a 4096 x 4096 layer takes seconds on a few host threads; K in the tens of
+ * thousands needs tens of GB and hours). */
 qlin_status qlin_w4_pack_gptq(const float* W, int N, int K, int G, const double* H, double damp,
                               uint32_t* qweight, uint16_t* scales, uint32_t* qzeros);
 

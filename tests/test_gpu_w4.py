@@ -176,7 +176,8 @@ def test_llama70b_gemm_full_layer_sampled_rows(layer):
 
 
 def test_small_batch_beyond_the_gemv_range_uses_the_gemm():
-    """M <= 16 with K above the GEMV's single-pass range runs the MFMA GEMM."""
+    """M <= 16 with K above the GEMV's single-pass range runs the small-batch
+    MFMA kernel (K split over the waves of a workgroup), M = 1 included."""
     N, K = 64, 20480
     W = synth.normal_f32((N, K), 0.02, "gpu/w4/longk")
     packed = dev_pack(W, 128)
