@@ -57,6 +57,18 @@ def _calls():
         qlin.sq_int8_gemm(Xq, xs, Wq, ws, 200, 1024, 2048, Y, F32, acc)
     out.append(("w8a8 M=200", sq, Y))
     out.append(("w8a8 acc", lambda: None, acc))
+    # W8A8 at M=600: the large-batch kernel (256 x 128 tiles, stream-K over 24 tiles)
+    X6 = dev(synth.x_f16(600, 2048, "gpu/graph/sqx600"))
+    Xq6 = empty((600, 2048), torch.int8)
+    xs6 = empty((600,), torch.float32)
+    Y6 = empty((600, 1024), torch.float16)
+    acc6 = empty((600, 1024), torch.int32)
+
+    def sq600():
+        qlin.sq_smooth_quant_act(X6, inv, 600, 2048, Xq6, xs6)
+        qlin.sq_int8_gemm(Xq6, xs6, Wq, ws, 600, 1024, 2048, Y6, F16, acc6)
+    out.append(("w8a8 M=600", sq600, Y6))
+    out.append(("w8a8 M=600 acc", lambda: None, acc6))
     return out, (qw, sc, qz, d, Wq)
 
 

@@ -66,9 +66,17 @@ def test_full_layer_end_to_end(layer):
         check_close(Y[:, cols], Y_o, f"{N}x{K} M={M}")
 
 
+# The last five shapes reach the large-batch kernels: 256 x 128 tiles from M = 512
+# (ragged M and N, a single K step, 8 waves), 128 x 128 tiles for 64 < M < 512 with at
+# least 128 tiles (M = 65 and 300 with ragged N), and the K % 128 = 64 fallback at
+# M = 513 to the 32 TM x 128 kernel.
+RAGGED = ((1, 100, 64), (3, 129, 192), (33, 64, 128), (100, 257, 4096), (300, 40, 320),
+          (520, 1000, 1024), (1100, 130, 128), (65, 16400, 256), (300, 6000, 512), (513, 300, 4160))
+
+
 def test_gemm_ragged_shapes():
     r = np.random.default_rng(11)
-    for (M, N, K) in ((1, 100, 64), (3, 129, 192), (33, 64, 128), (100, 257, 4096), (300, 40, 320)):
+    for (M, N, K) in RAGGED:
         say(f"sq gemm M={M} N={N} K={K}")
         Xq = r.integers(-127, 128, size=(M, K)).astype(np.int8)
         Wq = r.integers(-127, 128, size=(N, K)).astype(np.int8)
