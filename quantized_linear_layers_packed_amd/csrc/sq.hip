@@ -16,9 +16,9 @@
 // (|acc| <= K * 127^2 < 2^31 for K <= 131072).  The token tile of Xq and the
 // weight rows stream from HBM straight into a multi-stage LDS ring several K
 // steps ahead.  Epilogue: float(acc) * x_scale[m] * w_scale[n], rounded once.
-// Small batches use tiles of 32 TM x 128 (one wave per 32 columns); large
-// batches use 64 x 64 wave tiles in a grid of four or eight waves, whose
-// operands are re-read from L2 half as often per multiply-add.
+// Small batches use tiles of 32 TM x 128 (one wave per 32 columns); larger
+// batches a 4 x 2 grid of waves with tiles of up to 256 x 128, whose operands
+// are re-read from L2 half as often per multiply-add.
 
 #include <algorithm>
 
@@ -509,15 +509,20 @@ void sq_act_launch(const uint16_t* X, const float* inv_s, int M, int K, int8_t* 
 
 qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
                            int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
-  // Large batches (K a multiple of 128): 64 x 64 wave tiles, two waves per SIMD.
-  // From 512 tokens, 256 x 128 tiles (eight waves); below that, 128 x 128 tiles
-  // (four waves) once there are enough of them to spread over the chip, which
-  // leaves fewer K splits to fix up.  Otherwise the 32 TM x 128 kernel, whose
-  // ring depth stays within 160 KB of LDS: stage = (32 TM + 128) rows x 128 bytes.
+  // Larger batches (K a multiple of 128): eight waves in a 4 x 2 grid, two per
+  // SIMD, and the largest tile of 256 x 128 (64 x 64 per wave), 128 x 128
+  // (32 x 64) or 128 x 64 (32 x 32) that still gives at least 160 tiles (the
+  // smallest one otherwise): bigger tiles re-read fewer operand bytes per
+  // multiply-add, enough tiles keep the K splits to fix up few.  Batches of at
+  // most 64 use the 32 TM x 128 kernel, whose ring depth stays within 160 KB of
+  // LDS: stage = (32 TM + 128) rows x 128 bytes.
   if (M > 64 && K % 128 == 0) {
-    if (M >= 512) return gemm_big_o<4, 2, 2, 2, 128, 3>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-    const long long tiles = static_cast<long long>((M + 127) / 128) * ((N + 127) / 128);
-    if (tiles >= 128) return gemm_big_o<2, 2, 2, 2, 128, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+    auto tiles = [&](int bm, int bn) { return static_cast<long long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (tiles(256, 128) >= 160)
+      return gemm_big_o<4, 2, 2, 2, 128, 3>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+    if (tiles(128, 128) >= 160)
+      return gemm_big_o<4, 2, 1, 2, 128, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+    return gemm_big_o<4, 2, 1, 1, 128, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
   }
   if (M <= 32) return gemm_o<1, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
   if (M <= 64) return gemm_o<2, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
