@@ -8,12 +8,14 @@
 // before it fills 256 compute units; splitting K across workgroups then needs
 // a global hand-off of partial sums whose latency dominates a layer of a few
 // microseconds.  Here the K split stays inside one workgroup:
-//   * a workgroup owns 16 output columns; its NWV (4) waves each take a
-//     contiguous run of 128-wide K blocks of those columns and accumulate a
-//     16 x 16 tile (two for TM = 2) with v_mfma_f32_16x16x32_f16; the partial
-//     tiles are added in wave order through LDS at the end (deterministic, no
-//     atomics, no workspace); four-wave workgroups keep every workgroup of an
-//     11008-column layer resident at once;
+//   * a workgroup owns CT tiles of 16 output columns (CT = 4 or 2 on wide
+//     layers while that leaves at least 160 workgroups, else 1); its NWV (4)
+//     waves each take a contiguous run of 128-wide K blocks of those columns
+//     and accumulate a 16 x 16 tile per column tile (two for TM = 2) with
+//     v_mfma_f32_16x16x32_f16, one activation fragment feeding the CT tiles;
+//     the partial tiles are added in wave order through LDS at the end
+//     (deterministic, no atomics, no workspace); four-wave workgroups keep
+//     every workgroup of an 11008-column layer resident at once;
 //   * B operand: per K block a lane loads one 16-byte piece (4 packed words of
 //     its column) and turns each word into 8 fp16 weights s * (q - z) (q - z
 //     exact, one rounding of the product), one word per matrix instruction;
@@ -37,7 +39,7 @@ namespace qlin {
 
 namespace {
 
-constexpr int kCols = 16;           // output columns per workgroup
+constexpr int kCols = 16;           // output columns per column tile
 
 // Eight fp16 weights s * (q - z) in natural k order from one packed word.
 __device__ __forceinline__ h8_t dequant_word(uint32_t w, h2_t zz, h2_t ss) {
@@ -61,42 +63,52 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
   return bitcast<uint32_t>(__builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
-template <int NWV, int TM, int D, bool XBF16, int OUTK>
+template <int NWV, int TM, int D, int CT, bool XBF16, int OUTK>
 __global__ __launch_bounds__(64 * NWV) void w4_skinny_kernel(const uint16_t* X, int M, int K,
                                                                const uint32_t* qweight, const uint16_t* scales,
                                                                const uint32_t* qzeros, int N, int gsh, void* Y) {
-  __shared__ f32x4_t red[NWV][TM][64];
+  __shared__ f32x4_t red[NWV][CT * TM][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loop control
   const int col = lane & 15, h = lane >> 4;
-  const int n0 = blockIdx.x * kCols;
-  const int n = n0 + col;
-  const size_t nn = static_cast<size_t>(min(n, N - 1));
+  const int n0 = blockIdx.x * (CT * kCols);
   const int nb = K >> 7;                        // 128-wide K blocks
   const int ng = K >> (7 + gsh);
   const int nzw = (ng + 7) >> 3;
   const int b0 = (wv * nb) / NWV, b1 = ((wv + 1) * nb) / NWV;
-  const uint4* qrow = reinterpret_cast<const uint4*>(qweight + nn * (K >> 3));
-  const uint16_t* srow = scales + nn * ng;
-  const uint32_t* zrow = qzeros + nn * nzw;
-
-  f32x4_t acc[TM];
+  const uint4* qrow[CT];                        // column tile c: column n0 + 16 c + col
+  const uint16_t* srow[CT];
+  const uint32_t* zrow[CT];
 #pragma unroll
-  for (int t = 0; t < TM; ++t) acc[t] = f32x4_t{};
+  for (int c = 0; c < CT; ++c) {
+    const size_t nn = static_cast<size_t>(min(n0 + kCols * c + col, N - 1));
+    qrow[c] = reinterpret_cast<const uint4*>(qweight + nn * (K >> 3));
+    srow[c] = scales + nn * ng;
+    zrow[c] = qzeros + nn * nzw;
+  }
+
+  f32x4_t acc[CT][TM];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[c][t] = f32x4_t{};
 
   if (b0 < b1) {
     const int blast = b1 - 1;
-    uint4 wq[D];
+    uint4 wq[D][CT];
     uint4 av[D][TM][4];
-    uint32_t sv[D], zv[D];
-    // block b: the lane's 4 words 4h .. 4h+3 of its column; scale and zero
-    // word of the block's group; activations of chunks 4h + i, rows
-    // col (+ 16 t) of the batch, clamped to M - 1
-    auto load = [&](int b, uint4& w, uint4 (&a)[TM][4], uint32_t& s, uint32_t& z) {
-      w = qrow[4 * b + h];
+    uint32_t sv[D][CT], zv[D][CT];
+    // block b: the lane's 4 words 4h .. 4h+3 of its column in each column tile;
+    // scale and zero word of the block's group; activations of chunks 4h + i,
+    // rows col (+ 16 t) of the batch, clamped to M - 1 (shared by the tiles)
+    auto load = [&](int b, uint4 (&w)[CT], uint4 (&a)[TM][4], uint32_t (&s)[CT], uint32_t (&z)[CT]) {
       const int g = b >> gsh;
-      s = srow[g];
-      z = zrow[g >> 3];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        w[c] = qrow[c][4 * b + h];
+        s[c] = srow[c][g];
+        z[c] = zrow[c][g >> 3];
+      }
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
         const int m = min(16 * t + col, M - 1);
@@ -105,17 +117,21 @@ __global__ __launch_bounds__(64 * NWV) void w4_skinny_kernel(const uint16_t* X, 
         for (int i = 0; i < 4; ++i) a[t][i] = xr[4 * h + i];
       }
     };
-    auto compute = [&](int b, const uint4& w, const uint4 (&a)[TM][4], uint32_t s, uint32_t zw) {
+    auto compute = [&](int b, const uint4 (&w)[CT], const uint4 (&a)[TM][4], const uint32_t (&s)[CT],
+                       const uint32_t (&zw)[CT]) {
       const int g = b >> gsh;
-      const uint32_t z = (zw >> (4 * (g & 7))) & 15u;
-      const _Float16 zb = static_cast<_Float16>(1024.0f + static_cast<float>(z));
-      const h2_t zz = {zb, zb};
-      const _Float16 sh = bitcast<_Float16>(static_cast<uint16_t>(s));
-      const h2_t ss = {sh, sh};
+      h2_t zz[CT], ss[CT];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const uint32_t z = (zw[c] >> (4 * (g & 7))) & 15u;
+        const _Float16 zb = static_cast<_Float16>(1024.0f + static_cast<float>(z));
+        zz[c] = h2_t{zb, zb};
+        const _Float16 sh = bitcast<_Float16>(static_cast<uint16_t>(s[c]));
+        ss[c] = h2_t{sh, sh};
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t word = i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
-        const h8_t bw = dequant_word(word, zz, ss);
+        h8_t at[TM];
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
           uint4 av4 = a[t][i];
@@ -125,7 +141,14 @@ __global__ __launch_bounds__(64 * NWV) void w4_skinny_kernel(const uint16_t* X, 
             av4.z = bf16x2_to_f16x2(av4.z);
             av4.w = bf16x2_to_f16x2(av4.w);
           }
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<h8_t>(av4), bw, acc[t], 0, 0, 0);
+          at[t] = bitcast<h8_t>(av4);
+        }
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          const uint32_t word = i == 0 ? w[c].x : i == 1 ? w[c].y : i == 2 ? w[c].z : w[c].w;
+          const h8_t bw = dequant_word(word, zz[c], ss[c]);
+#pragma unroll
+          for (int t = 0; t < TM; ++t) acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(at[t], bw, acc[c][t], 0, 0, 0);
         }
       }
     };
@@ -145,16 +168,19 @@ __global__ __launch_bounds__(64 * NWV) void w4_skinny_kernel(const uint16_t* X, 
     }
   }
 
-  // fixed-order sum of the 8 waves' tiles; lane l of the tile holds column
-  // l % 16, rows 4 (l / 16) + r
+  // fixed-order sum of the waves' tiles; lane l of a tile holds column
+  // l % 16, rows 4 (l / 16) + r; wave c TM + t sums tile (c, t)
 #pragma unroll
-  for (int t = 0; t < TM; ++t) red[wv][t][lane] = acc[t];
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) red[wv][c * TM + t][lane] = acc[c][t];
   __syncthreads();
-  if (wv < TM) {
-    const int t = wv;
-    f32x4_t tot = red[0][t][lane];
+  if (wv < CT * TM) {
+    const int t = wv % TM;
+    const int n = n0 + kCols * (wv / TM) + col;
+    f32x4_t tot = red[0][wv][lane];
 #pragma unroll
-    for (int w = 1; w < NWV; ++w) tot += red[w][t][lane];
+    for (int w = 1; w < NWV; ++w) tot += red[w][wv][lane];
     if (n < N) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -165,31 +191,41 @@ __global__ __launch_bounds__(64 * NWV) void w4_skinny_kernel(const uint16_t* X, 
   }
 }
 
-template <int NWV, int TM, int D, bool XBF16, int OUTK>
+template <int NWV, int TM, int D, int CT, bool XBF16, int OUTK>
 void launch_k(const W4Args& a, hipStream_t stream) {
+  static_assert(CT * TM <= NWV, "one summing wave per output tile");
   const int gsh = a.G == 256 ? 1 : 0;
-  hipLaunchKernelGGL((w4_skinny_kernel<NWV, TM, D, XBF16, OUTK>), dim3((a.N + kCols - 1) / kCols), dim3(64 * NWV), 0,
-                     stream, static_cast<const uint16_t*>(a.X), a.M, a.K, a.qweight, a.scales, a.qzeros, a.N, gsh,
-                     a.Y);
+  hipLaunchKernelGGL((w4_skinny_kernel<NWV, TM, D, CT, XBF16, OUTK>), dim3((a.N + CT * kCols - 1) / (CT * kCols)),
+                     dim3(64 * NWV), 0, stream, static_cast<const uint16_t*>(a.X), a.M, a.K, a.qweight, a.scales,
+                     a.qzeros, a.N, gsh, a.Y);
 }
 
-template <int NWV, int TM, int D, bool XBF16>
+template <int NWV, int TM, int D, int CT, bool XBF16>
 void launch_o(const W4Args& a, hipStream_t stream) {
-  if (a.y_dtype == QLIN_F16) launch_k<NWV, TM, D, XBF16, OUT_F16>(a, stream);
-  else if (a.y_dtype == QLIN_BF16) launch_k<NWV, TM, D, XBF16, OUT_BF16>(a, stream);
-  else launch_k<NWV, TM, D, XBF16, OUT_F32>(a, stream);
+  if (a.y_dtype == QLIN_F16) launch_k<NWV, TM, D, CT, XBF16, OUT_F16>(a, stream);
+  else if (a.y_dtype == QLIN_BF16) launch_k<NWV, TM, D, CT, XBF16, OUT_BF16>(a, stream);
+  else launch_k<NWV, TM, D, CT, XBF16, OUT_F32>(a, stream);
 }
 
-template <int NWV, int TM, int D>
+template <int NWV, int TM, int D, int CT = 1>
 void launch_x(const W4Args& a, hipStream_t stream) {
-  if (a.x_dtype == QLIN_BF16) launch_o<NWV, TM, D, true>(a, stream);
-  else launch_o<NWV, TM, D, false>(a, stream);
+  if (a.x_dtype == QLIN_BF16) launch_o<NWV, TM, D, CT, true>(a, stream);
+  else launch_o<NWV, TM, D, CT, false>(a, stream);
 }
 
 }  // namespace
 
 bool w4_skinny_supported(int M, int K, int G) { return M >= 1 && M <= 16 && (G == 128 || G == 256) && K % 128 == 0; }
 
-void w4_skinny_launch(const W4Args& a, hipStream_t stream) { launch_x<4, 1, 4>(a, stream); }
+// Wide layers: 4 or 2 column tiles per workgroup (each activation fragment then
+// feeds 4 or 2 matrix instructions, so the activations are re-read from cache 4
+// or 2 times less) as long as that leaves at least 160 workgroups; one tile
+// otherwise (a 4096-column layer keeps its 256 workgroups).
+void w4_skinny_launch(const W4Args& a, hipStream_t stream) {
+  const long long wg4 = (a.N + 4 * kCols - 1) / (4 * kCols), wg2 = (a.N + 2 * kCols - 1) / (2 * kCols);
+  if (wg4 >= 160) launch_x<4, 1, 3, 4>(a, stream);
+  else if (wg2 >= 160) launch_x<4, 1, 2, 2>(a, stream);
+  else launch_x<4, 1, 4, 1>(a, stream);
+}
 
 }  // namespace qlin

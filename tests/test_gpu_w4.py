@@ -189,6 +189,25 @@ def test_small_batch_beyond_the_gemv_range_uses_the_gemm():
 
 
 @pytest.mark.parametrize("x_dtype", [F16, BF16])
+def test_small_batches_on_wide_layers(x_dtype):
+    """Batches of 4..16 rows on layers wide enough for the small-batch kernel to
+    give a workgroup 2 tiles of 16 columns (N = 5200: 163 workgroups) or 4
+    (N = 10300: 161 workgroups), both with a ragged last tile."""
+    for (N, K, G) in ((5200, 1024, 128), (10300, 512, 256)):
+        W = synth.normal_f32((N, K), 0.02, f"gpu/w4/wide{N}")
+        packed = dev_pack(W, G)
+        st = ow4.encode(W, G)
+        for M in (4, 9, 16):
+            say(f"w4 small-batch wide N={N} K={K} G={G} M={M} x={x_dtype}")
+            X = (synth.x_bf16_bits if x_dtype == BF16 else synth.x_f16)(M, K, f"gpu/w4/widex{M}")
+            ref = ow4.forward(X, *st, K, G)
+            y32 = gpu_w4(X, x_dtype, packed, N, K, G, F32)
+            check_close(y32, ref, f"M={M} f32 out")
+            yb = gpu_w4(X, x_dtype, packed, N, K, G, BF16)
+            assert np.array_equal(yb, f32_to_bf16_bits(y32)), "bf16 store is not RNE of the fp32 result"
+
+
+@pytest.mark.parametrize("x_dtype", [F16, BF16])
 def test_small_batches_through_the_mfma_kernels(x_dtype):
     """Batches of 2..24 rows on layers whose activations exceed the GEMV's LDS
     staging: 4..16 rows run the small-batch kernel (K split over the waves of a
