@@ -509,13 +509,16 @@ void sq_act_launch(const uint16_t* X, const float* inv_s, int M, int K, int8_t* 
 
 qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
                            int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
-  // Larger batches (K a multiple of 128): eight waves in a 4 x 2 grid, two per
-  // SIMD, and the largest tile of 256 x 128 (64 x 64 per wave), 128 x 128
-  // (32 x 64) or 128 x 64 (32 x 32) that still gives at least 160 tiles (the
-  // smallest one otherwise): bigger tiles re-read fewer operand bytes per
-  // multiply-add, enough tiles keep the K splits to fix up few.  Batches of at
-  // most 64 use the 32 TM x 128 kernel, whose ring depth stays within 160 KB of
-  // LDS: stage = (32 TM + 128) rows x 128 bytes.
+  // Larger batches (K a multiple of 128): eight waves, two per SIMD.  Above 64
+  // tokens a 4 x 2 wave grid and the largest tile of 256 x 128 (64 x 64 per
+  // wave), 128 x 128 (32 x 64) or 128 x 64 (32 x 32) that still gives at least
+  // 160 tiles (the smallest one otherwise): bigger tiles re-read fewer operand
+  // bytes per multiply-add, enough tiles keep the K splits to fix up few; 33 to
+  // 64 tokens a 2 x 4 grid of 32 x 32 wave tiles (64 x 128).  Batches of at most
+  // 32 use the 32 TM x 128 kernel, whose ring depth stays within 160 KB of LDS:
+  // stage = (32 TM + 128) rows x 128 bytes.
+  if (M > 32 && M <= 64 && K % 128 == 0)
+    return gemm_big_o<2, 4, 1, 1, 128, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
   if (M > 64 && K % 128 == 0) {
     auto tiles = [&](int bm, int bn) { return static_cast<long long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 128) >= 160)
