@@ -69,11 +69,12 @@ def test_full_layer_end_to_end(layer):
 # (33, 64, 128) and (60, 3000, 512) reach the wave-grid kernel's 64 x 128 tiles (33..64
 # tokens, K a multiple of 128); from (520, 1000, 1024) on, its tile sizes for more than 64
 # tokens: 128 x 64 (ragged M and N, a single K step at K = 128, M = 65), 128 x 128
-# (200 x 11000: 172 tiles) and 256 x 128 (600 x 8192: 192 tiles); the last shape
-# (K % 128 = 64) and (300, 40, 320) fall back to the 32 TM x 128 kernel.
+# (200 x 11000: 172 tiles) and 256 x 128 (600 x 8192: 192 tiles), and 8 output columns
+# (every weight row past N clamped); the last shape (K % 128 = 64) and (300, 40, 320)
+# fall back to the 32 TM x 128 kernel.
 RAGGED = ((1, 100, 64), (3, 129, 192), (33, 64, 128), (60, 3000, 512), (100, 257, 4096), (300, 40, 320),
           (520, 1000, 1024), (1100, 130, 128), (65, 16400, 256), (300, 6000, 512),
-          (200, 11000, 384), (600, 8192, 256), (513, 300, 4160))
+          (200, 11000, 384), (600, 8192, 256), (520, 8, 256), (513, 300, 4160))
 
 
 def test_gemm_ragged_shapes():
