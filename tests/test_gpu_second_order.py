@@ -76,9 +76,9 @@ def test_sensitivity_spqr_encode_through_the_fused_kernel():
 def test_act_order_forward_through_the_gather(G):
     """Act-order storage without static groups runs through qlin_w4_forward_perm
     (gather of X by perm, then the regular kernels): parity with the oracle's
-    X[:, perm] . W_stored^T at GEMV and GEMM batch sizes; with static groups the
-    storage is natural and runs through qlin_w4_forward; an identity perm gives
-    qlin_w4_forward's result bit for bit."""
+    X[:, perm] . W_stored^T at GEMV (M = 1, 3) and MFMA batch sizes; with static
+    groups the storage is natural and runs through qlin_w4_forward; an identity
+    perm gives qlin_w4_forward's result bit for bit."""
     from oracle import gptq as ogptq
     torch = torch_cuda()
     N, K = 640, 2048
@@ -90,7 +90,7 @@ def test_act_order_forward_through_the_gather(G):
     sta = qlin.qlin_w4_pack_gptq_actorder(W, G, H, static_groups=True)
     qw, sc, qz, perm = (dev(a) for a in dyn)
     ident = dev(np.arange(K, dtype=np.int32))
-    for M in (1, 8, 64):
+    for M in (1, 3, 8, 64):
         say(f"act-order W4 N={N} K={K} G={G} M={M}")
         X = Xc[:M]
         Xd = dev(X)
