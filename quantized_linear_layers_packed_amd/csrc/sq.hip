@@ -33,6 +33,7 @@ namespace qlin {
 namespace {
 
 constexpr int kActThreads = 256;
+constexpr int kActKeep = 4;           // groups of 8 values per thread kept in registers between the passes
 
 __global__ __launch_bounds__(kActThreads) void sq_act_kernel(const uint16_t* __restrict__ X,
                                                              const float* __restrict__ inv_s, int K,
@@ -41,18 +42,34 @@ __global__ __launch_bounds__(kActThreads) void sq_act_kernel(const uint16_t* __r
   const int m = blockIdx.x;
   const uint4* xr = reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K);
   const int nv = K >> 3;                      // groups of 8 values
-  float amax = 0.0f;
-  for (int i = threadIdx.x; i < nv; i += kActThreads) {
+  // x~ = x * inv_s for group i; the first kActKeep groups of each thread stay
+  // in registers for the quantize pass (rows up to 8 * 4 * 256 = 8192 values
+  // are read once), later groups are read again
+  auto scaled = [&](int i, float (&t)[8]) {
     const uint4 v = xr[i];
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
     const float4 s0 = reinterpret_cast<const float4*>(inv_s)[2 * i];
     const float4 s1 = reinterpret_cast<const float4*>(inv_s)[2 * i + 1];
     const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float x = f16_bits_to_f32(static_cast<uint16_t>(u[j >> 1] >> (16 * (j & 1))));
-      amax = fmaxf(amax, fabsf(x * sv[j]));
+    for (int j = 0; j < 8; ++j) t[j] = f16_bits_to_f32(static_cast<uint16_t>(u[j >> 1] >> (16 * (j & 1)))) * sv[j];
+  };
+  float keep[kActKeep][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kActKeep; ++c) {
+    const int i = threadIdx.x + c * kActThreads;
+    if (i < nv) {
+      scaled(i, keep[c]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(keep[c][j]));
     }
+  }
+  for (int i = threadIdx.x + kActKeep * kActThreads; i < nv; i += kActThreads) {
+    float t[8];
+    scaled(i, t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(t[j]));
   }
   amax = wave_max(amax);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
@@ -64,22 +81,25 @@ __global__ __launch_bounds__(kActThreads) void sq_act_kernel(const uint16_t* __r
   if (threadIdx.x == 0) x_scale[m] = (a == 0.0f) ? 0.0f : __fdiv_rn(a, 127.0f);
 
   uint2* qr = reinterpret_cast<uint2*>(Xq + static_cast<size_t>(m) * K);
-  for (int i = threadIdx.x; i < nv; i += kActThreads) {
-    const uint4 v = xr[i];
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-    const float4 s0 = reinterpret_cast<const float4*>(inv_s)[2 * i];
-    const float4 s1 = reinterpret_cast<const float4*>(inv_s)[2 * i + 1];
-    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  auto quantize = [&](int i, const float (&t)[8]) {
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float x = f16_bits_to_f32(static_cast<uint16_t>(u[j >> 1] >> (16 * (j & 1))));
-      const float t = __fmul_rn(x * sv[j], r);
-      const float q = fminf(fmaxf(rintf(t), -127.0f), 127.0f);
+      const float q = fminf(fmaxf(rintf(__fmul_rn(t[j], r)), -127.0f), 127.0f);
       const uint32_t b = static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xFFu;
       packed[j >> 2] |= b << (8 * (j & 3));
     }
     qr[i] = make_uint2(packed[0], packed[1]);
+  };
+#pragma unroll
+  for (int c = 0; c < kActKeep; ++c) {
+    const int i = threadIdx.x + c * kActThreads;
+    if (i < nv) quantize(i, keep[c]);
+  }
+  for (int i = threadIdx.x + kActKeep * kActThreads; i < nv; i += kActThreads) {
+    float t[8];
+    scaled(i, t);
+    quantize(i, t);
   }
 }
 

@@ -42,6 +42,18 @@ def test_activation_quantization_is_bit_exact():
         Xq_o, xs_o = osq.quantize_act(X[:M], inv_s)
         assert np.array_equal(host(Xq_d), Xq_o)
         assert host(xs_d).tobytes() == xs_o.tobytes()
+    # rows longer than the values a thread keeps in registers (8192) are partly
+    # read again in the quantize pass; rows shorter than one group per thread
+    r = np.random.default_rng(5)
+    for (M, K) in ((5, 11008), (3, 40), (2, 20000)):
+        say(f"sq act M={M} K={K}")
+        Xk = (r.standard_normal((M, K)) * 2).astype(np.float16)
+        Xk[0, K // 3] = 300.0                          # an outlier channel value
+        inv_k = r.uniform(0.2, 5.0, K).astype(np.float32)
+        Xq_d, xs_d = gpu_act(Xk, inv_k)
+        Xq_o, xs_o = osq.quantize_act(Xk, inv_k)
+        assert np.array_equal(host(Xq_d), Xq_o)
+        assert host(xs_d).tobytes() == xs_o.tobytes()
 
 
 @pytest.mark.parametrize("layer", [0, 1])
