@@ -16,9 +16,10 @@
 // (|acc| <= K * 127^2 < 2^31 for K <= 131072).  The token tile of Xq and the
 // weight rows stream from HBM straight into a multi-stage LDS ring several K
 // steps ahead.  Epilogue: float(acc) * x_scale[m] * w_scale[n], rounded once.
-// Small batches use tiles of 32 TM x 128 (one wave per 32 columns); larger
-// batches a 4 x 2 grid of waves with tiles of up to 256 x 128, whose operands
-// are re-read from L2 half as often per multiply-add.
+// Up to 4 tokens a GEMV with v_dot4; small batches use tiles of 32 TM x 128
+// (one wave per 32 columns); larger batches a grid of eight waves with tiles
+// of up to 256 x 128, whose operands are re-read from L2 half as often per
+// multiply-add.
 
 #include <algorithm>
 
@@ -101,6 +102,108 @@ __global__ __launch_bounds__(kActThreads) void sq_act_kernel(const uint16_t* __r
     scaled(i, t);
     quantize(i, t);
   }
+}
+
+// GEMV for batches of at most 4 tokens, where the product is bound by the
+// weight stream: each output row is served by KS waves (KS contiguous blocks
+// of 64 lanes x 16 bytes interleaved, so every load instruction covers 1 KB of
+// the row); all of a lane's weight chunks are loaded first, then the matching
+// 16-byte activation chunks (shared by every row of the workgroup, so they come
+// from cache) feed v_dot4 (exact int32); lane sums, then the KS waves' sums in a
+// fixed order, then the same epilogue as the GEMM.
+constexpr int kGemvWaves = 8;
+
+template <int MT, int KS, int BPL, int OUTK>
+__global__ __launch_bounds__(64 * kGemvWaves) void sq_gemv_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ x_scale, const int8_t* __restrict__ Wq,
+    const float* __restrict__ w_scale, int M, int N, int K, void* __restrict__ Y, int32_t* __restrict__ acc_out) {
+  __shared__ int red[kGemvWaves][MT];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int part = wv % KS;
+  const int n = blockIdx.x * (kGemvWaves / KS) + wv / KS;
+  const int C = K >> 4;                                           // 16-byte chunks per row
+  const uint4* wrow = reinterpret_cast<const uint4*>(Wq + static_cast<size_t>(min(n, N - 1)) * K);
+  uint4 w[BPL];
+#pragma unroll
+  for (int b = 0; b < BPL; ++b) {
+    const int c = 64 * (KS * b + part) + lane;
+    w[b] = make_uint4(0u, 0u, 0u, 0u);
+    if (c < C) w[b] = load_stream16(wrow + c);
+  }
+  int acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = 0;
+#pragma unroll
+  for (int b = 0; b < BPL; ++b) {
+    const int c = 64 * (KS * b + part) + lane;
+    if (c < C) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < M) {
+          const uint4 x = reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(m) * K)[c];
+          acc[m] = __builtin_amdgcn_sdot4(static_cast<int>(w[b].x), static_cast<int>(x.x), acc[m], false);
+          acc[m] = __builtin_amdgcn_sdot4(static_cast<int>(w[b].y), static_cast<int>(x.y), acc[m], false);
+          acc[m] = __builtin_amdgcn_sdot4(static_cast<int>(w[b].z), static_cast<int>(x.z), acc[m], false);
+          acc[m] = __builtin_amdgcn_sdot4(static_cast<int>(w[b].w), static_cast<int>(x.w), acc[m], false);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc[m] += __shfl_xor(acc[m], off);
+  }
+  if constexpr (KS > 1) {
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) red[wv][m] = acc[m];
+    }
+    __syncthreads();
+  }
+  if (part == 0 && lane == 0 && n < N) {
+    const float wsc = w_scale[n];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < M) {
+        int a = acc[m];
+        if constexpr (KS > 1) {
+          a = red[wv][m];
+#pragma unroll
+          for (int q = 1; q < KS; ++q) a += red[wv + q][m];
+        }
+        const size_t idx = static_cast<size_t>(m) * N + n;
+        store_out<OUTK>(Y, idx, static_cast<float>(a) * x_scale[m] * wsc);
+        if (acc_out) acc_out[idx] = a;
+      }
+    }
+  }
+}
+
+template <int MT, int KS, int BPL, int OUTK>
+void gemv_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K, void* Y,
+            int32_t* acc_out, hipStream_t stream) {
+  constexpr int rows = kGemvWaves / KS;
+  hipLaunchKernelGGL((sq_gemv_kernel<MT, KS, BPL, OUTK>), dim3((N + rows - 1) / rows), dim3(64 * kGemvWaves), 0,
+                     stream, Xq, xsc, Wq, wsc, M, N, K, Y, acc_out);
+}
+
+template <int MT, int OUTK>
+void gemv_k(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K, void* Y,
+            int32_t* acc_out, hipStream_t stream) {
+  // blocks of 64 chunks (1 KB) per row, at most 4 per lane: 1, 2, 4 or 8 waves per row
+  const int blocks = ((K >> 4) + 63) / 64;
+  if (blocks <= 4) gemv_t<MT, 1, 4, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+  else if (blocks <= 8) gemv_t<MT, 2, 4, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+  else if (blocks <= 16) gemv_t<MT, 4, 4, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+  else gemv_t<MT, 8, 4, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+}
+
+template <int MT>
+void gemv_o(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K, void* Y,
+            int y_dtype, int32_t* acc_out, hipStream_t stream) {
+  if (y_dtype == QLIN_F32) gemv_k<MT, OUT_F32>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+  else gemv_k<MT, OUT_F16>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
 }
 
 constexpr int kGemmThreads = 256;   // 4 waves side by side along N
@@ -529,6 +632,7 @@ void sq_act_launch(const uint16_t* X, const float* inv_s, int M, int K, int8_t* 
 
 qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
                            int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
+  // Up to 4 tokens (rows up to 32768): the GEMV, bound by the weight stream.
   // Larger batches (K a multiple of 128): eight waves, two per SIMD.  Above 64
   // tokens a 4 x 2 wave grid and the largest tile of 256 x 128 (64 x 64 per
   // wave), 128 x 128 (32 x 64) or 128 x 64 (32 x 32) that still gives at least
@@ -537,6 +641,12 @@ qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t*
   // 64 tokens a 2 x 4 grid of 32 x 32 wave tiles (64 x 128).  Batches of at most
   // 32 use the 32 TM x 128 kernel, whose ring depth stays within 160 KB of LDS:
   // stage = (32 TM + 128) rows x 128 bytes.
+  if (M <= 4 && K <= 32768) {
+    if (M == 1) gemv_o<1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+    else if (M == 2) gemv_o<2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+    else gemv_o<4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+    return QLIN_OK;
+  }
   if (M > 32 && M <= 64 && K % 128 == 0)
     return gemm_big_o<2, 4, 1, 1, 128, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
   if (M > 64 && K % 128 == 0) {

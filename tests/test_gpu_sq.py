@@ -84,7 +84,10 @@ def test_full_layer_end_to_end(layer):
 # (200 x 11000: 172 tiles) and 256 x 128 (600 x 8192: 192 tiles), and 8 output columns
 # (every weight row past N clamped); the last shape (K % 128 = 64) and (300, 40, 320)
 # fall back to the 32 TM x 128 kernel.
-RAGGED = ((1, 100, 64), (3, 129, 192), (33, 64, 128), (60, 3000, 512), (100, 257, 4096), (300, 40, 320),
+# Up to 4 tokens with rows up to 32768 the GEMV runs: (1, 100, 64), (3, 129, 192), (4, 300, 4096) and
+# (2, 5000, 32768) (eight waves per row); (1, 64, 40000) falls back to the 32 TM x 128 kernel.
+RAGGED = ((1, 100, 64), (3, 129, 192), (4, 300, 4096), (2, 5000, 32768), (1, 64, 40000),
+          (33, 64, 128), (60, 3000, 512), (100, 257, 4096), (300, 40, 320),
           (520, 1000, 1024), (1100, 130, 128), (65, 16400, 256), (300, 6000, 512),
           (200, 11000, 384), (600, 8192, 256), (520, 8, 256), (513, 300, 4160))
 
