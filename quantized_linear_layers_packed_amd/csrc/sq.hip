@@ -16,10 +16,11 @@
 // (|acc| <= K * 127^2 < 2^31 for K <= 131072).  The token tile of Xq and the
 // weight rows stream from HBM straight into a multi-stage LDS ring several K
 // steps ahead.  Epilogue: float(acc) * x_scale[m] * w_scale[n], rounded once.
-// Up to 4 tokens a GEMV with v_dot4; small batches use tiles of 32 TM x 128
-// (one wave per 32 columns); larger batches a grid of eight waves with tiles
-// of up to 256 x 128, whose operands are re-read from L2 half as often per
-// multiply-add.
+// Up to 4 tokens a GEMV with v_dot4; up to 32 a small-batch kernel with the K
+// split inside the workgroup (v_mfma_i32_16x16x64_i8); larger batches a grid of
+// eight waves with tiles of up to 256 x 128, whose operands are re-read from L2
+// half as often per multiply-add; tiles of 32 TM x 128 (one wave per 32
+// columns) where K is not a multiple of 128.
 
 #include <algorithm>
 
@@ -204,6 +205,117 @@ void gemv_o(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* w
             int y_dtype, int32_t* acc_out, hipStream_t stream) {
   if (y_dtype == QLIN_F32) gemv_k<MT, OUT_F32>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
   else gemv_k<MT, OUT_F16>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+}
+
+// Small batches (5 .. 32 tokens): CT tiles of 16 output columns per workgroup
+// of NWV waves that split K (128-byte blocks) among themselves, each wave
+// accumulating 16 x 16 int32 tiles (TM of them along the batch) with
+// v_mfma_i32_16x16x64_i8; the waves' tiles are added in wave order through LDS
+// (exact, no workspace, no hand-off between workgroups), then the GEMM's
+// epilogue.  Weights and activations go straight from memory into D-deep
+// register rings (unconditional, clamped loads); lane quarter h of an MFMA
+// takes bytes 64 s + 16 h .. + 15 of block s of both operands.
+template <int NWV, int TM, int D, int CT, int OUTK>
+__global__ __launch_bounds__(64 * NWV) void sq_skinny_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ x_scale, const int8_t* __restrict__ Wq,
+    const float* __restrict__ w_scale, int M, int N, int K, void* __restrict__ Y, int32_t* __restrict__ acc_out) {
+  __shared__ i32x4_t red[NWV][CT * TM][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, h = lane >> 4;
+  const int n0 = blockIdx.x * (16 * CT);
+  const int nb = K >> 7;                                          // 128-byte K blocks
+  const int b0 = (wv * nb) / NWV, b1 = ((wv + 1) * nb) / NWV;
+  const int8_t* wrow[CT];
+  const int8_t* xrow[TM];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) wrow[c] = Wq + static_cast<size_t>(min(n0 + 16 * c + col, N - 1)) * K + 16 * h;
+#pragma unroll
+  for (int t = 0; t < TM; ++t) xrow[t] = Xq + static_cast<size_t>(min(16 * t + col, M - 1)) * K + 16 * h;
+
+  i32x4_t acc[CT][TM];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[c][t] = i32x4_t{};
+
+  if (b0 < b1) {
+    const int blast = b1 - 1;
+    uint4 wq[D][CT][2];
+    uint4 av[D][TM][2];
+    auto load = [&](int b, uint4 (&w)[CT][2], uint4 (&a)[TM][2]) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) w[c][q] = *reinterpret_cast<const uint4*>(wrow[c] + 128 * b + 64 * q);
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) a[t][q] = *reinterpret_cast<const uint4*>(xrow[t] + 128 * b + 64 * q);
+    };
+    auto compute = [&](const uint4 (&w)[CT][2], const uint4 (&a)[TM][2]) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int t = 0; t < TM; ++t)
+            acc[c][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bitcast<i32x4_t>(a[t][q]), bitcast<i32x4_t>(w[c][q]),
+                                                             acc[c][t], 0, 0, 0);
+    };
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) load(min(b0 + j, blast), wq[j], av[j]);
+    auto step = [&](auto slot_c, int b) {
+      constexpr int S = decltype(slot_c)::value;
+      constexpr int SF = (S + D - 1) % D;
+      load(min(b + D - 1, blast), wq[SF], av[SF]);
+      __builtin_amdgcn_sched_barrier(0);     // keep the prefetch issued ahead of the math
+      compute(wq[S], av[S]);
+    };
+    int b = b0;
+    while (sk_run_steps<0, D>(step, b, b1)) {
+    }
+  }
+
+  // fixed-order sum of the waves' tiles; lane l of a tile holds column l % 16,
+  // rows 4 (l / 16) + r; wave c TM + t sums tile (c, t) and stores it
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) red[wv][c * TM + t][lane] = acc[c][t];
+  __syncthreads();
+  if (wv < CT * TM) {
+    const int t = wv % TM;
+    const int n = n0 + 16 * (wv / TM) + col;
+    i32x4_t tot = red[0][wv][lane];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) tot += red[w][wv][lane];
+    if (n < N) {
+      const float wsc = w_scale[n];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * t + 4 * h + r;
+        if (m < M) {
+          const size_t idx = static_cast<size_t>(m) * N + n;
+          store_out<OUTK>(Y, idx, static_cast<float>(tot[r]) * x_scale[m] * wsc);
+          if (acc_out) acc_out[idx] = tot[r];
+        }
+      }
+    }
+  }
+}
+
+template <int NWV, int TM, int D, int CT>
+void skinny_o(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K, void* Y,
+              int y_dtype, int32_t* acc_out, hipStream_t stream) {
+  static_assert(CT * TM <= NWV, "one summing wave per output tile");
+  const dim3 grid((N + 16 * CT - 1) / (16 * CT));
+  if (y_dtype == QLIN_F32)
+    hipLaunchKernelGGL((sq_skinny_kernel<NWV, TM, D, CT, OUT_F32>), grid, dim3(64 * NWV), 0, stream, Xq, xsc, Wq, wsc,
+                       M, N, K, Y, acc_out);
+  else
+    hipLaunchKernelGGL((sq_skinny_kernel<NWV, TM, D, CT, OUT_F16>), grid, dim3(64 * NWV), 0, stream, Xq, xsc, Wq, wsc,
+                       M, N, K, Y, acc_out);
 }
 
 constexpr int kGemmThreads = 256;   // 4 waves side by side along N
@@ -632,7 +744,8 @@ void sq_act_launch(const uint16_t* X, const float* inv_s, int M, int K, int8_t* 
 
 qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
                            int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
-  // Up to 4 tokens (rows up to 32768): the GEMV, bound by the weight stream.
+  // Up to 4 tokens (rows up to 32768): the GEMV, bound by the weight stream;
+  // then up to 32 tokens (K a multiple of 128) the small-batch MFMA kernel.
   // Larger batches (K a multiple of 128): eight waves, two per SIMD.  Above 64
   // tokens a 4 x 2 wave grid and the largest tile of 256 x 128 (64 x 64 per
   // wave), 128 x 128 (32 x 64) or 128 x 64 (32 x 32) that still gives at least
@@ -645,6 +758,20 @@ qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t*
     if (M == 1) gemv_o<1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
     else if (M == 2) gemv_o<2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
     else gemv_o<4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+    return QLIN_OK;
+  }
+  if (M <= 32 && K % 128 == 0) {
+    // small batches: 16-column tiles, 4, 2 or 1 per workgroup while at least 160
+    // workgroups remain (2 or 1 with two 16-token tiles)
+    const long long wg4 = (N + 63) / 64, wg2 = (N + 31) / 32;
+    if (M <= 16) {
+      if (wg4 >= 160) skinny_o<4, 1, 3, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+      else if (wg2 >= 160) skinny_o<4, 1, 3, 2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+      else skinny_o<4, 1, 4, 1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+    } else {
+      if (wg2 >= 160) skinny_o<4, 2, 3, 2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+      else skinny_o<4, 2, 3, 1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+    }
     return QLIN_OK;
   }
   if (M > 32 && M <= 64 && K % 128 == 0)

@@ -86,7 +86,11 @@ def test_full_layer_end_to_end(layer):
 # fall back to the 32 TM x 128 kernel.
 # Up to 4 tokens with rows up to 32768 the GEMV runs: (1, 100, 64), (3, 129, 192), (4, 300, 4096) and
 # (2, 5000, 32768) (eight waves per row); (1, 64, 40000) falls back to the 32 TM x 128 kernel.
+# 5..32 tokens with K a multiple of 128 run the small-batch kernel: one 16-column tile per
+# workgroup (5 x 1000), two (9 x 5200: 163 workgroups), four (16 x 11008: 172), and two
+# 16-token tiles with one (24 x 77) or two column tiles (32 x 6000: 188 workgroups).
 RAGGED = ((1, 100, 64), (3, 129, 192), (4, 300, 4096), (2, 5000, 32768), (1, 64, 40000),
+          (5, 1000, 640), (9, 5200, 256), (16, 11008, 512), (24, 77, 1024), (32, 6000, 384),
           (33, 64, 128), (60, 3000, 512), (100, 257, 4096), (300, 40, 320),
           (520, 1000, 1024), (1100, 130, 128), (65, 16400, 256), (300, 6000, 512),
           (200, 11000, 384), (600, 8192, 256), (520, 8, 256), (513, 300, 4160))
