@@ -16,7 +16,7 @@
 // (|acc| <= K * 127^2 < 2^31 for K <= 131072).  The token tile of Xq and the
 // weight rows stream from HBM straight into a multi-stage LDS ring several K
 // steps ahead.  Epilogue: float(acc) * x_scale[m] * w_scale[n], rounded once.
-// Up to 4 tokens a GEMV with v_dot4; up to 32 a small-batch kernel with the K
+// Up to 2 tokens a GEMV with v_dot4; up to 32 a small-batch kernel with the K
 // split inside the workgroup (v_mfma_i32_16x16x64_i8); larger batches a grid of
 // eight waves with tiles of up to 256 x 128, whose operands are re-read from L2
 // half as often per multiply-add; tiles of 32 TM x 128 (one wave per 32
@@ -105,7 +105,8 @@ __global__ __launch_bounds__(kActThreads) void sq_act_kernel(const uint16_t* __r
   }
 }
 
-// GEMV for batches of at most 4 tokens, where the product is bound by the
+// GEMV for batches of at most 2 tokens (4 where K is not a multiple of 128),
+// where the product is bound by the
 // weight stream: each output row is served by KS waves (KS contiguous blocks
 // of 64 lanes x 16 bytes interleaved, so every load instruction covers 1 KB of
 // the row); all of a lane's weight chunks are loaded first, then the matching
@@ -744,7 +745,7 @@ void sq_act_launch(const uint16_t* X, const float* inv_s, int M, int K, int8_t* 
 
 qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
                            int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
-  // Up to 4 tokens (rows up to 32768): the GEMV, bound by the weight stream;
+  // Up to 2 tokens (rows up to 32768): the GEMV, bound by the weight stream;
   // then up to 32 tokens (K a multiple of 128) the small-batch MFMA kernel.
   // Larger batches (K a multiple of 128): eight waves, two per SIMD.  Above 64
   // tokens a 4 x 2 wave grid and the largest tile of 256 x 128 (64 x 64 per
@@ -754,24 +755,27 @@ qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t*
   // 64 tokens a 2 x 4 grid of 32 x 32 wave tiles (64 x 128).  Batches of at most
   // 32 use the 32 TM x 128 kernel, whose ring depth stays within 160 KB of LDS:
   // stage = (32 TM + 128) rows x 128 bytes.
-  if (M <= 4 && K <= 32768) {
+  if (M <= 2 && K <= 32768) {
     if (M == 1) gemv_o<1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-    else if (M == 2) gemv_o<2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-    else gemv_o<4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+    else gemv_o<2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
     return QLIN_OK;
   }
   if (M <= 32 && K % 128 == 0) {
-    // small batches: 16-column tiles, 4, 2 or 1 per workgroup while at least 160
-    // workgroups remain (2 or 1 with two 16-token tiles)
+    // small batches: 16-column tiles, 4, 2 or 1 per workgroup while at least
+    // 300 workgroups remain (with two 16-token tiles: 2 while at least 160)
     const long long wg4 = (N + 63) / 64, wg2 = (N + 31) / 32;
     if (M <= 16) {
-      if (wg4 >= 160) skinny_o<4, 1, 3, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-      else if (wg2 >= 160) skinny_o<4, 1, 3, 2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+      if (wg4 >= 300) skinny_o<4, 1, 3, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+      else if (wg2 >= 300) skinny_o<4, 1, 3, 2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
       else skinny_o<4, 1, 4, 1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
     } else {
       if (wg2 >= 160) skinny_o<4, 2, 3, 2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
       else skinny_o<4, 2, 3, 1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
     }
+    return QLIN_OK;
+  }
+  if (M <= 4 && K <= 32768) {          // K not a multiple of 128
+    gemv_o<4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
     return QLIN_OK;
   }
   if (M > 32 && M <= 64 && K % 128 == 0)
