@@ -113,3 +113,26 @@ def test_gemm_ragged_shapes():
         check_close(Y, osq.dequant_output(acc_o, xs, ws), "f32 out")
         Y16, _ = gpu_gemm(dev(Xq), dev(xs), dev(Wq), dev(ws), M, N, K, F16, want_acc=False)
         check_close(Y16, osq.dequant_output(acc_o, xs, ws), "f16 out")
+
+
+def test_every_int8_kernel_gives_the_same_accumulators():
+    """int32 accumulation is exact, so the int8 kernels agree bit for bit on the rows
+    they share: prefixes of one batch through the GEMV (2 tokens), the small-batch
+    kernel (5 and 24 tokens), the 64 x 128 wave-grid tiles (40), the larger wave-grid
+    tiles (300) and, with K not a multiple of 128, the 32 TM x 128 kernel (the oracle
+    checks the longest prefix)."""
+    r = np.random.default_rng(21)
+    for K in (2048, 2112):
+        N = 1500
+        Xq = r.integers(-127, 128, size=(300, K)).astype(np.int8)
+        Wq = r.integers(-127, 128, size=(N, K)).astype(np.int8)
+        xs = r.uniform(1e-3, 1e-2, 300).astype(np.float32)
+        ws = r.uniform(1e-4, 1e-3, N).astype(np.float32)
+        Wq_d, ws_d = dev(Wq), dev(ws)
+        accs = {}
+        for M in (2, 5, 24, 40, 300):
+            say(f"sq int8 kernels K={K} M={M}")
+            _, accs[M] = gpu_gemm(dev(Xq[:M]), dev(xs[:M]), Wq_d, ws_d, M, N, K, F32)
+        assert np.array_equal(accs[300], osq.int_gemm(Xq, Wq))
+        for M in (2, 5, 24, 40):
+            assert np.array_equal(accs[M], accs[300][:M]), f"M={M} differs from the first rows of M=300"
