@@ -118,9 +118,10 @@ __device__ __forceinline__ float row_sum64(float v) {
 //   1. the activation loads for the LDS staging (one 32-value piece per
 //      thread; vector loads return in order, so these arrive first),
 //   2. everything the wave needs from HBM: its chunks, the statistics of its
-//      blocks and, on the first slice, up to 4 CSR entries per lane,
-//   3. the staging (pairs in the unpack order + two per-chunk sums) and the
-//      wave's statistics into LDS,
+//      blocks and, on the first slice, up to 4 CSR entries per lane (no load
+//      waits for another before the stream is issued),
+//   3. the staging (pairs in the unpack order + two per-chunk sums), then
+//      the wave's statistics into LDS,
 //   4. the code unpack, while other waves' staging may still be in flight,
 //   5. after the barrier, the dot products, then the row's CSR entries of the
 //      slice into the same accumulators.
@@ -157,18 +158,15 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
   const int e0 = nok ? row_ptr[n] : 0;
   const int e1 = nok ? row_ptr[n + 1] : 0;
 
-  // CSR entries of this row held by this lane: e0 + 64 (KSW i + part) + lane
+  // CSR entries of this row held by this lane: e0 + 64 (KSW i + part) + lane,
+  // loaded on the first slice behind the dense stream and kept as raw fp16
+  // bits until used (a conversion here would make the wave wait for each load)
   int ccol[kCsr];
-  float cval[kCsr];
+  uint32_t cbits[kCsr];
 #pragma unroll
   for (int i = 0; i < kCsr; ++i) {
-    const int e = e0 + 64 * (KSW * i + part) + lane;
     ccol[i] = -1;
-    cval[i] = 0.0f;
-    if (e < e1) {
-      ccol[i] = col_idx[e];
-      cval[i] = f16_bits_to_f32(vals[e]);
-    }
+    cbits[i] = 0u;
   }
 
   float res[MT];
@@ -208,16 +206,21 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
       s1[t] = *reinterpret_cast<const uint3*>(s1row + 3 * (bbase + blk));
       s2[t] = s2row[bbase + blk];
     }
-    // ---- 3. staging (the previous slice's readers are done after this barrier)
-    __syncthreads();
+    if (k0 == 0) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int blk = b0 + 64 * t + lane;
-      if (blk < b1) {
-        st4[blk] = make_uint4(s1[t].x, s1[t].y, s1[t].z, s2[t].x);
-        st1[blk] = s2[t].y;
+      for (int i = 0; i < kCsr; ++i) {
+        const int e = e0 + 64 * (KSW * i + part) + lane;
+        if (e < e1) {
+          ccol[i] = col_idx[e];
+          cbits[i] = vals[e];
+        }
       }
     }
+    // ---- 3. staging (the previous slice's readers are done after this barrier);
+    //      the activations first: they were loaded first, so this VALU work
+    //      overlaps the weight loads still in flight, while the statistics
+    //      below were loaded last and wait for this wave's whole stream
+    __syncthreads();
     for (int it = tid; it < items; it += kThreads) {
       const int m = it / cs, c = it - m * cs;
       uint32_t u[16];
@@ -249,6 +252,14 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
       }
       xs[m * 2 * CS + 2 * c] = sa;
       xs[m * 2 * CS + 2 * c + 1] = sb;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int blk = b0 + 64 * t + lane;
+      if (blk < b1) {
+        st4[blk] = make_uint4(s1[t].x, s1[t].y, s1[t].z, s2[t].x);
+        st1[blk] = s2[t].y;
+      }
     }
     // ---- 4. unpack this wave's chunks while the staging completes
     uint32_t pk[BPL][16];
@@ -324,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
     if (nok) {
 #pragma unroll
       for (int i = 0; i < kCsr; ++i)
-        if (ccol[i] >= 0) outlier(ccol[i], cval[i]);
+        if (ccol[i] >= 0) outlier(ccol[i], f16_bits_to_f32(static_cast<uint16_t>(cbits[i])));
       for (int e = e0 + 64 * (KSW * kCsr + part) + lane; e < e1; e += 64 * KSW)
         outlier(col_idx[e], f16_bits_to_f32(vals[e]));
     }

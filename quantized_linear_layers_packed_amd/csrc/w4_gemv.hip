@@ -98,16 +98,19 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
   const int cshift = gshift - 5;               // chunk -> group
 
   // ---- 1. activation loads for the staging: chunk tid of batch rows 0 and 1
-  //      (C <= 512 = threads, so each thread stages at most one chunk per row)
+  //      (C <= 512 = threads, so each thread stages at most one chunk per row).
+  //      Every load up to the staging is unconditional (threads past the row
+  //      read its last chunk, lanes past it the last valid address), so the
+  //      count of loads issued after these is fixed and the staging waits for
+  //      the activations alone, not for the weight stream behind them.
+  constexpr int XR = MT < 2 ? MT : 2;          // batch rows staged from these registers (M >= XR)
   const bool stager = tid < C;
-  uint4 xv[2][4];
+  uint4 xv[XR][4];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    if (m < M && stager) {
-      const uint4* src = reinterpret_cast<const uint4*>(X + m * K) + 4 * tid;
+  for (int m = 0; m < XR; ++m) {
+    const uint4* src = reinterpret_cast<const uint4*>(X + m * K) + 4 * min(tid, C - 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[m][i] = src[i];
-    }
+    for (int i = 0; i < 4; ++i) xv[m][i] = src[i];
   }
 
   // ---- 2. weights, then the row's scales and zero words (rows past N read row N - 1)
@@ -119,34 +122,32 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
 #pragma unroll
   for (int b = 0; b < BPL; ++b) {
     const int c = LPR * (KS * b + part) + sl;
-    if (c < C) w[b] = load_stream16(qrow + c);
+    w[b] = load_stream16(qrow + min(c, C - 1));
   }
   // scale registers: lane i of the row, register t, holds the scale of group
-  // LPR t + i (a row has at most one group per chunk, so KS * BPL registers suffice)
+  // LPR t + i (a row has at most one group per chunk, so KS * BPL registers
+  // suffice; lanes past the row's groups hold its last scale, never read)
   constexpr int SV = KS * BPL;
   uint32_t sv[SV];
   const uint16_t* srow = scales + nn * ng;
 #pragma unroll
-  for (int t = 0; t < SV; ++t) {
-    const int g = LPR * t + sl;
-    sv[t] = 0u;
-    if (LPR * t < ng && g < ng) sv[t] = static_cast<uint32_t>(srow[g]);
-  }
-  uint32_t zv = 0u;                            // nzw <= LPR for the shapes that pick LPR
-  if (sl < nzw) zv = qzeros[nn * nzw + sl];
+  for (int t = 0; t < SV; ++t) sv[t] = static_cast<uint32_t>(srow[min(LPR * t + sl, ng - 1)]);
+  // nzw <= LPR for the shapes that pick LPR; lanes past it hold the last word
+  const uint32_t zv = qzeros[nn * nzw + min(sl, nzw - 1)];
 
-  // ---- 3. finish staging the activations
-  if (stager) {
-    for (int m = 0; m < M; ++m) {
-      uint4 v4[4];
-      if (m < 2) {
+  // ---- 3. finish staging the activations: rows 0 and 1 from the registers
+  //      above, any further rows (batches of three or more) loaded here.  The
+  //      branch condition reads every loaded activation word (its second term
+  //      is never true: M >= 1), so the compiler cannot sink those loads into
+  //      the branch, behind the weight stream.
+  uint32_t xfold = 0u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = xv[m & 1][i];
-      } else {
-        const uint4* src = reinterpret_cast<const uint4*>(X + m * K) + 4 * tid;
+  for (int m = 0; m < XR; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = src[i];
-      }
+    for (int i = 0; i < 4; ++i) xfold ^= xv[m][i].x ^ xv[m][i].y ^ xv[m][i].z ^ xv[m][i].w;
+  const bool stage_here = stager | ((M <= 0) & (xfold == 0u));
+  if (stage_here) {
+    auto stage_row = [&](int m, const uint4 (&v4)[4]) {
       float2 es = make_float2(0.0f, 0.0f);
       uint4 pq[4];
 #pragma unroll
@@ -160,6 +161,15 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) xl[(m * 4 + i) * C + tid] = pq[i];
       xs[m * C + tid] = Codec::sums(es);
+    };
+#pragma unroll
+    for (int m = 0; m < XR; ++m) stage_row(m, xv[m]);
+    for (int m = XR; m < MT && m < M; ++m) {
+      uint4 v4[4];
+      const uint4* src = reinterpret_cast<const uint4*>(X + m * K) + 4 * tid;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = src[i];
+      stage_row(m, v4);
     }
   }
   // ---- 4. unpack the codes and look up the groups' scales and zero points
