@@ -125,30 +125,38 @@ __global__ __launch_bounds__(64 * kGemvWaves) void sq_gemv_kernel(
   const int n = blockIdx.x * (kGemvWaves / KS) + wv / KS;
   const int C = K >> 4;                                           // 16-byte chunks per row
   const uint4* wrow = reinterpret_cast<const uint4*>(Wq + static_cast<size_t>(min(n, N - 1)) * K);
+  // Every load is issued before any arithmetic and none is conditional (chunks
+  // past the row end re-read its last chunk, batch rows past M the last row),
+  // so the waits before the dot products count exactly: the activation chunks
+  // (cache hits behind the weight stream) are never fetched one at a time.
+  // A chunk past the row end gets a zero weight, adding exactly nothing; the
+  // launch shape keeps such chunks to less than one block per row.
   uint4 w[BPL];
 #pragma unroll
   for (int b = 0; b < BPL; ++b) {
     const int c = 64 * (KS * b + part) + lane;
-    w[b] = make_uint4(0u, 0u, 0u, 0u);
-    if (c < C) w[b] = load_stream16(wrow + c);
+    w[b] = load_stream16(wrow + min(c, C - 1));
+  }
+  uint4 x[BPL][MT];
+#pragma unroll
+  for (int b = 0; b < BPL; ++b) {
+    const int c = min(64 * (KS * b + part) + lane, C - 1);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) x[b][m] = reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(min(m, M - 1)) * K)[c];
   }
   int acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0;
 #pragma unroll
   for (int b = 0; b < BPL; ++b) {
-    const int c = 64 * (KS * b + part) + lane;
-    if (c < C) {
+    const bool inrow = 64 * (KS * b + part) + lane < C;
+    const uint4 wb = inrow ? w[b] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < M) {
-          const uint4 x = reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(m) * K)[c];
-          acc[m] = __builtin_amdgcn_sdot4(static_cast<int>(w[b].x), static_cast<int>(x.x), acc[m], false);
-          acc[m] = __builtin_amdgcn_sdot4(static_cast<int>(w[b].y), static_cast<int>(x.y), acc[m], false);
-          acc[m] = __builtin_amdgcn_sdot4(static_cast<int>(w[b].z), static_cast<int>(x.z), acc[m], false);
-          acc[m] = __builtin_amdgcn_sdot4(static_cast<int>(w[b].w), static_cast<int>(x.w), acc[m], false);
-        }
-      }
+    for (int m = 0; m < MT; ++m) {
+      acc[m] = __builtin_amdgcn_sdot4(static_cast<int>(wb.x), static_cast<int>(x[b][m].x), acc[m], false);
+      acc[m] = __builtin_amdgcn_sdot4(static_cast<int>(wb.y), static_cast<int>(x[b][m].y), acc[m], false);
+      acc[m] = __builtin_amdgcn_sdot4(static_cast<int>(wb.z), static_cast<int>(x[b][m].z), acc[m], false);
+      acc[m] = __builtin_amdgcn_sdot4(static_cast<int>(wb.w), static_cast<int>(x[b][m].w), acc[m], false);
     }
   }
 #pragma unroll
@@ -193,11 +201,19 @@ void gemv_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* w
 template <int MT, int OUTK>
 void gemv_k(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K, void* Y,
             int32_t* acc_out, hipStream_t stream) {
-  // blocks of 64 chunks (1 KB) per row, at most 4 per lane: 1, 2, 4 or 8 waves per row
+  // blocks of 64 chunks (1 KB) per row, at most 4 per lane: 1, 2, 4 or 8 waves
+  // per row, each with the fewest blocks that cover the row (every block is
+  // loaded, so a block past the row end would be wasted work)
   const int blocks = ((K >> 4) + 63) / 64;
-  if (blocks <= 4) gemv_t<MT, 1, 4, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+  if (blocks <= 1) gemv_t<MT, 1, 1, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+  else if (blocks <= 2) gemv_t<MT, 1, 2, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+  else if (blocks <= 3) gemv_t<MT, 1, 3, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+  else if (blocks <= 4) gemv_t<MT, 1, 4, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+  else if (blocks <= 6) gemv_t<MT, 2, 3, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
   else if (blocks <= 8) gemv_t<MT, 2, 4, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+  else if (blocks <= 12) gemv_t<MT, 4, 3, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
   else if (blocks <= 16) gemv_t<MT, 4, 4, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+  else if (blocks <= 24) gemv_t<MT, 8, 3, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
   else gemv_t<MT, 8, 4, OUTK>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
 }
 

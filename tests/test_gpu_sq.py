@@ -84,12 +84,15 @@ def test_full_layer_end_to_end(layer):
 # (200 x 11000: 172 tiles) and 256 x 128 (600 x 8192: 192 tiles), and 8 output columns
 # (every weight row past N clamped); the last shape (K % 128 = 64) and (300, 40, 320)
 # fall back to the 32 TM x 128 kernel.
-# Up to 2 tokens with rows up to 32768 the GEMV runs: (1, 100, 64), (2, 5000, 32768) (eight waves
-# per row), and up to 4 where K is not a multiple of 128: (3, 129, 192); (1, 64, 40000) falls back
-# to the 32 TM x 128 kernel.  3..32 tokens with K a multiple of 128 run the small-batch kernel: one
+# Up to 2 tokens with rows up to 32768 the GEMV runs, with 1, 2, 4 or 8 waves per row of 1 to 4
+# blocks of 1 KB each: (1, 100, 64) one wave of one block, (2, 333, 5120) 2 x 3, (1, 700, 11008)
+# 4 x 3 (one block past the row end), (2, 90, 12352) 4 x 4, (1, 257, 20480) 8 x 3 and
+# (2, 5000, 32768) 8 x 4; up to 4 tokens where K is not a multiple of 128: (3, 129, 192);
+# (1, 64, 40000) falls back to the 32 TM x 128 kernel.  3..32 tokens with K a multiple of 128 run the small-batch kernel: one
 # 16-column tile per workgroup (4 x 300, 5 x 1000, 9 x 5200), two (16 x 11008: 344 workgroups),
 # four (8 x 19300: 302), and two 16-token tiles with one (24 x 77) or two column tiles (32 x 6000).
 RAGGED = ((1, 100, 64), (3, 129, 192), (4, 300, 4096), (2, 5000, 32768), (1, 64, 40000),
+          (2, 333, 5120), (1, 700, 11008), (2, 90, 12352), (1, 257, 20480),
           (5, 1000, 640), (9, 5200, 256), (16, 11008, 512), (8, 19300, 256), (24, 77, 1024), (32, 6000, 384),
           (33, 64, 128), (60, 3000, 512), (100, 257, 4096), (300, 40, 320),
           (520, 1000, 1024), (1100, 130, 128), (65, 16400, 256), (300, 6000, 512),
