@@ -73,20 +73,15 @@ __host__ __device__ constexpr int pair_hi(int p) {
   return p < 5 ? p + 5 : p < 8 ? p + 8 : p == 8 ? 18 : p == 9 ? 19 : p < 15 ? p + 15 : 31;
 }
 
-// Inverse: (pair << 1 | half) of within-chunk offset o.
+// Inverse: (pair << 1 | half) of within-chunk offset o, without branches (it
+// runs once per outlier, in divergent lanes): the pair is o - d(o), d a step
+// function rising by 5, 3, 2, 5 and 1 at offsets 5, 13, 18, 25 and 31, and the
+// offsets held in high halves are the set bits of 0xBE0CE3E0 (5-9, 13-15,
+// 18-19, 25-29 and 31), as pair_lo / pair_hi above lay them out.
 __device__ __forceinline__ int pair_slot(int o) {
-  if (o < 16) {
-    if (o < 5) return o << 1;
-    if (o < 10) return ((o - 5) << 1) | 1;
-    if (o < 13) return (o - 5) << 1;
-    return ((o - 8) << 1) | 1;
-  }
-  const int b = o - 16;
-  if (b < 2) return (8 + b) << 1;
-  if (b < 4) return ((6 + b) << 1) | 1;
-  if (b < 9) return (6 + b) << 1;
-  if (b < 14) return ((1 + b) << 1) | 1;
-  return (15 << 1) | (b - 14);
+  const int d = (o >= 5 ? 5 : 0) + (o >= 13 ? 3 : 0) + (o >= 18 ? 2 : 0) + (o >= 25 ? 5 : 0) + (o >= 31 ? 1 : 0);
+  const int half = static_cast<int>((0xBE0CE3E0u >> o) & 1u);
+  return ((o - d) << 1) | half;
 }
 
 __device__ __forceinline__ uint32_t half_of(const uint32_t u[16], int o) {
