@@ -35,7 +35,9 @@ namespace {
 
 constexpr int kWaves = 8;                // output rows (one per wavefront) per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr size_t kLdsBudget = 60 * 1024;
+// LDS for one K slice: two workgroups still fit a CU's 160 KB, and a 6656-wide row is one slice up
+// to 4 batch rows
+constexpr size_t kLdsBudget = 72 * 1024;
 
 // fp16 pair (1024 + 8 c_lo, 1024 + 8 c_hi) from field i of both halves of w:
 // a shift and one v_and_or_b32.
@@ -371,6 +373,16 @@ void launch_k(const SpqrArgs& a, int KS, hipStream_t stream) {
                      static_cast<size_t>(kWaves) * BS * 20;
   const int rows = kWaves / KSW;
   const int grid = (a.N + rows - 1) / rows;
+  // more than 64 KB of dynamic LDS must be allowed per kernel (once per process,
+  // thread-safe initialisation of function-local statics)
+  static const bool lds_f32 = (hipFuncSetAttribute(reinterpret_cast<const void*>(spqr_gemv_kernel<MT, KSW, BPL, OUT_F32>),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   static_cast<int>(kLdsBudget + 1024)) == hipSuccess);
+  static const bool lds_f16 = (hipFuncSetAttribute(reinterpret_cast<const void*>(spqr_gemv_kernel<MT, KSW, BPL, OUT_F16>),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   static_cast<int>(kLdsBudget + 1024)) == hipSuccess);
+  (void)lds_f32;
+  (void)lds_f16;
   if (a.y_dtype == QLIN_F32)
     hipLaunchKernelGGL((spqr_gemv_kernel<MT, KSW, BPL, OUT_F32>), dim3(grid), dim3(kThreads), lds, stream,
                        a.X, a.M, a.K, KS, a.codes, a.stats1, a.stats2, a.row_ptr, a.col_idx, a.vals, a.N, a.Y);
@@ -391,12 +403,30 @@ void launch_m(const SpqrArgs& a, hipStream_t stream) {
   KS = KS / 256 * 256;
   if (KS < 256) KS = 256;
   if (KS > a.K) KS = a.K;
+  // as many slices as that needs, of equal size (a short last slice would pay a
+  // whole pass of staging, barriers and load latency for little work); K and
+  // the largest slice are multiples of 256, so this size stays within the budget
+  const int nslices = (a.K + KS - 1) / KS;
+  KS = (a.K / 256 + nslices - 1) / nslices * 256;
   // split a row over KSW waves so that each wave has at most 4 chunks per lane
-  // (its unpacked codes then stay in registers)
+  // (its unpacked codes then stay in registers), and give each wave the fewest
+  // 64-chunk blocks that cover its part (every block is loaded and unpacked)
   const int cs = KS / 32;
-  if (cs <= 256) launch_k<MT, 1, 4>(a, KS, stream);
-  else if (cs <= 512) launch_k<MT, 2, 4>(a, KS, stream);
-  else launch_k<MT, 4, 4>(a, KS, stream);
+  const int ksw = cs <= 256 ? 1 : cs <= 512 ? 2 : 4;
+  const int cp = ((cs + ksw - 1) / ksw + 7) & ~7;          // chunks per wave, as in the kernel
+  const int bpl = (cp + 63) / 64;
+  if (ksw == 1) {
+    if (bpl <= 1) launch_k<MT, 1, 1>(a, KS, stream);
+    else if (bpl == 2) launch_k<MT, 1, 2>(a, KS, stream);
+    else if (bpl == 3) launch_k<MT, 1, 3>(a, KS, stream);
+    else launch_k<MT, 1, 4>(a, KS, stream);
+  } else if (ksw == 2) {
+    if (bpl <= 3) launch_k<MT, 2, 3>(a, KS, stream);
+    else launch_k<MT, 2, 4>(a, KS, stream);
+  } else {
+    if (bpl <= 3) launch_k<MT, 4, 3>(a, KS, stream);
+    else launch_k<MT, 4, 4>(a, KS, stream);
+  }
 }
 
 // Debug: dense codes and first-level statistic codes via the forward's routines.
