@@ -1,5 +1,7 @@
 """Comparison metrics and storage-dtype decoders used by the oracle checks.
 
+Pinned by hand-worked values in tests/golden/metrics.json (tests/test_oracle_metrics.py).
+
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 """
 from __future__ import annotations
