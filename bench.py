@@ -440,13 +440,13 @@ def sweep_actorder(torch, qlin, synth, steps):
 # ---------------------------------------------------------------------------
 
 def cpu_baseline(synth):
-    """The oracle, untouched, on one forward step of the headline workload."""
+    """The plain C++ oracle (oracle/qlin_oracle.cpp: fp64 decode + fp64 dot
+    products, OpenMP over output rows), untouched, on full forward steps of the
+    headline workload with one thread per core of the process affinity mask,
+    plus the 1024x1024 4-bit layer at M=1 on one thread."""
+    from oracle import cref
     from oracle import w4 as ow4
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    cores = len(os.sched_getaffinity(0))
     cfg = synth.WORKLOADS["w4_llama7b"]
     packed = []
     total_bytes = 0
@@ -456,18 +456,34 @@ def cpu_baseline(synth):
         X = synth.activations("w4_llama7b", li, 1)
         packed.append((X, st, K))
         total_bytes += sum(a.nbytes for a in st) + X.nbytes + N * 2
+    cref.w4_forward(packed[0][0], *packed[0][1], packed[0][2], 128, threads=cores)     # load + warm
     t0 = time.perf_counter()
     reps = 0
     while True:
         for X, st, K in packed:
-            ow4.forward(X, *st, K, 128)
+            cref.w4_forward(X, *st, K, 128, threads=cores)
         reps += 1
-        if time.perf_counter() - t0 > 10.0 or reps >= 5:
+        if time.perf_counter() - t0 > 10.0 or reps >= 20:
             break
     dt = (time.perf_counter() - t0) / reps
-    return {"value": total_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{reps} full forward step(s) of the three 4-bit layers at M=1 "
-                      f"(numpy fp64 decode + matvec), {dt * 1e3:.0f} ms per step"}
+    # small layer (1024 x 1024, M = 1) on one thread, median of 3
+    c1 = synth.WORKLOADS["w4_1k"]
+    N1, K1 = c1["layers"][0]
+    st1 = ow4.encode(synth.layer_weight("w4_1k", 0), 128)
+    X1 = synth.activations("w4_1k", 0, 1)
+    b1 = sum(a.nbytes for a in st1) + X1.nbytes + N1 * 2
+    ts = []
+    for _ in range(3):
+        t1 = time.perf_counter()
+        cref.w4_forward(X1, *st1, K1, 128, threads=1)
+        ts.append(time.perf_counter() - t1)
+    t1 = sorted(ts)[1]
+    return {"value": round(total_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} full forward step(s) of the three 4-bit Llama-7B-shaped layers at M=1 through the "
+                      f"plain C++ oracle (fp64 decode + fp64 dot, OpenMP over rows, {cores} threads = cores in "
+                      f"the affinity mask), {dt * 1e3:.1f} ms per step",
+            "one_thread_small_layer": {"layer": f"{N1}x{K1}, M=1", "GB/s": round(b1 / t1 / 1e9, 3),
+                                       "ms": round(t1 * 1e3, 2), "threads": 1}}
 
 
 # ---------------------------------------------------------------------------

@@ -21,6 +21,13 @@ Sources (three "Makale Bülteni" newsletter pages):
   weights, alpha about 0.8-0.85, maxima from calibration samples.  Section
   "İddia ve Gerçeklik".
 
+Two forms, sharing nothing with the library: the numpy modules below (format
+encoders, decoders and fp64 forwards), and plain C++17 forwards in
+qlin_oracle.cpp (fp64 decode + fp64 dot products per output row, OpenMP over
+rows; int64 accumulation for W8A8), compiled on its own by the host compiler
+and loaded through ``oracle.cref``.  Each is pinned against hand-worked values,
+grid points, brute force and textbook routines (tests/test_oracle_*.py).
+
 Precision: encoders run in fp32 in the written operation order (numpy float32
 arithmetic is IEEE round-to-nearest-even, element by element, with no fused
 multiply-add); decoders and forwards run in fp64.
