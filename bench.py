@@ -68,6 +68,11 @@ def to_dev(torch, a):
     return torch.from_numpy(a).cuda()
 
 
+def zeros_ws(torch, nbytes):
+    """A zero-filled device workspace (None when none is needed)."""
+    return torch.zeros(int(nbytes), dtype=torch.uint8, device="cuda") if nbytes else None
+
+
 def copies_for(bytes_per_set):
     return max(2, -(-ROTATE_BYTES // max(1, bytes_per_set)))
 
@@ -149,6 +154,10 @@ def w4_layers(torch, qlin, synth, workload, M):
                            xdt=qlin.QLIN_BF16 if xbf else qlin.QLIN_F16,
                            ydt=qlin.QLIN_BF16 if cfg["y_dtype"] == "bf16" else qlin.QLIN_F16,
                            io=X.numel() * X.element_size() + Y.numel() * Y.element_size()))
+    need = max(qlin.qlin_w4_workspace_bytes(l["xdt"], M, l["K"], l["N"], G, l["ydt"]) for l in layers)
+    ws = zeros_ws(torch, need)
+    for l in layers:
+        l["ws"] = ws
     rotate(torch, layers)
     return layers
 
@@ -167,7 +176,8 @@ def w4_step_fns(qlin, layers):
     for l in layers:
         def f(i, l=l):
             qw, sc, qz = l["packed"][i % len(l["packed"])]
-            qlin.qlin_w4_forward(l["X"], l["xdt"], l["M"], l["K"], qw, sc, qz, l["N"], l["G"], l["Y"], l["ydt"])
+            qlin.qlin_w4_forward(l["X"], l["xdt"], l["M"], l["K"], qw, sc, qz, l["N"], l["G"], l["Y"], l["ydt"],
+                                 workspace=l["ws"])
         fns.append(f)
     return fns
 
@@ -215,6 +225,9 @@ def sq_layers(torch, qlin, synth, M):
                            xs=torch.empty((M,), dtype=torch.float32, device="cuda"),
                            Y=torch.empty((M, N), dtype=torch.float16, device="cuda"),
                            wbytes=sum(t.numel() * t.element_size() for t in packed)))
+    ws = zeros_ws(torch, max(qlin.sq_int8_gemm_workspace_bytes(M, l["N"], l["K"], qlin.QLIN_F16) for l in layers))
+    for l in layers:
+        l["ws"] = ws
     rotate(torch, layers)
     return layers
 
@@ -227,7 +240,8 @@ def sq_step_fns(qlin, layers):
 
         def g(i, l=l):
             Wq, ws = l["packed"][i % len(l["packed"])]
-            qlin.sq_int8_gemm(l["Xq"], l["xs"], Wq, ws, l["M"], l["N"], l["K"], l["Y"], qlin.QLIN_F16, None)
+            qlin.sq_int8_gemm(l["Xq"], l["xs"], Wq, ws, l["M"], l["N"], l["K"], l["Y"], qlin.QLIN_F16, None,
+                              workspace=l["ws"])
         act.append(a)
         gemm.append(g)
     return act, gemm
@@ -295,6 +309,9 @@ def sweep_batch(torch, qlin, synth, steps):
     f16 = dense_f16_weights(torch, Ws)
     f16_bytes = sum(t.numel() * 2 for t in f16[0])
     del Ws
+    wsp = zeros_ws(torch, max(max(qlin.qlin_w4_workspace_bytes(qlin.QLIN_F16, M, K, N, 128, qlin.QLIN_F16),
+                                  qlin.sq_int8_gemm_workspace_bytes(M, N, K, qlin.QLIN_F16))
+                              for M in SWEEP_M for N, K in shapes))
 
     rows = []
     for M in SWEEP_M:
@@ -304,7 +321,7 @@ def sweep_batch(torch, qlin, synth, steps):
                 def f(i, li=li, N=N, K=K):
                     qw, sc, qz = w4[i % len(w4)][li]
                     qlin.qlin_w4_forward(Xd[li][:M], qlin.QLIN_F16, M, K, qw, sc, qz, N, 128, Yd[li][:M],
-                                         qlin.QLIN_F16)
+                                         qlin.QLIN_F16, workspace=wsp)
                 out.append(f)
             return out
 
@@ -314,7 +331,8 @@ def sweep_batch(torch, qlin, synth, steps):
                 def f(i, li=li, N=N, K=K):
                     Wq, ws = sq[i % len(sq)][li]
                     qlin.sq_smooth_quant_act(Xd[li][:M], inv[li], M, K, Xq[li][:M], xs[li][:M])
-                    qlin.sq_int8_gemm(Xq[li][:M], xs[li][:M], Wq, ws, M, N, K, Yd[li][:M], qlin.QLIN_F16, None)
+                    qlin.sq_int8_gemm(Xq[li][:M], xs[li][:M], Wq, ws, M, N, K, Yd[li][:M], qlin.QLIN_F16, None,
+                                      workspace=wsp)
                 out.append(f)
             return out
 
@@ -413,6 +431,8 @@ def sweep_actorder(torch, qlin, synth, steps):
     perms = [to_dev(torch, synth.rng(f"actorder/perm{li}").permutation(K).astype(np.int32))
              for li, (_, K) in enumerate(shapes)]
     rows = []
+    wsp = zeros_ws(torch, max(qlin.qlin_w4_workspace_bytes(qlin.QLIN_F16, M, K, N, 128, qlin.QLIN_F16)
+                              for M in Ms for N, K in shapes))
     for M in Ms:
         Xd = [to_dev(torch, synth.x_f16(M, K, f"actorder/X{li}")) for li, (_, K) in enumerate(shapes)]
         Xp = [torch.empty_like(x) for x in Xd]
@@ -421,13 +441,14 @@ def sweep_actorder(torch, qlin, synth, steps):
         def natural(i):
             for li, (N, K) in enumerate(shapes):
                 qw, sc, qz = sets[i % len(sets)][li]
-                qlin.qlin_w4_forward(Xd[li], qlin.QLIN_F16, M, K, qw, sc, qz, N, 128, Yd[li], qlin.QLIN_F16)
+                qlin.qlin_w4_forward(Xd[li], qlin.QLIN_F16, M, K, qw, sc, qz, N, 128, Yd[li], qlin.QLIN_F16,
+                                     workspace=wsp)
 
         def gathered(i):
             for li, (N, K) in enumerate(shapes):
                 qw, sc, qz = sets[i % len(sets)][li]
                 qlin.qlin_w4_forward_perm(Xd[li], qlin.QLIN_F16, M, K, perms[li], Xp[li], qw, sc, qz, N, 128,
-                                          Yd[li], qlin.QLIN_F16)
+                                          Yd[li], qlin.QLIN_F16, workspace=wsp)
         t_nat = graph_step_ms(torch, [natural], len(sets), steps)
         t_gat = graph_step_ms(torch, [gathered], len(sets), steps)
         rec = {"M": M, "static_groups_us": round(t_nat * 1e3, 2), "act_order_gather_us": round(t_gat * 1e3, 2),

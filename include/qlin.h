@@ -20,7 +20,9 @@
  *          equation.
  *
  * Conventions for every call:
- *   - The caller owns every buffer.  Nothing here allocates device memory.
+ *   - The caller owns every buffer, the device workspace of the W4 and int8
+ *     GEMMs included.  Nothing here allocates or frees device memory or
+ *     synchronizes the device.
  *   - *_forward / sq_* device calls take DEVICE pointers and a HIP stream and are
  *     asynchronous: they validate arguments on the host, enqueue kernels on
  *     `stream` and return.  A device-side fault surfaces at the caller's next
@@ -33,8 +35,20 @@
  *   - Errors: every call returns a qlin_status.  Invalid arguments are reported
  *     before anything is enqueued; qlin_last_error() then returns a
  *     thread-local message naming the argument.
- *   - Calls on distinct streams may run concurrently; the library keeps no
- *     state besides the thread-local error message.
+ *   - Calls on distinct streams may run concurrently as long as they do not
+ *     share a workspace.  The library keeps no state besides the thread-local
+ *     error message and a per-device cache of the compute-unit count.
+ *   - Workspace (qlin_w4_forward, qlin_w4_forward_perm, sq_int8_gemm): device
+ *     memory of at least the size the matching *_workspace_bytes call reports
+ *     for the shape (0 means none is needed and NULL may be passed), 16-byte
+ *     aligned.  Its first 16 KiB are arrival counters that must be zero before
+ *     the first call using the workspace (fill the whole buffer with zeros
+ *     once after allocating it); every call leaves them zero again when it
+ *     completes, so one workspace, sized for the largest shape, can serve any
+ *     sequence of calls and shapes on one stream.  Calls sharing a workspace
+ *     must not overlap in time.  Everything else in it is scratch.  A too small
+ *     or NULL workspace where one is needed gives EINVAL, with the needed size
+ *     in qlin_last_error().
  */
 #ifndef QLIN_H
 #define QLIN_H
@@ -88,26 +102,39 @@ qlin_status qlin_w4_sizes(int N, int K, int G,
 qlin_status qlin_w4_pack(const float* W, int N, int K, int G,
                          uint32_t* qweight, uint16_t* scales, uint32_t* qzeros);
 
+/* Device workspace bytes qlin_w4_forward / qlin_w4_forward_perm need for this
+ * shape and these dtypes on the current device (0: none).  Errors as the
+ * forward's shape checks (EINVAL / EUNSUPPORTED), EINVAL for a NULL bytes. */
+qlin_status qlin_w4_workspace_bytes(int x_dtype, int M, int K, int N, int G, int y_dtype, size_t* bytes);
+
 /* Y = X . W_hat^T on the GPU.
  *   X  device, [M][K], x_dtype QLIN_F16 or QLIN_BF16
  *   Y  device, [M][N], y_dtype QLIN_F16, QLIN_BF16 or QLIN_F32
- * Accumulation is fp32.  Small batches (M <= 16, K <= 16384, and the batch's
- * staged activations within 64 KB of LDS) run a fused unpack-dequant GEMV on
- * exact codes.  Otherwise an fp16 MFMA GEMM runs: for G = 128 or 256 on
- * weights S * (q - z) rounded once to fp16, split over the device's compute
- * units (stream-K); for G = 32 or 64 on exact integer codes with a per-group
- * fp32 rescale.  The GEMM computes with fp16 activations: bf16 X must lie in
- * the fp16 range (|x| <= 65504; below 2^-14 the subnormal step limits precision).
- * The stream-K GEMM uses a workspace the library allocates per device on first
- * use of a larger shape and keeps until the process ends; calls that reach it
- * on one device must not run concurrently, and a call that would have to grow
- * it while `stream` is being captured returns EUNSUPPORTED (make one uncaptured
- * call of the largest shape first).
- * Requirements: M, N, K > 0; G % 32 == 0; K % G == 0.  EUNSUPPORTED for other G. */
+ *   workspace / workspace_bytes: see the conventions at the top
+ * Accumulation is fp32.  Kernel by batch size:
+ *   - M <= 3 (up to 16 for G = 32 / 64), K <= 16384, staged activations within
+ *     64 KB of LDS: a fused unpack-dequant GEMV on exact codes, fp16 or bf16
+ *     activations as given;
+ *   - 4 <= M <= 16, G = 128 / 256: a small-batch fp16 MFMA kernel (16 columns
+ *     per workgroup, K split over its waves) on weights S * (q - z) rounded
+ *     once to fp16;
+ *   - larger M, G = 128 / 256: an fp16 MFMA GEMM on the same fp16 weights,
+ *     split over the device's compute units (stream-K, workspace);
+ *   - larger M, G = 32 / 64: an fp16 MFMA GEMM on exact codes q - z with a
+ *     per-group fp32 rescale.
+ * The MFMA paths take fp16 activations.  bf16 X on those paths is first
+ * converted (one extra kernel, workspace) into an fp16 copy in which each row
+ * m is scaled by 2^-e_m so that its largest magnitude lies in [2^14, 2^15);
+ * the outputs of row m are multiplied back by 2^e_m (exact).  Values down to
+ * 2^-31 of their row's maximum keep every bit; smaller ones are rounded to the
+ * fp16 subnormal step (an error of at most 2^-39 of the row maximum).
+ * Requirements: M, N, K > 0; G in {32, 64, 128, 256} (EUNSUPPORTED for other
+ * G); K % G == 0. */
 qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
                             const uint32_t* qweight, const uint16_t* scales,
                             const uint32_t* qzeros, int N, int G,
-                            void* Y, int y_dtype, hipStream_t stream);
+                            void* Y, int y_dtype, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /* Forward of act-order storage (qlin_w4_pack_gptq_actorder without static
  * groups): the stored columns are in quantization order and stored column t is
@@ -120,12 +147,14 @@ qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
  *        range, so a non-permutation gives a meaningless result, never a fault)
  *   Xp   device scratch [M][K] of x_dtype, overwritten, 16-byte aligned, must
  *        not overlap X
- * Other arguments, requirements and errors as qlin_w4_forward (EINVAL for a
- * NULL perm or Xp, or Xp overlapping X). */
+ * Other arguments (the workspace as sized by qlin_w4_workspace_bytes),
+ * requirements and errors as qlin_w4_forward (EINVAL for a NULL perm or Xp,
+ * or Xp overlapping X). */
 qlin_status qlin_w4_forward_perm(const void* X, int x_dtype, int M, int K, const int32_t* perm, void* Xp,
                                  const uint32_t* qweight, const uint16_t* scales,
                                  const uint32_t* qzeros, int N, int G,
-                                 void* Y, int y_dtype, hipStream_t stream);
+                                 void* Y, int y_dtype, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /* Debug: unpack codes (uint8 [N][K]) and zeros (uint8 [N][K/G]) on the GPU with
  * the same unpack routine the forward kernels use. */
@@ -216,17 +245,23 @@ qlin_status sq_pack_weight(const float* W, const float* s, int N, int K,
 qlin_status sq_smooth_quant_act(const uint16_t* X, const float* inv_s, int M, int K,
                                 int8_t* Xq, float* x_scale, hipStream_t stream);
 
+/* Device workspace bytes sq_int8_gemm needs for this shape and output dtype on
+ * the current device (0: none).  Errors as sq_int8_gemm's shape checks, EINVAL
+ * for a NULL bytes. */
+qlin_status sq_int8_gemm_workspace_bytes(int M, int N, int K, int y_dtype, size_t* bytes);
+
 /* GPU: acc[m][n] = sum_k Xq[m][k] * Wq[n][k] (int32, exact);
  * Y[m][n] = y_dtype(float(acc) * x_scale[m] * w_scale[n]).
  * Y device [M][N] with y_dtype QLIN_F16 or QLIN_F32; acc_out, if not NULL,
  * receives acc (int32 [M][N], device).  Requirements: K % 64 == 0, K <= 131072.
- * The K range of a tile may be split over several workgroups (stream-K) through
- * the same per-device workspace as the W4 GEMM, with the same rules: calls on one
- * device must not overlap, and growing it during graph capture is refused. */
+ * Batches of more than 32 tokens (or more than 4 where K % 128 != 0) split the
+ * K range of a tile over several workgroups (stream-K) through the caller's
+ * workspace (conventions at the top); smaller batches need none. */
 qlin_status sq_int8_gemm(const int8_t* Xq, const float* x_scale,
                          const int8_t* Wq, const float* w_scale,
                          int M, int N, int K, void* Y, int y_dtype,
-                         int32_t* acc_out, hipStream_t stream);
+                         int32_t* acc_out, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /* ======================================================================== */
 /* Second-order encoders (host, offline): same storage, same forward calls   */

@@ -25,20 +25,63 @@ qlin_status need_aligned(const char* fn, const char* name, const void* p) {
     if (_s != QLIN_OK) return _s;           \
   } while (0)
 
-// Validation and kernel choice of the W4 forward; with perm != NULL the
-// activations are first gathered into Xp (act-order storage).
-qlin_status w4_forward_checked(const char* fn, const void* X, int x_dtype, int M, int K,
-                               const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int N, int G,
-                               void* Y, int y_dtype, hipStream_t stream, bool gather, const int32_t* perm,
-                               void* Xp) {
+qlin_status need_workspace(const char* fn, const void* ws, size_t ws_bytes, size_t total) {
+  if (total == 0) return QLIN_OK;
+  if (!ws || ws_bytes < total)
+    return fail(QLIN_EINVAL, std::string(fn) + ": this shape needs a workspace of " + std::to_string(total) +
+                                 " bytes (ask the matching *_workspace_bytes call); got " +
+                                 (ws ? std::to_string(ws_bytes) + " bytes" : std::string("NULL")));
+  return need_aligned(fn, "workspace", ws);
+}
+
+// Kernel choice of the W4 forward and the workspace it needs.
+enum class W4Path { kGemv, kSkinny, kSplitK, kGroup };
+
+struct W4Plan {
+  W4Path path = W4Path::kGemv;
+  bool prep = false;           // bf16 X converted to a row-scaled fp16 copy first
+  size_t prep_off = 0;         // offset of that copy in the workspace
+  size_t total = 0;            // workspace bytes (0: none)
+};
+
+qlin_status w4_plan(const W4Args& a, W4Plan* p) {
+  // M = 1 (and M <= 3 while the activations fit its LDS staging): the GEMV;
+  // M = 4 .. 16: the small-batch MFMA kernel; larger: the GEMMs.
+  if (w4_gemv_supported(a.M, a.K, a.G) && (a.M <= 3 || !w4_skinny_supported(a.M, a.K, a.G))) p->path = W4Path::kGemv;
+  else if (w4_skinny_supported(a.M, a.K, a.G)) p->path = W4Path::kSkinny;
+  else if (a.G >= 128) p->path = W4Path::kSplitK;
+  else p->path = W4Path::kGroup;
+  p->prep = a.x_dtype == QLIN_BF16 && p->path != W4Path::kGemv;
+  size_t partial = 0;
+  if (p->path == W4Path::kSplitK) QLIN_TRY(w4_gemm_sk_launch(a, WsView{}, &partial, nullptr));
+  if (p->path != W4Path::kSplitK && !p->prep) {
+    p->total = 0;
+    return QLIN_OK;
+  }
+  p->prep_off = kCounterBytes + ws_round(partial);
+  p->total = p->prep_off;
+  if (p->prep) p->total += ws_round(static_cast<size_t>(a.M) * a.K * 2) + ws_round(static_cast<size_t>(a.M) * 4);
+  return QLIN_OK;
+}
+
+qlin_status w4_check_shape(const char* fn, int x_dtype, int M, int K, int N, int G, int y_dtype) {
   if (M <= 0 || N <= 0 || K <= 0 || G <= 0) return fail(QLIN_EINVAL, std::string(fn) + ": M, N, K, G must be positive");
-  if (!X || !qweight || !scales || !qzeros || !Y) return fail(QLIN_EINVAL, std::string(fn) + ": NULL pointer");
   if (x_dtype != QLIN_F16 && x_dtype != QLIN_BF16) return fail(QLIN_EINVAL, std::string(fn) + ": x_dtype must be F16 or BF16");
   if (!is_out_dtype(y_dtype)) return fail(QLIN_EINVAL, std::string(fn) + ": y_dtype must be F16, BF16 or F32");
   if (K % G != 0) return fail(QLIN_EINVAL, std::string(fn) + ": K must be a multiple of G");
-  if (G % 32 != 0 || G > 256) return fail(QLIN_EUNSUPPORTED, std::string(fn) + ": G must be 32, 64, 128 or 256 (multiple of 32, at most 256)");
   if (G != 32 && G != 64 && G != 128 && G != 256)
     return fail(QLIN_EUNSUPPORTED, std::string(fn) + ": G must be 32, 64, 128 or 256");
+  return QLIN_OK;
+}
+
+// Validation and kernel choice of the W4 forward; with gather the activations
+// are first gathered through perm into Xp (act-order storage).
+qlin_status w4_forward_checked(const char* fn, const void* X, int x_dtype, int M, int K,
+                               const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int N, int G,
+                               void* Y, int y_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                               bool gather, const int32_t* perm, void* Xp) {
+  QLIN_TRY(w4_check_shape(fn, x_dtype, M, K, N, G, y_dtype));
+  if (!X || !qweight || !scales || !qzeros || !Y) return fail(QLIN_EINVAL, std::string(fn) + ": NULL pointer");
   QLIN_TRY(need_aligned(fn, "X", X));
   QLIN_TRY(need_aligned(fn, "qweight", qweight));
   QLIN_TRY(need_aligned(fn, "scales", scales));
@@ -51,44 +94,82 @@ qlin_status w4_forward_checked(const char* fn, const void* X, int x_dtype, int M
     const char* p0 = static_cast<const char*>(Xp);
     const size_t bytes = static_cast<size_t>(M) * K * 2;
     if (p0 < x0 + bytes && x0 < p0 + bytes) return fail(QLIN_EINVAL, std::string(fn) + ": Xp overlaps X");
-    permute_cols_launch(X, perm, M, K, Xp, stream);
-    X = Xp;
   }
-  W4Args a{X, x_dtype, M, K, N, G, qweight, scales, qzeros, Y, y_dtype};
-  // M = 1 (and M <= 3 while the activations fit its LDS staging): the GEMV;
-  // M = 4 .. 16: the small-batch MFMA kernel; larger: the GEMMs.
-  if (w4_gemv_supported(M, K, G) && (M <= 3 || !w4_skinny_supported(M, K, G))) {
-    w4_gemv_launch(a, stream);
-  } else if (w4_skinny_supported(M, K, G)) {
-    w4_skinny_launch(a, stream);
-  } else if (G >= 128) {
-    QLIN_TRY(w4_gemm_sk_launch(a, stream));
-  } else {
-    w4_gemm_launch(a, stream);
+  W4Args a{X, x_dtype, M, K, N, G, qweight, scales, qzeros, Y, y_dtype, nullptr};
+  W4Plan plan;
+  QLIN_TRY(w4_plan(a, &plan));
+  QLIN_TRY(need_workspace(fn, workspace, workspace_bytes, plan.total));
+  const WsView ws{static_cast<char*>(workspace), workspace_bytes};
+  if (gather) {
+    permute_cols_launch(X, perm, M, K, Xp, stream);
+    a.X = Xp;
+  }
+  if (plan.prep) {
+    uint16_t* xh = reinterpret_cast<uint16_t*>(ws.base + plan.prep_off);
+    int* rowexp = reinterpret_cast<int*>(ws.base + plan.prep_off + ws_round(static_cast<size_t>(M) * K * 2));
+    x_rowscale_launch(static_cast<const uint16_t*>(a.X), M, K, xh, rowexp, stream);
+    a.X = xh;
+    a.x_dtype = QLIN_F16;
+    a.rowexp = rowexp;
+  }
+  switch (plan.path) {
+    case W4Path::kGemv: w4_gemv_launch(a, stream); break;
+    case W4Path::kSkinny: w4_skinny_launch(a, stream); break;
+    case W4Path::kSplitK: QLIN_TRY(w4_gemm_sk_launch(a, ws, nullptr, stream)); break;
+    case W4Path::kGroup: w4_gemm_group_launch(a, stream); break;
   }
   return check_launch(fn);
+}
+
+qlin_status sq_check(const char* fn, int M, int N, int K, int y_dtype) {
+  if (M <= 0 || N <= 0 || K <= 0) return fail(QLIN_EINVAL, std::string(fn) + ": M, N, K must be positive");
+  if (K % 64 != 0) return fail(QLIN_EINVAL, std::string(fn) + ": K must be a multiple of 64");
+  if (K > 131072) return fail(QLIN_EUNSUPPORTED, std::string(fn) + ": K above 131072 could overflow int32");
+  if (y_dtype != QLIN_F16 && y_dtype != QLIN_F32) return fail(QLIN_EINVAL, std::string(fn) + ": y_dtype must be F16 or F32");
+  return QLIN_OK;
+}
+
+qlin_status sq_workspace_total(int M, int N, int K, int y_dtype, size_t* total) {
+  size_t partial = 0;
+  QLIN_TRY(sq_gemm_launch(nullptr, nullptr, nullptr, nullptr, M, N, K, nullptr, y_dtype, nullptr, WsView{}, &partial,
+                          nullptr));
+  // a kernel with a K split needs the counters even when its plan splits no tile
+  *total = partial ? kCounterBytes + ws_round(partial) : 0;
+  return QLIN_OK;
 }
 
 }  // namespace
 
 extern "C" {
 
+qlin_status qlin_w4_workspace_bytes(int x_dtype, int M, int K, int N, int G, int y_dtype, size_t* bytes) {
+  static const char* fn = "qlin_w4_workspace_bytes";
+  clear_error();
+  if (!bytes) return fail(QLIN_EINVAL, std::string(fn) + ": NULL bytes");
+  QLIN_TRY(w4_check_shape(fn, x_dtype, M, K, N, G, y_dtype));
+  W4Args a{nullptr, x_dtype, M, K, N, G, nullptr, nullptr, nullptr, nullptr, y_dtype, nullptr};
+  W4Plan plan;
+  QLIN_TRY(w4_plan(a, &plan));
+  *bytes = plan.total;
+  return QLIN_OK;
+}
+
 qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
                             const uint32_t* qweight, const uint16_t* scales,
                             const uint32_t* qzeros, int N, int G,
-                            void* Y, int y_dtype, hipStream_t stream) {
+                            void* Y, int y_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   clear_error();
-  return w4_forward_checked("qlin_w4_forward", X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype, stream,
-                            false, nullptr, nullptr);
+  return w4_forward_checked("qlin_w4_forward", X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype,
+                            workspace, workspace_bytes, stream, false, nullptr, nullptr);
 }
 
 qlin_status qlin_w4_forward_perm(const void* X, int x_dtype, int M, int K, const int32_t* perm, void* Xp,
                                  const uint32_t* qweight, const uint16_t* scales,
                                  const uint32_t* qzeros, int N, int G,
-                                 void* Y, int y_dtype, hipStream_t stream) {
+                                 void* Y, int y_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   clear_error();
   return w4_forward_checked("qlin_w4_forward_perm", X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype,
-                            stream, true, perm, Xp);
+                            workspace, workspace_bytes, stream, true, perm, Xp);
 }
 
 qlin_status qlin_w4_unpack(const uint32_t* qweight, const uint32_t* qzeros, int N, int K, int G,
@@ -148,20 +229,30 @@ qlin_status sq_smooth_quant_act(const uint16_t* X, const float* inv_s, int M, in
   return check_launch(fn);
 }
 
+qlin_status sq_int8_gemm_workspace_bytes(int M, int N, int K, int y_dtype, size_t* bytes) {
+  static const char* fn = "sq_int8_gemm_workspace_bytes";
+  clear_error();
+  if (!bytes) return fail(QLIN_EINVAL, std::string(fn) + ": NULL bytes");
+  QLIN_TRY(sq_check(fn, M, N, K, y_dtype));
+  return sq_workspace_total(M, N, K, y_dtype, bytes);
+}
+
 qlin_status sq_int8_gemm(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
-                         int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
+                         int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
   static const char* fn = "sq_int8_gemm";
   clear_error();
-  if (M <= 0 || N <= 0 || K <= 0) return fail(QLIN_EINVAL, std::string(fn) + ": M, N, K must be positive");
-  if (K % 64 != 0) return fail(QLIN_EINVAL, std::string(fn) + ": K must be a multiple of 64");
-  if (K > 131072) return fail(QLIN_EUNSUPPORTED, std::string(fn) + ": K above 131072 could overflow int32");
+  QLIN_TRY(sq_check(fn, M, N, K, y_dtype));
   if (!Xq || !x_scale || !Wq || !w_scale || !Y) return fail(QLIN_EINVAL, std::string(fn) + ": NULL pointer");
-  if (y_dtype != QLIN_F16 && y_dtype != QLIN_F32) return fail(QLIN_EINVAL, std::string(fn) + ": y_dtype must be F16 or F32");
   QLIN_TRY(need_aligned(fn, "Xq", Xq));
   QLIN_TRY(need_aligned(fn, "Wq", Wq));
   QLIN_TRY(need_aligned(fn, "Y", Y));
   if (acc_out) QLIN_TRY(need_aligned(fn, "acc_out", acc_out));
-  QLIN_TRY(sq_gemm_launch(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream));
+  size_t total = 0;
+  QLIN_TRY(sq_workspace_total(M, N, K, y_dtype, &total));
+  QLIN_TRY(need_workspace(fn, workspace, workspace_bytes, total));
+  QLIN_TRY(sq_gemm_launch(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out,
+                          WsView{static_cast<char*>(workspace), workspace_bytes}, nullptr, stream));
   return check_launch(fn);
 }
 

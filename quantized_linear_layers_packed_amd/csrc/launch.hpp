@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "../../include/qlin.h"
+#include "workspace.hpp"
 
 namespace qlin {
 
@@ -19,16 +20,22 @@ struct W4Args {
   const uint32_t* qzeros;
   void* Y;
   int y_dtype;
+  const int* rowexp;   // non-NULL: X is a row-scaled fp16 copy of bf16 input, row m scaled by 2^-rowexp[m]
 };
 
 // Fused GEMV for M <= 16 (activations staged in LDS).
 size_t w4_gemv_lds_bytes(int M, int K);
 bool w4_gemv_supported(int M, int K, int G);
 void w4_gemv_launch(const W4Args& a, hipStream_t stream);
-// MFMA GEMM for larger batches: stream-K kernel for groups of 128 / 256
-// (uses the library workspace), one-group-per-step kernel for 32 / 64.
-qlin_status w4_gemm_sk_launch(const W4Args& a, hipStream_t stream);
-void w4_gemm_launch(const W4Args& a, hipStream_t stream);
+// MFMA GEMM for larger batches, groups of 128 / 256: stream-K over the
+// caller's workspace.  With need != NULL only the partial-tile bytes it needs
+// are reported (nothing is launched).
+qlin_status w4_gemm_sk_launch(const W4Args& a, WsView ws, size_t* need, hipStream_t stream);
+// Groups of 32 / 64: one K step per group, exact codes and an fp32 rescale.
+void w4_gemm_group_launch(const W4Args& a, hipStream_t stream);
+// bf16 X [M][K] -> fp16 Xh = X * 2^-e_m per row (round to nearest even) and
+// e_m (int32 [M]) with the row maximum scaled into [2^14, 2^15).
+void x_rowscale_launch(const uint16_t* X, int M, int K, uint16_t* Xh, int* rowexp, hipStream_t stream);
 // Small batches (M <= 16, G = 128 / 256): 16 columns per workgroup, K split
 // over its waves, fp16 MFMA, no workspace.
 bool w4_skinny_supported(int M, int K, int G);
@@ -57,7 +64,10 @@ void spqr_unpack_launch(const uint32_t* codes, const uint32_t* stats1, int N, in
 
 void sq_act_launch(const uint16_t* X, const float* inv_s, int M, int K, int8_t* Xq, float* x_scale,
                    hipStream_t stream);
+// With need != NULL only the workspace bytes beyond the counters are reported
+// (0 if the kernel chosen needs none); nothing is launched.
 qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
-                           int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream);
+                           int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, WsView ws, size_t* need,
+                           hipStream_t stream);
 
 }  // namespace qlin

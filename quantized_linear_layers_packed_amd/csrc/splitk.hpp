@@ -33,13 +33,17 @@ __device__ __forceinline__ int sk_owner(const SkPlan& s, long long u) {
   return static_cast<int>(((u + 1) * s.P + s.units - 1) / s.units) - 1;
 }
 
-// Partial tiles cross XCDs, whose L2 caches are not coherent with each other.
-// Device-scope fences would write back and invalidate the whole L2 of the
-// issuing XCD (and so every other workgroup's cached operands) at each hand-off;
-// instead the partials are written and read with device-coherent accesses
-// (performed at the device coherence point, bypassing the non-coherent caches),
-// the writer drains its stores before the workgroup barrier, and the arrival
-// counter is a relaxed device-scope atomic issued after that barrier.
+// Hand-off of a shared tile.  Partial tiles cross XCDs, whose L2 caches are
+// not coherent with each other, so the partials are written and read with
+// device-scope (agent) atomic accesses, which are performed at the device
+// coherence point rather than in an XCD's L2.  Each contributor drains its own
+// stores (s_waitcnt vmcnt(0)) before the workgroup barrier; thread 0 then bumps
+// the tile's arrival counter with a device-scope RELEASE read-modify-write, and
+// the workgroup that sees the final count runs a device-scope ACQUIRE fence
+// before it reads the partials.  Release/acquire on the counter is what the
+// HIP memory model needs for the partials to be visible; on gfx950 it costs
+// one write-back of the issuing XCD's L2 per arrival and one L2 invalidate per
+// finished shared tile (at most one per workgroup).
 __device__ __forceinline__ void sk_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -53,11 +57,34 @@ __device__ __forceinline__ int sk_load(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void sk_drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ int sk_arrive(int* counter) {
-  return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+// Every thread of the workgroup calls this after storing its part of the
+// partial tile.  Returns true (in every thread) for the workgroup that arrives
+// last, i.e. sees `prior` earlier arrivals; that workgroup has run the acquire
+// fence and may read the other partials.  s_flag: a __shared__ int.
+__device__ __forceinline__ bool sk_arrive_last(int* counter, int prior, int* s_flag) {
+  sk_drain_stores();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == prior;
+  __syncthreads();
+  const bool last = *s_flag != 0;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
 }
+
+// The last arriver returns the counter to zero once it has read the partials
+// (the next use is a later kernel, ordered by the kernel boundary).
 __device__ __forceinline__ void sk_reset(int* counter) {
   __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Counter of a shared tile: indexed by the tile's first contributor.  A
+// workgroup can be the first contributor of several tiles only when its range
+// covers the earlier ones entirely, so at most one shared tile per workgroup:
+// P counters suffice whatever the tile count.
+__device__ __forceinline__ int sk_counter_index(const SkPlan& s, int t) {
+  return sk_owner(s, static_cast<long long>(t) * s.ksteps);
 }
 
 // Workspace slot holding workgroup q's partial of tile t.

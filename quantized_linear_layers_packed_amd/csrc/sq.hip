@@ -454,11 +454,7 @@ __global__ __launch_bounds__(kGemmThreads) void sq_gemm_sk_kernel(
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sk_store(mine + ((wv * TM + i) * 16 + r) * 64 + lane, acc[i][r]);
-      sk_drain_stores();
-      __syncthreads();
-      if (tid == 0) s_last = sk_arrive(&counters[t]) == last - first;
-      __syncthreads();
-      write = s_last != 0;
+      write = sk_arrive_last(&counters[first], last - first, &s_last);
       if (write) {
         for (int q = first; q <= last; ++q) {
           if (q == p) continue;
@@ -473,7 +469,7 @@ __global__ __launch_bounds__(kGemmThreads) void sq_gemm_sk_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][r] += part[i][r];
         }
-        if (tid == 0) sk_reset(&counters[t]);
+        if (tid == 0) sk_reset(&counters[first]);
       }
     }
     if (write && nok) {
@@ -621,11 +617,7 @@ void sq_gemm_big_kernel(const int8_t* __restrict__ Xq, const float* __restrict__
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             sk_store(mine + (((wv * TM + i) * TN + j) * 16 + r) * 64 + lane, acc[i][j][r]);
-      sk_drain_stores();
-      __syncthreads();
-      if (tid == 0) s_last = sk_arrive(&counters[t]) == last - first;
-      __syncthreads();
-      write = s_last != 0;
+      write = sk_arrive_last(&counters[first], last - first, &s_last);
       if (write) {
         for (int q = first; q <= last; ++q) {
           if (q == p) continue;
@@ -641,7 +633,7 @@ void sq_gemm_big_kernel(const int8_t* __restrict__ Xq, const float* __restrict__
               for (int r = 0; r < 16; ++r) acc[i][j][r] += part[r];
             }
         }
-        if (tid == 0) sk_reset(&counters[t]);
+        if (tid == 0) sk_reset(&counters[first]);
       }
     }
     if (write) {
@@ -674,7 +666,7 @@ void sq_gemm_big_kernel(const int8_t* __restrict__ Xq, const float* __restrict__
 
 template <int TM, int NS, int OUTK>
 qlin_status gemm_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
-                   void* Y, int32_t* acc_out, hipStream_t stream) {
+                   void* Y, int32_t* acc_out, WsView ws, size_t* need, hipStream_t stream) {
   constexpr int BM = 32 * TM;
   constexpr size_t lds = static_cast<size_t>(NS) * (BM + kBN) * 8 * sizeof(uint4);
   // resident workgroups per CU, queried once per process (thread-safe
@@ -694,19 +686,23 @@ qlin_status gemm_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const f
   SkPlan plan;
   plan.ksteps = (K + kBK - 1) / kBK;
   plan.units = tiles * plan.ksteps;
-  plan.P = static_cast<int>(std::min<long long>(static_cast<long long>(occ) * device_cus(), plan.units));
-  Workspace w;
-  const qlin_status s = get_workspace(static_cast<size_t>(2) * plan.P * BM * kBN * sizeof(int),
-                                      static_cast<size_t>(tiles), stream, "sq_int8_gemm", &w);
-  if (s != QLIN_OK) return s;
+  plan.P = static_cast<int>(std::min<long long>(
+      std::min<long long>(static_cast<long long>(occ) * device_cus(), kCounterSlots), plan.units));
+  const size_t partial_bytes = static_cast<size_t>(2) * plan.P * BM * kBN * sizeof(int);
+  if (need) {
+    *need = partial_bytes;
+    return QLIN_OK;
+  }
+  if (ws.bytes < kCounterBytes + partial_bytes)
+    return fail(QLIN_EINVAL, "sq_int8_gemm: workspace too small for the split-K GEMM");
   hipLaunchKernelGGL((sq_gemm_sk_kernel<TM, NS, OUTK>), dim3(plan.P), dim3(kGemmThreads), lds, stream, Xq, xsc, Wq,
-                     wsc, M, N, K, tiles_n, plan, Y, acc_out, reinterpret_cast<int*>(w.partials), w.counters);
+                     wsc, M, N, K, tiles_n, plan, Y, acc_out, static_cast<int*>(ws.partials()), ws.counters());
   return QLIN_OK;
 }
 
 template <int WM, int WN, int TM, int TN, int BK, int NS, int OUTK>
 qlin_status gemm_big_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
-                       void* Y, int32_t* acc_out, hipStream_t stream) {
+                       void* Y, int32_t* acc_out, WsView ws, size_t* need, hipStream_t stream) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN, threads = 64 * WM * WN;
   constexpr size_t lds = static_cast<size_t>(NS) * (BM + BN) * BK;
   static_assert(lds + 16 <= 160 * 1024, "LDS ring within the 160 KB of a CU");
@@ -726,30 +722,34 @@ qlin_status gemm_big_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, con
   SkPlan plan;
   plan.ksteps = K / BK;
   plan.units = tiles * plan.ksteps;
-  plan.P = static_cast<int>(std::min<long long>(static_cast<long long>(occ) * device_cus(), plan.units));
-  Workspace w;
-  const qlin_status s = get_workspace(static_cast<size_t>(2) * plan.P * BM * BN * sizeof(int),
-                                      static_cast<size_t>(tiles), stream, "sq_int8_gemm", &w);
-  if (s != QLIN_OK) return s;
+  plan.P = static_cast<int>(std::min<long long>(
+      std::min<long long>(static_cast<long long>(occ) * device_cus(), kCounterSlots), plan.units));
+  const size_t partial_bytes = static_cast<size_t>(2) * plan.P * BM * BN * sizeof(int);
+  if (need) {
+    *need = partial_bytes;
+    return QLIN_OK;
+  }
+  if (ws.bytes < kCounterBytes + partial_bytes)
+    return fail(QLIN_EINVAL, "sq_int8_gemm: workspace too small for the split-K GEMM");
   hipLaunchKernelGGL((sq_gemm_big_kernel<WM, WN, TM, TN, BK, NS, OUTK>), dim3(plan.P), dim3(threads), lds, stream,
-                     Xq, xsc, Wq, wsc, M, N, K, tiles_m, plan, Y, acc_out, reinterpret_cast<int*>(w.partials),
-                     w.counters);
+                     Xq, xsc, Wq, wsc, M, N, K, tiles_m, plan, Y, acc_out, static_cast<int*>(ws.partials()),
+                     ws.counters());
   return QLIN_OK;
 }
 
 template <int WM, int WN, int TM, int TN, int BK, int NS>
 qlin_status gemm_big_o(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
-                       void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
+                       void* Y, int y_dtype, int32_t* acc_out, WsView ws, size_t* need, hipStream_t stream) {
   return y_dtype == QLIN_F32
-             ? gemm_big_t<WM, WN, TM, TN, BK, NS, OUT_F32>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream)
-             : gemm_big_t<WM, WN, TM, TN, BK, NS, OUT_F16>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+             ? gemm_big_t<WM, WN, TM, TN, BK, NS, OUT_F32>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, ws, need, stream)
+             : gemm_big_t<WM, WN, TM, TN, BK, NS, OUT_F16>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, ws, need, stream);
 }
 
 template <int TM, int NS>
 qlin_status gemm_o(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
-                   void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
-  return y_dtype == QLIN_F32 ? gemm_t<TM, NS, OUT_F32>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream)
-                             : gemm_t<TM, NS, OUT_F16>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, stream);
+                   void* Y, int y_dtype, int32_t* acc_out, WsView ws, size_t* need, hipStream_t stream) {
+  return y_dtype == QLIN_F32 ? gemm_t<TM, NS, OUT_F32>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, ws, need, stream)
+                             : gemm_t<TM, NS, OUT_F16>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, ws, need, stream);
 }
 
 }  // namespace
@@ -760,7 +760,8 @@ void sq_act_launch(const uint16_t* X, const float* inv_s, int M, int K, int8_t* 
 }
 
 qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
-                           int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, hipStream_t stream) {
+                           int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, WsView ws, size_t* need,
+                           hipStream_t stream) {
   // Up to 2 tokens (rows up to 32768): the GEMV, bound by the weight stream;
   // then up to 32 tokens (K a multiple of 128) the small-batch MFMA kernel.
   // Larger batches (K a multiple of 128): eight waves, two per SIMD.  Above 64
@@ -771,12 +772,15 @@ qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t*
   // 64 tokens a 2 x 4 grid of 32 x 32 wave tiles (64 x 128).  Batches of at most
   // 32 use the 32 TM x 128 kernel, whose ring depth stays within 160 KB of LDS:
   // stage = (32 TM + 128) rows x 128 bytes.
+  if (need) *need = 0;                 // the kernels without a K split need no workspace
   if (M <= 2 && K <= 32768) {
+    if (need) return QLIN_OK;
     if (M == 1) gemv_o<1>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
     else gemv_o<2>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
     return QLIN_OK;
   }
   if (M <= 32 && K % 128 == 0) {
+    if (need) return QLIN_OK;
     // small batches: 16-column tiles, 4, 2 or 1 per workgroup while at least
     // 300 workgroups remain (with two 16-token tiles: 2 while at least 160)
     const long long wg4 = (N + 63) / 64, wg2 = (N + 31) / 32;
@@ -791,22 +795,23 @@ qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t*
     return QLIN_OK;
   }
   if (M <= 4 && K <= 32768) {          // K not a multiple of 128
+    if (need) return QLIN_OK;
     gemv_o<4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
     return QLIN_OK;
   }
   if (M > 32 && M <= 64 && K % 128 == 0)
-    return gemm_big_o<2, 4, 1, 1, 128, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+    return gemm_big_o<2, 4, 1, 1, 128, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, ws, need, stream);
   if (M > 64 && K % 128 == 0) {
     auto tiles = [&](int bm, int bn) { return static_cast<long long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 128) >= 160)
-      return gemm_big_o<4, 2, 2, 2, 128, 3>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+      return gemm_big_o<4, 2, 2, 2, 128, 3>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, ws, need, stream);
     if (tiles(128, 128) >= 160)
-      return gemm_big_o<4, 2, 1, 2, 128, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-    return gemm_big_o<4, 2, 1, 1, 128, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+      return gemm_big_o<4, 2, 1, 2, 128, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, ws, need, stream);
+    return gemm_big_o<4, 2, 1, 1, 128, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, ws, need, stream);
   }
-  if (M <= 32) return gemm_o<1, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-  if (M <= 64) return gemm_o<2, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
-  return gemm_o<4, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, stream);
+  if (M <= 32) return gemm_o<1, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, ws, need, stream);
+  if (M <= 64) return gemm_o<2, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, ws, need, stream);
+  return gemm_o<4, 4>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, ws, need, stream);
 }
 
 }  // namespace qlin

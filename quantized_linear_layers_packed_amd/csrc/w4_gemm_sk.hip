@@ -16,10 +16,11 @@
 //     1024.0, one packed fp16 subtraction removes 1024 + z (exact) and one packed
 //     multiply by the group's fp16 scale rounds the weight once to fp16, as the
 //     GPTQ kernels do, so the matrix cores accumulate across groups directly;
-//   * A operand: the activation tile of one 128-wide K step, converted to fp16
-//     (bf16 inputs exactly, for values in the fp16 normal range) and stored in
-//     LDS as 256-byte rows whose 16-byte chunks are XOR-swizzled by the row, so
-//     the 32 rows an MFMA reads land in distinct banks; double buffered;
+//   * A operand: the fp16 activation tile of one 128-wide K step (bf16 inputs
+//     arrive as a row-scaled fp16 copy whose per-row power of two the epilogue
+//     puts back), stored in LDS as 256-byte rows whose 16-byte chunks are
+//     XOR-swizzled by the row, so the 32 rows an MFMA reads land in distinct
+//     banks; double buffered;
 //   * packed words, the group scale/zero and the activations are fetched R - 1
 //     K steps ahead into R-deep register rings (every load unconditional, so the
 //     compiler's in-order wait counts never drain the rings): with a few waves
@@ -60,17 +61,11 @@ __device__ __forceinline__ h8_t dequant_nat(uint32_t w, h2_t zz, h2_t ss) {
   return b;
 }
 
-// Two bf16 values -> two fp16 values (exact in the fp16 normal range).
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
-  const float lo = bitcast<float>(u << 16);
-  const float hi = bitcast<float>(u & 0xFFFF0000u);
-  return bitcast<uint32_t>(__builtin_amdgcn_cvt_pkrtz(lo, hi));
-}
-
-template <int TM, int NW, int R, int RV, bool XBF16, int OUTK>
+template <int TM, int NW, int R, int RV, int OUTK>
 __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
     const uint16_t* X, int M, int K, const uint32_t* qweight, const uint16_t* scales,
-    const uint32_t* qzeros, int N, int gsh, int tiles_n, SkPlan plan, void* Y, float* ws, int* counters) {
+    const uint32_t* qzeros, int N, int gsh, int tiles_n, SkPlan plan, void* Y, const int* rowexp, float* ws,
+    int* counters) {
   // (no __restrict__: with it the prefetch loads count as invariant and get sunk
   // across the step barriers to their first use, which defeats the prefetch)
   constexpr int kThreads = 64 * NW;           // NW waves side by side along N
@@ -127,14 +122,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
       for (int j = 0; j < APT; ++j) {
         const int piece = tid + j * kThreads;
         const int r = piece >> 4, c = piece & 15;
-        uint4 v = src[j];
-        if constexpr (XBF16) {
-          v.x = bf16x2_to_f16x2(v.x);
-          v.y = bf16x2_to_f16x2(v.y);
-          v.z = bf16x2_to_f16x2(v.z);
-          v.w = bf16x2_to_f16x2(v.w);
-        }
-        dst[r * 16 + (c ^ (r & 15))] = v;
+        dst[r * 16 + (c ^ (r & 15))] = src[j];
       }
     };
     uint4 bq[R][2];                            // weight ring: step k0 + j in set j % R
@@ -215,11 +203,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < RV; ++r) sk_store(mine + ((wv * TM + i) * 16 + r) * 64 + lane, acc[i][r]);
-      sk_drain_stores();
-      __syncthreads();
-      if (tid == 0) s_last = sk_arrive(&counters[t]) == last - first;
-      __syncthreads();
-      write = s_last != 0;
+      write = sk_arrive_last(&counters[first], last - first, &s_last);
       if (write) {
         // K-order sum of every contributor's stored partial (this workgroup's
         // included), QC partials per batch with all their loads in flight at
@@ -247,7 +231,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
           }
           acc[i] = tot;
         }
-        if (tid == 0) sk_reset(&counters[t]);
+        if (tid == 0) sk_reset(&counters[first]);
       }
     }
     if (write && nok) {
@@ -256,22 +240,22 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, acc[i][r]);
+          if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, row_scaled(acc[i][r], rowexp, m));
         }
     }
     u += k1 - k0;
   }
 }
 
-template <int TM, int NW, int R, int RV, bool XBF16, int OUTK>
-qlin_status launch_sk(const W4Args& a, hipStream_t stream) {
+template <int TM, int NW, int R, int RV, int OUTK>
+qlin_status launch_sk(const W4Args& a, WsView ws, size_t* need, hipStream_t stream) {
   constexpr int BM = 32 * TM, BN = 32 * NW;
   constexpr size_t lds = static_cast<size_t>(2) * BM * 16 * sizeof(uint4);
   // resident workgroups per CU (register / LDS bound), queried once per
   // process (thread-safe initialisation of a function-local static)
   static const int occ = [] {
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, w4_gemm_sk_kernel<TM, NW, R, RV, XBF16, OUTK>, 64 * NW, lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, w4_gemm_sk_kernel<TM, NW, R, RV, OUTK>, 64 * NW, lds) !=
             hipSuccess || o <= 0)
       o = 1;
     return std::min(o, 2);
@@ -282,41 +266,39 @@ qlin_status launch_sk(const W4Args& a, hipStream_t stream) {
   SkPlan plan;
   plan.ksteps = a.K / kKS;
   plan.units = tiles * plan.ksteps;
-  plan.P = static_cast<int>(std::min<long long>(static_cast<long long>(occ) * device_cus(), plan.units));
-  Workspace w;
-  const qlin_status s = get_workspace(static_cast<size_t>(2) * plan.P * BM * BN * sizeof(float),
-                                      static_cast<size_t>(tiles), stream, "qlin_w4_forward", &w);
-  if (s != QLIN_OK) return s;
+  plan.P = static_cast<int>(std::min<long long>(
+      std::min<long long>(static_cast<long long>(occ) * device_cus(), kCounterSlots), plan.units));
+  const size_t partial_bytes = static_cast<size_t>(2) * plan.P * BM * BN * sizeof(float);
+  if (need) {
+    *need = partial_bytes;
+    return QLIN_OK;
+  }
+  if (ws.bytes < kCounterBytes + partial_bytes)
+    return fail(QLIN_EINVAL, "qlin_w4_forward: workspace too small for the split-K GEMM");
   const int gsh = a.G == 256 ? 1 : 0;
-  hipLaunchKernelGGL((w4_gemm_sk_kernel<TM, NW, R, RV, XBF16, OUTK>), dim3(plan.P), dim3(64 * NW), lds, stream,
+  hipLaunchKernelGGL((w4_gemm_sk_kernel<TM, NW, R, RV, OUTK>), dim3(plan.P), dim3(64 * NW), lds, stream,
                      static_cast<const uint16_t*>(a.X), a.M, a.K, a.qweight, a.scales, a.qzeros, a.N, gsh, tiles_n,
-                     plan, a.Y, w.partials, w.counters);
+                     plan, a.Y, a.rowexp, static_cast<float*>(ws.partials()), ws.counters());
   return QLIN_OK;
 }
 
-template <int TM, int NW, int R, int RV, bool XBF16>
-qlin_status launch_o(const W4Args& a, hipStream_t stream) {
-  if (a.y_dtype == QLIN_F16) return launch_sk<TM, NW, R, RV, XBF16, OUT_F16>(a, stream);
-  if (a.y_dtype == QLIN_BF16) return launch_sk<TM, NW, R, RV, XBF16, OUT_BF16>(a, stream);
-  return launch_sk<TM, NW, R, RV, XBF16, OUT_F32>(a, stream);
-}
-
 template <int TM, int NW, int R, int RV>
-qlin_status launch_x(const W4Args& a, hipStream_t stream) {
-  return a.x_dtype == QLIN_BF16 ? launch_o<TM, NW, R, RV, true>(a, stream)
-                                : launch_o<TM, NW, R, RV, false>(a, stream);
+qlin_status launch_o(const W4Args& a, WsView ws, size_t* need, hipStream_t stream) {
+  if (a.y_dtype == QLIN_F16) return launch_sk<TM, NW, R, RV, OUT_F16>(a, ws, need, stream);
+  if (a.y_dtype == QLIN_BF16) return launch_sk<TM, NW, R, RV, OUT_BF16>(a, ws, need, stream);
+  return launch_sk<TM, NW, R, RV, OUT_F32>(a, ws, need, stream);
 }
 
 }  // namespace
 
-qlin_status w4_gemm_sk_launch(const W4Args& a, hipStream_t stream) {
+qlin_status w4_gemm_sk_launch(const W4Args& a, WsView ws, size_t* need, hipStream_t stream) {
   // RV: accumulator registers per 32-row block that can hold rows below M
   // (register r holds rows 8 (r / 4) + 4 h + r % 4, h the lane half)
-  if (a.M <= 8) return launch_x<1, 8, 6, 4>(a, stream);
-  if (a.M <= 16) return launch_x<1, 8, 6, 8>(a, stream);
-  if (a.M <= 32) return launch_x<1, 8, 6, 16>(a, stream);
-  if (a.M <= 64) return launch_x<2, 8, 4, 16>(a, stream);
-  return launch_x<4, 8, 3, 16>(a, stream);
+  if (a.M <= 8) return launch_o<1, 8, 6, 4>(a, ws, need, stream);
+  if (a.M <= 16) return launch_o<1, 8, 6, 8>(a, ws, need, stream);
+  if (a.M <= 32) return launch_o<1, 8, 6, 16>(a, ws, need, stream);
+  if (a.M <= 64) return launch_o<2, 8, 4, 16>(a, ws, need, stream);
+  return launch_o<4, 8, 3, 16>(a, ws, need, stream);
 }
 
 }  // namespace qlin

@@ -19,8 +19,9 @@
 //   * B operand: per K block a lane loads one 16-byte piece (4 packed words of
 //     its column) and turns each word into 8 fp16 weights s * (q - z) (q - z
 //     exact, one rounding of the product), one word per matrix instruction;
-//   * A operand: straight from global memory into registers (16 bytes = 8
-//     consecutive k per lane and instruction; rows past M re-read row M - 1);
+//   * A operand: fp16 straight from global memory into registers (16 bytes =
+//     8 consecutive k per lane and instruction; rows past M re-read row M - 1);
+//     bf16 inputs arrive as a row-scaled fp16 copy, scaled back at the store;
 //     within a 128-wide block, instruction i of lane quarter h covers the
 //     8-wide chunk 4 h + i for both operands;
 //   * packed words, scales, zeros and activations are fetched D blocks ahead
@@ -57,16 +58,11 @@ __device__ __forceinline__ h8_t dequant_word(uint32_t w, h2_t zz, h2_t ss) {
   return b;
 }
 
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
-  const float lo = bitcast<float>(u << 16);
-  const float hi = bitcast<float>(u & 0xFFFF0000u);
-  return bitcast<uint32_t>(__builtin_amdgcn_cvt_pkrtz(lo, hi));
-}
-
-template <int NWV, int TM, int D, int CT, bool XBF16, int OUTK>
+template <int NWV, int TM, int D, int CT, int OUTK>
 __global__ __launch_bounds__(64 * NWV) void w4_skinny_kernel(const uint16_t* X, int M, int K,
                                                                const uint32_t* qweight, const uint16_t* scales,
-                                                               const uint32_t* qzeros, int N, int gsh, void* Y) {
+                                                               const uint32_t* qzeros, int N, int gsh, void* Y,
+                                                               const int* rowexp) {
   __shared__ f32x4_t red[NWV][CT * TM][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loop control
@@ -133,16 +129,7 @@ __global__ __launch_bounds__(64 * NWV) void w4_skinny_kernel(const uint16_t* X, 
       for (int i = 0; i < 4; ++i) {
         h8_t at[TM];
 #pragma unroll
-        for (int t = 0; t < TM; ++t) {
-          uint4 av4 = a[t][i];
-          if constexpr (XBF16) {
-            av4.x = bf16x2_to_f16x2(av4.x);
-            av4.y = bf16x2_to_f16x2(av4.y);
-            av4.z = bf16x2_to_f16x2(av4.z);
-            av4.w = bf16x2_to_f16x2(av4.w);
-          }
-          at[t] = bitcast<h8_t>(av4);
-        }
+        for (int t = 0; t < TM; ++t) at[t] = bitcast<h8_t>(a[t][i]);
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
           const uint32_t word = i == 0 ? w[c].x : i == 1 ? w[c].y : i == 2 ? w[c].z : w[c].w;
@@ -185,32 +172,26 @@ __global__ __launch_bounds__(64 * NWV) void w4_skinny_kernel(const uint16_t* X, 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 16 * t + 4 * h + r;
-        if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, tot[r]);
+        if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, row_scaled(tot[r], rowexp, m));
       }
     }
   }
 }
 
-template <int NWV, int TM, int D, int CT, bool XBF16, int OUTK>
+template <int NWV, int TM, int D, int CT, int OUTK>
 void launch_k(const W4Args& a, hipStream_t stream) {
   static_assert(CT * TM <= NWV, "one summing wave per output tile");
   const int gsh = a.G == 256 ? 1 : 0;
-  hipLaunchKernelGGL((w4_skinny_kernel<NWV, TM, D, CT, XBF16, OUTK>), dim3((a.N + CT * kCols - 1) / (CT * kCols)),
+  hipLaunchKernelGGL((w4_skinny_kernel<NWV, TM, D, CT, OUTK>), dim3((a.N + CT * kCols - 1) / (CT * kCols)),
                      dim3(64 * NWV), 0, stream, static_cast<const uint16_t*>(a.X), a.M, a.K, a.qweight, a.scales,
-                     a.qzeros, a.N, gsh, a.Y);
-}
-
-template <int NWV, int TM, int D, int CT, bool XBF16>
-void launch_o(const W4Args& a, hipStream_t stream) {
-  if (a.y_dtype == QLIN_F16) launch_k<NWV, TM, D, CT, XBF16, OUT_F16>(a, stream);
-  else if (a.y_dtype == QLIN_BF16) launch_k<NWV, TM, D, CT, XBF16, OUT_BF16>(a, stream);
-  else launch_k<NWV, TM, D, CT, XBF16, OUT_F32>(a, stream);
+                     a.qzeros, a.N, gsh, a.Y, a.rowexp);
 }
 
 template <int NWV, int TM, int D, int CT = 1>
-void launch_x(const W4Args& a, hipStream_t stream) {
-  if (a.x_dtype == QLIN_BF16) launch_o<NWV, TM, D, CT, true>(a, stream);
-  else launch_o<NWV, TM, D, CT, false>(a, stream);
+void launch_o(const W4Args& a, hipStream_t stream) {
+  if (a.y_dtype == QLIN_F16) launch_k<NWV, TM, D, CT, OUT_F16>(a, stream);
+  else if (a.y_dtype == QLIN_BF16) launch_k<NWV, TM, D, CT, OUT_BF16>(a, stream);
+  else launch_k<NWV, TM, D, CT, OUT_F32>(a, stream);
 }
 
 }  // namespace
@@ -223,9 +204,9 @@ bool w4_skinny_supported(int M, int K, int G) { return M >= 1 && M <= 16 && (G =
 // otherwise (a 4096-column layer keeps its 256 workgroups).
 void w4_skinny_launch(const W4Args& a, hipStream_t stream) {
   const long long wg4 = (a.N + 4 * kCols - 1) / (4 * kCols), wg2 = (a.N + 2 * kCols - 1) / (2 * kCols);
-  if (wg4 >= 160) launch_x<4, 1, 3, 4>(a, stream);
-  else if (wg2 >= 160) launch_x<4, 1, 2, 2>(a, stream);
-  else launch_x<4, 1, 4, 1>(a, stream);
+  if (wg4 >= 160) launch_o<4, 1, 3, 4>(a, stream);
+  else if (wg2 >= 160) launch_o<4, 1, 2, 2>(a, stream);
+  else launch_o<4, 1, 4, 1>(a, stream);
 }
 
 }  // namespace qlin

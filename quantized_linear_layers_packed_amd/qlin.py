@@ -46,6 +46,7 @@ EXPORTS = (
     "qlin_stream_read", "qlin_stream_copy",
     "qlin_hessian", "qlin_w4_pack_gptq", "spqr_pack_hessian",
     "qlin_w4_pack_gptq_actorder", "qlin_w4_forward_perm",
+    "qlin_w4_workspace_bytes", "sq_int8_gemm_workspace_bytes",
 )
 
 _vp, _i, _i64, _sz, _d = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.c_double
@@ -55,7 +56,8 @@ _sigs = {
     "qlin_last_error": ([], C.c_char_p),
     "qlin_w4_sizes": ([_i, _i, _i, _vp, _vp, _vp], _i),
     "qlin_w4_pack": ([_vp, _i, _i, _i, _vp, _vp, _vp], _i),
-    "qlin_w4_forward": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _vp], _i),
+    "qlin_w4_forward": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _vp, _sz, _vp], _i),
+    "qlin_w4_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _vp], _i),
     "qlin_w4_unpack": ([_vp, _vp, _i, _i, _i, _vp, _vp, _vp], _i),
     "spqr_sizes": ([_i, _i, _d, _vp, _vp, _vp, _vp], _i),
     "spqr_pack": ([_vp, _i, _i, _d, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp], _i),
@@ -65,14 +67,15 @@ _sigs = {
     "sq_compute_smoothing": ([_vp, _vp, _i, _i, _d, _vp, _vp], _i),
     "sq_pack_weight": ([_vp, _vp, _i, _i, _vp, _vp], _i),
     "sq_smooth_quant_act": ([_vp, _vp, _i, _i, _vp, _vp, _vp], _i),
-    "sq_int8_gemm": ([_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp], _i),
+    "sq_int8_gemm": ([_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _sz, _vp], _i),
+    "sq_int8_gemm_workspace_bytes": ([_i, _i, _i, _i, _vp], _i),
     "qlin_stream_read": ([_vp, _sz, _i, _i, _i, _vp, _vp], _i),
     "qlin_stream_copy": ([_vp, _vp, _sz, _vp], _i),
     "qlin_hessian": ([_vp, _i, _i, _vp], _i),
     "qlin_w4_pack_gptq": ([_vp, _i, _i, _i, _vp, _d, _vp, _vp, _vp], _i),
     "spqr_pack_hessian": ([_vp, _i, _i, _d, _vp, _d, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp], _i),
     "qlin_w4_pack_gptq_actorder": ([_vp, _i, _i, _i, _vp, _d, _i, _vp, _vp, _vp, _vp], _i),
-    "qlin_w4_forward_perm": ([_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _vp], _i),
+    "qlin_w4_forward_perm": ([_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _vp, _sz, _vp], _i),
 }
 for _name, (_args, _res) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -109,6 +112,19 @@ def _stream(s):
     if isinstance(s, int):
         return s
     return s.cuda_stream
+
+
+def _nbytes(ws, nbytes):
+    """Workspace size argument: the given count, else the buffer's own size."""
+    if ws is None:
+        return 0
+    if nbytes is not None:
+        return int(nbytes)
+    if isinstance(ws, np.ndarray):
+        return ws.nbytes
+    if hasattr(ws, "untyped_storage"):
+        return ws.numel() * ws.element_size()
+    raise ValueError("pass workspace_bytes with an integer workspace pointer")
 
 
 def _check(st: int):
@@ -192,14 +208,24 @@ def qlin_w4_pack_gptq_actorder(W: np.ndarray, G: int, H: np.ndarray, damp: float
     return qw, sc.view(np.float16), qz, perm
 
 
-def qlin_w4_forward_perm(X, x_dtype, M, K, perm, Xp, qweight, scales, qzeros, N, G, Y, y_dtype, stream=None):
+def qlin_w4_workspace_bytes(x_dtype, M, K, N, G, y_dtype):
+    b = C.c_size_t()
+    _check(_lib.qlin_w4_workspace_bytes(x_dtype, M, K, N, G, y_dtype, C.byref(b)))
+    return b.value
+
+
+def qlin_w4_forward_perm(X, x_dtype, M, K, perm, Xp, qweight, scales, qzeros, N, G, Y, y_dtype,
+                         workspace=None, workspace_bytes=None, stream=None):
     _check(_lib.qlin_w4_forward_perm(_ptr(X), x_dtype, M, K, _ptr(perm), _ptr(Xp), _ptr(qweight), _ptr(scales),
-                                     _ptr(qzeros), N, G, _ptr(Y), y_dtype, _stream(stream)))
+                                     _ptr(qzeros), N, G, _ptr(Y), y_dtype, _ptr(workspace),
+                                     _nbytes(workspace, workspace_bytes), _stream(stream)))
 
 
-def qlin_w4_forward(X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype, stream=None):
+def qlin_w4_forward(X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype,
+                    workspace=None, workspace_bytes=None, stream=None):
     _check(_lib.qlin_w4_forward(_ptr(X), x_dtype, M, K, _ptr(qweight), _ptr(scales), _ptr(qzeros),
-                                N, G, _ptr(Y), y_dtype, _stream(stream)))
+                                N, G, _ptr(Y), y_dtype, _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                                _stream(stream)))
 
 
 def qlin_w4_unpack(qweight, qzeros, N, K, G, codes, zeros, stream=None):
@@ -298,9 +324,16 @@ def sq_smooth_quant_act(X, inv_s, M, K, Xq, x_scale, stream=None):
     _check(_lib.sq_smooth_quant_act(_ptr(X), _ptr(inv_s), M, K, _ptr(Xq), _ptr(x_scale), _stream(stream)))
 
 
-def sq_int8_gemm(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype=QLIN_F16, acc_out=None, stream=None):
+def sq_int8_gemm_workspace_bytes(M, N, K, y_dtype=QLIN_F16):
+    b = C.c_size_t()
+    _check(_lib.sq_int8_gemm_workspace_bytes(M, N, K, y_dtype, C.byref(b)))
+    return b.value
+
+
+def sq_int8_gemm(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype=QLIN_F16, acc_out=None,
+                 workspace=None, workspace_bytes=None, stream=None):
     _check(_lib.sq_int8_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y), y_dtype,
-                             _ptr(acc_out), _stream(stream)))
+                             _ptr(acc_out), _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

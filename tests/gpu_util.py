@@ -43,6 +43,36 @@ def host(t, np_dtype=None):
     return a.view(np_dtype) if np_dtype is not None else a
 
 
+_WORKSPACES = []
+
+
+def workspace(nbytes):
+    """A zero-filled device workspace of at least ``nbytes`` (None when 0).
+
+    Buffers are shared by the calls of a test process (which run one after the
+    other on one stream) and are never freed: a captured graph may still refer
+    to one."""
+    if nbytes == 0:
+        return None
+    torch = torch_cuda()
+    for t in _WORKSPACES:
+        if t.numel() >= nbytes:
+            return t
+    t = torch.zeros(max(int(nbytes), 1 << 20), dtype=torch.uint8, device="cuda")
+    _WORKSPACES.append(t)
+    return t
+
+
+def w4_ws(x_dtype, M, K, N, G, y_dtype):
+    from quantized_linear_layers_packed_amd import qlin
+    return workspace(qlin.qlin_w4_workspace_bytes(x_dtype, M, K, N, G, y_dtype))
+
+
+def sq_ws(M, N, K, y_dtype):
+    from quantized_linear_layers_packed_amd import qlin
+    return workspace(qlin.sq_int8_gemm_workspace_bytes(M, N, K, y_dtype))
+
+
 def bf16_bits_to_f64(bits):
     return metrics.bf16_bits_to_f64(bits)
 

@@ -11,7 +11,7 @@ import pytest
 from oracle import spqr as ospqr
 from oracle import w4 as ow4
 from quantized_linear_layers_packed_amd import qlin
-from tests.gpu_util import check_close, dev, empty, host, say, torch_cuda
+from tests.gpu_util import check_close, dev, empty, host, say, torch_cuda, w4_ws
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +30,7 @@ def _w4_gpu(X, packed, N, K, G):
     M = X.shape[0]
     Y = empty((M, N), torch.float32)
     qw, sc, qz = (dev(a) for a in packed)
-    qlin.qlin_w4_forward(dev(X), F16, M, K, qw, sc, qz, N, G, Y, F32)
+    qlin.qlin_w4_forward(dev(X), F16, M, K, qw, sc, qz, N, G, Y, F32, workspace=w4_ws(F16, M, K, N, G, F32))
     return host(Y).astype(np.float64)
 
 
@@ -96,11 +96,12 @@ def test_act_order_forward_through_the_gather(G):
         Xd = dev(X)
         Xp = empty((M, K), torch.float16)
         Y = empty((M, N), torch.float32)
-        qlin.qlin_w4_forward_perm(Xd, F16, M, K, perm, Xp, qw, sc, qz, N, G, Y, F32)
+        wsp = w4_ws(F16, M, K, N, G, F32)
+        qlin.qlin_w4_forward_perm(Xd, F16, M, K, perm, Xp, qw, sc, qz, N, G, Y, F32, workspace=wsp)
         check_close(host(Y).astype(np.float64), ogptq.forward_perm(X, *dyn, K, G), f"dynamic groups M={M}")
         check_close(_w4_gpu(X, sta[:3], N, K, G), ow4.forward(X, *sta[:3], K, G), f"static groups M={M}")
         Y1 = empty((M, N), torch.float32)
-        qlin.qlin_w4_forward_perm(Xd, F16, M, K, ident, Xp, qw, sc, qz, N, G, Y1, F32)
+        qlin.qlin_w4_forward_perm(Xd, F16, M, K, ident, Xp, qw, sc, qz, N, G, Y1, F32, workspace=wsp)
         Y2 = empty((M, N), torch.float32)
-        qlin.qlin_w4_forward(Xd, F16, M, K, qw, sc, qz, N, G, Y2, F32)
+        qlin.qlin_w4_forward(Xd, F16, M, K, qw, sc, qz, N, G, Y2, F32, workspace=wsp)
         assert np.array_equal(host(Y1), host(Y2))

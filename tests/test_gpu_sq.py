@@ -6,7 +6,7 @@ import pytest
 import synth
 from oracle import smoothquant as osq
 from quantized_linear_layers_packed_amd import qlin
-from tests.gpu_util import check_close, dev, empty, host, say, torch_cuda
+from tests.gpu_util import check_close, dev, empty, host, say, sq_ws, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +26,7 @@ def gpu_gemm(Xq_d, xs_d, Wq_d, ws_d, M, N, K, y_dtype=F16, want_acc=True):
     torch = torch_cuda()
     Y = empty((M, N), torch.float16 if y_dtype == F16 else torch.float32)
     acc = empty((M, N), torch.int32) if want_acc else None
-    qlin.sq_int8_gemm(Xq_d, xs_d, Wq_d, ws_d, M, N, K, Y, y_dtype, acc)
+    qlin.sq_int8_gemm(Xq_d, xs_d, Wq_d, ws_d, M, N, K, Y, y_dtype, acc, workspace=sq_ws(M, N, K, y_dtype))
     return host(Y).astype(np.float64), (host(acc) if want_acc else None)
 
 

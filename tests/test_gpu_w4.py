@@ -8,7 +8,7 @@ import synth
 from oracle import metrics
 from oracle import w4 as ow4
 from quantized_linear_layers_packed_amd import qlin
-from tests.gpu_util import check_close, dev, empty, host, say, torch_cuda
+from tests.gpu_util import check_close, dev, empty, host, say, torch_cuda, w4_ws
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +24,8 @@ def gpu_w4(X, x_dtype, packed_dev, N, K, G, y_dtype):
     M = X.shape[0]
     qw, sc, qz = packed_dev
     Y = empty((M, N), _tdtype(y_dtype))
-    qlin.qlin_w4_forward(dev(X), x_dtype, M, K, qw, sc, qz, N, G, Y, y_dtype)
+    qlin.qlin_w4_forward(dev(X), x_dtype, M, K, qw, sc, qz, N, G, Y, y_dtype,
+                         workspace=w4_ws(x_dtype, M, K, N, G, y_dtype))
     y = host(Y)
     if y_dtype == BF16:
         return y                            # bit patterns
@@ -222,3 +223,37 @@ def test_small_batches_through_the_mfma_kernels(x_dtype):
             say(f"w4 small-batch N={N} K={K} G={G} M={M} x={x_dtype}")
             X = (synth.x_bf16_bits if x_dtype == BF16 else synth.x_f16)(M, K, f"gpu/w4/smallmx{M}")
             check_close(gpu_w4(X, x_dtype, packed, N, K, G, F32), ow4.forward(X, *st, K, G), f"M={M}")
+
+
+@pytest.mark.parametrize("G", [128, 64])
+def test_bf16_activations_beyond_the_fp16_range(G):
+    """bf16 activations that fp16 cannot hold: entries up to +-1e5, bf16
+    subnormals, a row of values around 1e-30, a row far above 65504 and an
+    all-zero row, at M = 5 (small-batch kernel, G = 128), 17 and 256 (GEMMs).
+    The MFMA paths take a row-scaled fp16 copy; each row's outputs are scaled
+    back, so the whole output meets the tolerance, and so does every special
+    row on its own (relative to that row)."""
+    N, K = 320, 2048
+    W = synth.normal_f32((N, K), 0.02, f"gpu/w4/bfrange{G}")
+    packed = dev_pack(W, G)
+    st = ow4.encode(W, G)
+    r = np.random.default_rng(7)
+    for M in (5, 17, 256):
+        say(f"w4 bf16 range N={N} K={K} G={G} M={M}")
+        X = synth.x_bf16_bits(M, K, f"gpu/w4/bfrangex{M}").copy()
+        big = r.choice(M * K, size=8, replace=False)
+        X.flat[big] = f32_to_bf16_bits(np.float32(1e5) * np.sign(r.standard_normal(8)).astype(np.float32))
+        sub = r.choice(M * K, size=64, replace=False)
+        X.flat[sub] = r.integers(1, 128, size=64).astype(np.uint16) | (r.integers(0, 2, 64) << 15).astype(np.uint16)
+        X[1] = f32_to_bf16_bits(synth.normal_f32((K,), 1e-30, f"gpu/w4/bftiny{M}"))       # tiny row
+        X[2] = f32_to_bf16_bits(synth.normal_f32((K,), 3e6, f"gpu/w4/bfhuge{M}"))         # huge row
+        X[3] = 0                                                                           # zero row
+        ref = ow4.forward(X, *st, K, G)
+        y32 = gpu_w4(X, BF16, packed, N, K, G, F32)
+        assert np.all(np.isfinite(y32))
+        check_close(y32, ref, f"M={M} all rows")
+        check_close(y32[1], ref[1], f"M={M} row of ~1e-30")
+        check_close(y32[2], ref[2], f"M={M} row of ~3e6")
+        assert not np.any(y32[3])
+        yb = gpu_w4(X, BF16, packed, N, K, G, BF16)
+        assert np.array_equal(yb, f32_to_bf16_bits(y32))
