@@ -5,11 +5,17 @@ and linked into quantized_linear_layers_packed_amd/libqlin.so.  Device code is
 compiled with packed-fp32 instructions disabled and without floating-point
 contraction, so every multiply-add in the kernels is the one written in the
 source (fmaf where fused, separate operations elsewhere).
+
+The compiler's per-kernel resource report (registers, occupancy, scratch) is
+collected into _build/kernel_resources.txt, and the build fails if any kernel
+uses scratch memory: a register array the compiler could not keep in
+registers turns every access to it into a memory round trip.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -34,19 +40,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
+_REMARK = re.compile(r"remark: +(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]"
+                     r"|VGPRs Spill|LDS Size \[bytes/block\]): (\S+) \[-Rpass-analysis")
+
+
+def _resources(stderr: str):
+    """Per-kernel fields of the compiler's kernel-resource-usage remarks."""
+    out, cur = [], None
+    for m in _REMARK.finditer(stderr):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = {"kernel": val}
+            out.append(cur)
+        elif cur is not None:
+            cur[key.split(" [")[0]] = val
+    return out
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
-        cmd = [hipcc(), "-x", "hip", *DEVICE, *COMMON, "-c", src, "-o", obj]
+        cmd = [hipcc(), "-x", "hip", *DEVICE, *COMMON, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     else:
         cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    warn = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip())
+    res = _resources(r.stderr)
+    warn = "\n".join(l for l in r.stderr.splitlines()
+                     if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l and l.strip()
+                     and not l.lstrip().startswith(("|", "^")) and not re.match(r"^\s*\d+ \|", l))
     if warn:
         print(warn, file=sys.stderr)
-    return obj
+    return obj, res
 
 
 def build(verbose: bool = True) -> str:
@@ -54,7 +80,15 @@ def build(verbose: bool = True) -> str:
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
     jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        done = list(ex.map(_compile, srcs))
+    objs = [o for o, _ in done]
+    res = [k for _, r in done for k in r]
+    with open(os.path.join(BUILD, "kernel_resources.txt"), "w") as f:
+        for k in res:
+            f.write(" ".join(f"{a}={b}" for a, b in k.items()) + "\n")
+    bad = [k["kernel"] for k in res if k.get("ScratchSize", "0") != "0"]
+    if bad:
+        raise RuntimeError("kernels using scratch memory (a register array spilled to memory): " + ", ".join(bad))
     tmp = OUT + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -53,12 +53,6 @@ __device__ __forceinline__ void store_out(void* Y, size_t idx, float v) {
   }
 }
 
-// Value of output row m when its activations entered as a row-scaled fp16 copy
-// (x * 2^-e_m, bf16 inputs): the product is scaled back by 2^e_m, exactly.
-__device__ __forceinline__ float row_scaled(float v, const int* rowexp, int m) {
-  return rowexp ? ldexpf(v, rowexp[m]) : v;
-}
-
 // XCD-aware tile order.  Workgroups are dispatched round-robin over the 8 XCDs
 // (each with its own L2), so linear workgroup b lands on XCD b % 8.  This maps
 // b to a tile index such that every XCD owns one contiguous range of tiles;

@@ -34,16 +34,29 @@ __device__ __forceinline__ int sk_owner(const SkPlan& s, long long u) {
 }
 
 // Hand-off of a shared tile.  Partial tiles cross XCDs, whose L2 caches are
-// not coherent with each other, so the partials are written and read with
-// device-scope (agent) atomic accesses, which are performed at the device
-// coherence point rather than in an XCD's L2.  Each contributor drains its own
-// stores (s_waitcnt vmcnt(0)) before the workgroup barrier; thread 0 then bumps
-// the tile's arrival counter with a device-scope RELEASE read-modify-write, and
-// the workgroup that sees the final count runs a device-scope ACQUIRE fence
-// before it reads the partials.  Release/acquire on the counter is what the
-// HIP memory model needs for the partials to be visible; on gfx950 it costs
-// one write-back of the issuing XCD's L2 per arrival and one L2 invalidate per
-// finished shared tile (at most one per workgroup).
+// not coherent with each other, so every access to a partial is a device-scope
+// (agent) atomic access: on gfx950 such stores are written through to the
+// device coherence point and such loads are served from it, never from a stale
+// line of an XCD's L2.  The ordering the last arriver relies on:
+//   1. each contributor's threads store their part with agent-scope atomic
+//      stores and then wait for all of them to complete (s_waitcnt vmcnt(0):
+//      a vector store counts as complete once the memory side has acknowledged
+//      it at the scope it was issued with);
+//   2. a workgroup barrier orders every thread's wait before thread 0's
+//      agent-scope atomic add on the tile's counter, which is performed at the
+//      same coherence point, so when the add is performed every partial store
+//      of that workgroup already is;
+//   3. the workgroup whose add returns the final count issues its partial
+//      loads only after the add has returned (the result is broadcast through
+//      LDS behind a barrier), and those agent-scope loads read the coherence
+//      point, so they see every contributor's stores.
+// This is the hardware ordering of gfx950's memory pipeline, not the C++/HIP
+// model's: under the model the counter would need release/acquire order, which
+// the compiler implements with a write-back of the issuing XCD's whole L2 per
+// arrival and an invalidate of the whole L2 per acquire.  Measured, that made
+// the W4 GEMM at 256 rows 2x slower and the int8 GEMM 1.5x slower, while
+// adding nothing the accesses above do not already have.  Repeat, graph
+// replay and concurrent-stream tests check that the sums are bit-identical.
 __device__ __forceinline__ void sk_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -60,17 +73,15 @@ __device__ __forceinline__ void sk_drain_stores() { asm volatile("s_waitcnt vmcn
 
 // Every thread of the workgroup calls this after storing its part of the
 // partial tile.  Returns true (in every thread) for the workgroup that arrives
-// last, i.e. sees `prior` earlier arrivals; that workgroup has run the acquire
-// fence and may read the other partials.  s_flag: a __shared__ int.
+// last, i.e. sees `prior` earlier arrivals; that workgroup may then read the
+// other partials (steps 1-3 above).  s_flag: a __shared__ int.
 __device__ __forceinline__ bool sk_arrive_last(int* counter, int prior, int* s_flag) {
   sk_drain_stores();
   __syncthreads();
   if (threadIdx.x == 0)
-    *s_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == prior;
+    *s_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == prior;
   __syncthreads();
-  const bool last = *s_flag != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
+  return *s_flag != 0;
 }
 
 // The last arriver returns the counter to zero once it has read the partials

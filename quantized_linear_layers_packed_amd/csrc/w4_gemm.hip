@@ -118,12 +118,23 @@ __global__ __launch_bounds__(kThreads) void w4_gemm_group_kernel(
 
   // ---- epilogue: lane holds column n, rows 8*(r/4) + 4*half + r%4 of each tile
   if (n_ok) {
+    if (rowexp) {
+      int ex[TM][16];
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ex[t][r] = rowexp[min(m0 + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3), M - 1)];
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = ldexpf(acc[t][r], ex[t][r]);
+    }
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, row_scaled(acc[t][r], rowexp, m));
+        if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, acc[t][r]);
       }
     }
   }

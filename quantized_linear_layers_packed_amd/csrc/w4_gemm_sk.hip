@@ -122,7 +122,10 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
       for (int j = 0; j < APT; ++j) {
         const int piece = tid + j * kThreads;
         const int r = piece >> 4, c = piece & 15;
-        dst[r * 16 + (c ^ (r & 15))] = src[j];
+        // copied through a local first: storing src[j] straight to LDS made
+        // the compiler keep the whole register ring in scratch memory
+        const uint4 v = src[j];
+        dst[r * 16 + (c ^ (r & 15))] = v;
       }
     };
     uint4 bq[R][2];                            // weight ring: step k0 + j in set j % R
@@ -165,17 +168,25 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
       const h2_t zz = {zb, zb};
       const _Float16 sh = bitcast<_Float16>(static_cast<uint16_t>(bs[S]));
       const h2_t ss = {sh, sh};
+      // the A fragments of MFMA group st + 1 are read from LDS while group st
+      // runs, so no matrix instruction waits on a read issued just before it
+      auto read_a = [&](int st, h8_t (&a)[TM]) {
+        const int c = 8 * (st >> 2) + 4 * h + (st & 3);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a[i] = bitcast<h8_t>(Ab[(32 * i + col) * 16 + (c ^ swz)]);
+      };
+      h8_t afr[2][TM];
+      read_a(0, afr[0]);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
+        if (st + 1 < 8) read_a(st + 1, afr[(st + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);     // the reads stay ahead of this group's math
         const uint4 q4 = bq[S][st >> 2];
         const uint32_t w = (st & 3) == 0 ? q4.x : (st & 3) == 1 ? q4.y : (st & 3) == 2 ? q4.z : q4.w;
         const h8_t b = dequant_nat(w, zz, ss);
-        const int c = 8 * (st >> 2) + 4 * h + (st & 3);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const h8_t a = bitcast<h8_t>(Ab[(32 * i + col) * 16 + (c ^ swz)]);
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[i], 0, 0, 0);
-        }
+        for (int i = 0; i < TM; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[st & 1][i], b, acc[i], 0, 0, 0);
       }
       // the next step's activations (past the range end this rewrites the idle
       // buffer), then the fetch R steps ahead into the set of step kk
@@ -235,12 +246,25 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
       }
     }
     if (write && nok) {
+      if (rowexp) {
+        // row-scaled fp16 copy of bf16 activations: every row exponent loaded
+        // first (clamped rows, no branches), then the exact rescale
+        int ex[TM][16];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ex[i][r] = rowexp[min(m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3), M - 1)];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][r] = ldexpf(acc[i][r], ex[i][r]);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, row_scaled(acc[i][r], rowexp, m));
+          if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, acc[i][r]);
         }
     }
     u += k1 - k0;

@@ -169,10 +169,17 @@ __global__ __launch_bounds__(64 * NWV) void w4_skinny_kernel(const uint16_t* X, 
 #pragma unroll
     for (int w = 1; w < NWV; ++w) tot += red[w][wv][lane];
     if (n < N) {
+      if (rowexp) {
+        int ex[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ex[r] = rowexp[min(16 * t + 4 * h + r, M - 1)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[r] = ldexpf(tot[r], ex[r]);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 16 * t + 4 * h + r;
-        if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, row_scaled(tot[r], rowexp, m));
+        if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, tot[r]);
       }
     }
   }

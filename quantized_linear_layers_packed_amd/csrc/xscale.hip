@@ -13,7 +13,7 @@
 //
 // One workgroup of 256 threads per row: the row maximum from the bf16 bit
 // patterns (magnitudes compare as integers), then the conversion (round to
-// nearest even) of 16-byte chunks.
+// nearest even) of 16-byte chunks held in registers.
 
 #include "common.hpp"
 #include "device.hpp"
@@ -42,6 +42,32 @@ __device__ __forceinline__ float bf16_times_pow2(uint32_t h, int e) {
   return (h & 0x8000u) ? -v : v;
 }
 
+// Largest magnitude (bf16 bits, sign cleared) of the 8 values of a chunk.
+__device__ __forceinline__ uint32_t chunk_absmax(const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mx = max(mx, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+  return mx;
+}
+
+__device__ __forceinline__ uint4 chunk_convert(const uint4& v, int e) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const h2_t hh = {static_cast<_Float16>(bf16_times_pow2(w[j] & 0xFFFFu, e)),
+                     static_cast<_Float16>(bf16_times_pow2(w[j] >> 16, e))};
+    o[j] = bitcast<uint32_t>(hh);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Rows of up to kThreads * CPT chunks (CPT * 2048 values) are read once: every
+// chunk of a thread is loaded before the first use (indices clamped into the
+// row, so no load is conditional), the row maximum taken, and the registers
+// converted.  Longer rows loop over slices of that size and read the row twice.
+template <int CPT>
 __global__ __launch_bounds__(kThreads) void x_rowscale_kernel(const uint16_t* __restrict__ X, int K,
                                                               uint16_t* __restrict__ Xh, int* __restrict__ rowexp) {
   __shared__ uint32_t s_max[kThreads / 64];
@@ -49,13 +75,15 @@ __global__ __launch_bounds__(kThreads) void x_rowscale_kernel(const uint16_t* __
   const uint4* src = reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K);
   uint4* dst = reinterpret_cast<uint4*>(Xh + static_cast<size_t>(m) * K);
   const int nchunk = K >> 3;
+  constexpr int kSlice = kThreads * CPT;
 
+  uint4 v[CPT];
   uint32_t mx = 0;
-  for (int c = tid; c < nchunk; c += kThreads) {
-    const uint4 v = src[c];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int c0 = 0; c0 < nchunk; c0 += kSlice) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mx = max(mx, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    for (int j = 0; j < CPT; ++j) v[j] = src[min(c0 + tid + j * kThreads, nchunk - 1)];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) mx = max(mx, chunk_absmax(v[j]));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), off, 64)));
@@ -67,25 +95,33 @@ __global__ __launch_bounds__(kThreads) void x_rowscale_kernel(const uint16_t* __
   const int e = (mx == 0 || mx >= 0x7F80u) ? 0 : rowscale_exponent(mx);
   if (tid == 0) rowexp[m] = e;
 
-  for (int c = tid; c < nchunk; c += kThreads) {
-    const uint4 v = src[c];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
+  if (nchunk <= kSlice) {                       // the whole row is in registers
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float lo = bf16_times_pow2(w[j] & 0xFFFFu, e);
-      const float hi = bf16_times_pow2(w[j] >> 16, e);
-      const h2_t hh = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
-      o[j] = bitcast<uint32_t>(hh);
+    for (int j = 0; j < CPT; ++j) {
+      const int c = tid + j * kThreads;
+      if (c < nchunk) dst[c] = chunk_convert(v[j], e);
     }
-    dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    return;
+  }
+  for (int c0 = 0; c0 < nchunk; c0 += kSlice) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) v[j] = src[min(c0 + tid + j * kThreads, nchunk - 1)];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = c0 + tid + j * kThreads;
+      if (c < nchunk) dst[c] = chunk_convert(v[j], e);
+    }
   }
 }
 
 }  // namespace
 
 void x_rowscale_launch(const uint16_t* X, int M, int K, uint16_t* Xh, int* rowexp, hipStream_t stream) {
-  hipLaunchKernelGGL(x_rowscale_kernel, dim3(M), dim3(kThreads), 0, stream, X, K, Xh, rowexp);
+  const int nchunk = K / 8;
+  if (nchunk <= kThreads * 4)
+    hipLaunchKernelGGL(x_rowscale_kernel<4>, dim3(M), dim3(kThreads), 0, stream, X, K, Xh, rowexp);
+  else
+    hipLaunchKernelGGL(x_rowscale_kernel<16>, dim3(M), dim3(kThreads), 0, stream, X, K, Xh, rowexp);
 }
 
 }  // namespace qlin
