@@ -136,6 +136,23 @@ qlin_status qlin_w4_forward(const void* X, int x_dtype, int M, int K,
                             void* Y, int y_dtype, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/* qlin_w4_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument; the workspace comes from a fixed device array of the
+ * library (80 MiB, zero at load, held on every device the library runs on
+ * until the process ends; its address is looked up on the first call on each
+ * device).  Allocates nothing.  Split-K shapes first clear the array's arrival
+ * counters with a small kernel on `stream`.  Every call on one device shares the
+ * array, so calls that overlap in time on one device (concurrent streams,
+ * threads) race and give wrong results; serialize them.  A shape whose
+ * workspace (qlin_w4_workspace_bytes) exceeds 80 MiB returns EUNSUPPORTED and
+ * enqueues nothing.  Other arguments, requirements, results and errors as
+ * qlin_w4_forward; results are bit-identical to it. */
+qlin_status qlin_w4_forward_scratch(const void* X, int x_dtype, int M, int K,
+                                    const uint32_t* qweight, const uint16_t* scales,
+                                    const uint32_t* qzeros, int N, int G,
+                                    void* Y, int y_dtype, hipStream_t stream);
+
 /* Forward of act-order storage (qlin_w4_pack_gptq_actorder without static
  * groups): the stored columns are in quantization order and stored column t is
  * input column perm[t], so Y = X[:, perm] . W_hat^T.  The GPTQ bulletin

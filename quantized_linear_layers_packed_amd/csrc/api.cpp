@@ -79,7 +79,7 @@ qlin_status w4_check_shape(const char* fn, int x_dtype, int M, int K, int N, int
 qlin_status w4_forward_checked(const char* fn, const void* X, int x_dtype, int M, int K,
                                const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int N, int G,
                                void* Y, int y_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                               bool gather, const int32_t* perm, void* Xp) {
+                               bool gather, const int32_t* perm, void* Xp, bool clear_counters = false) {
   QLIN_TRY(w4_check_shape(fn, x_dtype, M, K, N, G, y_dtype));
   if (!X || !qweight || !scales || !qzeros || !Y) return fail(QLIN_EINVAL, std::string(fn) + ": NULL pointer");
   QLIN_TRY(need_aligned(fn, "X", X));
@@ -100,6 +100,8 @@ qlin_status w4_forward_checked(const char* fn, const void* X, int x_dtype, int M
   QLIN_TRY(w4_plan(a, &plan));
   QLIN_TRY(need_workspace(fn, workspace, workspace_bytes, plan.total));
   const WsView ws{static_cast<char*>(workspace), workspace_bytes};
+  // nothing is enqueued before this point
+  if (clear_counters && plan.path == W4Path::kSplitK) scratch_clear_counters(ws.base, stream);
   if (gather) {
     permute_cols_launch(X, perm, M, K, Xp, stream);
     a.X = Xp;
@@ -170,6 +172,28 @@ qlin_status qlin_w4_forward_perm(const void* X, int x_dtype, int M, int K, const
   clear_error();
   return w4_forward_checked("qlin_w4_forward_perm", X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype,
                             workspace, workspace_bytes, stream, true, perm, Xp);
+}
+
+qlin_status qlin_w4_forward_scratch(const void* X, int x_dtype, int M, int K,
+                                    const uint32_t* qweight, const uint16_t* scales,
+                                    const uint32_t* qzeros, int N, int G,
+                                    void* Y, int y_dtype, hipStream_t stream) {
+  static const char* fn = "qlin_w4_forward_scratch";
+  clear_error();
+  QLIN_TRY(w4_check_shape(fn, x_dtype, M, K, N, G, y_dtype));
+  W4Args a{X, x_dtype, M, K, N, G, qweight, scales, qzeros, Y, y_dtype, nullptr};
+  W4Plan plan;
+  QLIN_TRY(w4_plan(a, &plan));
+  if (plan.total > scratch_bytes())
+    return fail(QLIN_EUNSUPPORTED, std::string(fn) + ": this shape needs " + std::to_string(plan.total) +
+                                       " bytes of scratch, the library's fixed scratch holds " +
+                                       std::to_string(scratch_bytes()) + "; use qlin_w4_forward with a workspace");
+  char* base = nullptr;
+  if (plan.total > 0) QLIN_TRY(scratch_base(&base));
+  // split-K shapes clear the shared counters first (after every argument check):
+  // the previous call on this device left them zero unless calls overlapped
+  return w4_forward_checked(fn, X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype, base,
+                            base ? scratch_bytes() : 0, stream, false, nullptr, nullptr, true);
 }
 
 qlin_status qlin_w4_unpack(const uint32_t* qweight, const uint32_t* qzeros, int N, int K, int G,

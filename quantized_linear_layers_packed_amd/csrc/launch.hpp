@@ -45,6 +45,13 @@ void permute_cols_launch(const void* X, const int32_t* perm, int M, int K, void*
 void w4_unpack_launch(const uint32_t* qweight, const uint32_t* qzeros, int N, int K, int G,
                       uint8_t* codes, uint8_t* zeros, hipStream_t stream);
 
+// The library's fixed device scratch (see scratch.hip): its size, its address on
+// the current device (looked up once per device), and a fill kernel that zeroes
+// its arrival counters on `stream`.
+size_t scratch_bytes();
+qlin_status scratch_base(char** out);
+void scratch_clear_counters(char* base, hipStream_t stream);
+
 struct SpqrArgs {
   const uint16_t* X;
   int M, K, N;

@@ -46,7 +46,7 @@ EXPORTS = (
     "qlin_stream_read", "qlin_stream_copy",
     "qlin_hessian", "qlin_w4_pack_gptq", "spqr_pack_hessian",
     "qlin_w4_pack_gptq_actorder", "qlin_w4_forward_perm",
-    "qlin_w4_workspace_bytes", "sq_int8_gemm_workspace_bytes",
+    "qlin_w4_workspace_bytes", "sq_int8_gemm_workspace_bytes", "qlin_w4_forward_scratch",
 )
 
 _vp, _i, _i64, _sz, _d = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.c_double
@@ -58,6 +58,7 @@ _sigs = {
     "qlin_w4_pack": ([_vp, _i, _i, _i, _vp, _vp, _vp], _i),
     "qlin_w4_forward": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _vp, _sz, _vp], _i),
     "qlin_w4_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _vp], _i),
+    "qlin_w4_forward_scratch": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _vp], _i),
     "qlin_w4_unpack": ([_vp, _vp, _i, _i, _i, _vp, _vp, _vp], _i),
     "spqr_sizes": ([_i, _i, _d, _vp, _vp, _vp, _vp], _i),
     "spqr_pack": ([_vp, _i, _i, _d, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp], _i),
@@ -226,6 +227,11 @@ def qlin_w4_forward(X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype,
     _check(_lib.qlin_w4_forward(_ptr(X), x_dtype, M, K, _ptr(qweight), _ptr(scales), _ptr(qzeros),
                                 N, G, _ptr(Y), y_dtype, _ptr(workspace), _nbytes(workspace, workspace_bytes),
                                 _stream(stream)))
+
+
+def qlin_w4_forward_scratch(X, x_dtype, M, K, qweight, scales, qzeros, N, G, Y, y_dtype, stream=None):
+    _check(_lib.qlin_w4_forward_scratch(_ptr(X), x_dtype, M, K, _ptr(qweight), _ptr(scales), _ptr(qzeros),
+                                        N, G, _ptr(Y), y_dtype, _stream(stream)))
 
 
 def qlin_w4_unpack(qweight, qzeros, N, K, G, codes, zeros, stream=None):
