@@ -47,6 +47,10 @@ def parse():
                    help="summarize rocprofv3 csv output under DIR (trace/, fetch/, write/) and exit")
     p.add_argument("--calibrate", action="store_true",
                    help="first run a plain 256 MiB device copy (known traffic) 5 times, for counter scaling")
+    p.add_argument("--profile", metavar="PATH",
+                   help="run one workload point (e.g. w4_llama7b_M1, spqr_33b_M16, w4_llama70b_M256, "
+                        "sq_w8a8_M256) --iters times, untimed, for a profiler, and exit")
+    p.add_argument("--iters", type=int, default=5)
     p.add_argument("--sweep", choices=("batch", "outliers", "actorder"),
                    help="instead of the headline: batch crossover sweep M = 1..2048 (W4A16 vs W8A8 vs "
                         "dense fp16), SpQR outlier-fraction sweep 0-4%% at M = 1 and 4, or the act-order "
@@ -137,24 +141,28 @@ def time_steps(torch, step_fns, steps, warmup, copies):
 # ---------------------------------------------------------------------------
 # workloads
 
-def w4_layers(torch, qlin, synth, workload, M):
+def w4_layers(torch, qlin, synth, workload, Ms):
+    """Packed, rotated weights of a W4 workload, with activations, outputs and a
+    shared workspace for every batch size in Ms."""
+    Ms = (Ms,) if isinstance(Ms, int) else tuple(Ms)
     cfg = synth.WORKLOADS[workload]
     G = cfg["G"]
     xbf = cfg["x_dtype"] == "bf16"
+    xdt = qlin.QLIN_BF16 if xbf else qlin.QLIN_F16
+    ydt = qlin.QLIN_BF16 if cfg["y_dtype"] == "bf16" else qlin.QLIN_F16
+    ytd = torch.bfloat16 if cfg["y_dtype"] == "bf16" else torch.float16
     layers = []
     for li, (N, K) in enumerate(cfg["layers"]):
         W = synth.layer_weight(workload, li)
         packed = [to_dev(torch, a) for a in qlin.qlin_w4_pack(W, G)]
         del W
-        X = to_dev(torch, synth.activations(workload, li, M))
-        ydt = torch.bfloat16 if cfg["y_dtype"] == "bf16" else torch.float16
-        Y = torch.empty((M, N), dtype=ydt, device="cuda")
+        X = {M: to_dev(torch, synth.activations(workload, li, M)) for M in Ms}
+        Y = {M: torch.empty((M, N), dtype=ytd, device="cuda") for M in Ms}
         wbytes = sum(t.numel() * t.element_size() for t in packed)
-        layers.append(dict(N=N, K=K, M=M, G=G, packed=[packed], X=X, Y=Y, wbytes=wbytes,
-                           xdt=qlin.QLIN_BF16 if xbf else qlin.QLIN_F16,
-                           ydt=qlin.QLIN_BF16 if cfg["y_dtype"] == "bf16" else qlin.QLIN_F16,
-                           io=X.numel() * X.element_size() + Y.numel() * Y.element_size()))
-    need = max(qlin.qlin_w4_workspace_bytes(l["xdt"], M, l["K"], l["N"], G, l["ydt"]) for l in layers)
+        layers.append(dict(N=N, K=K, G=G, packed=[packed], Xs=X, Ys=Y, wbytes=wbytes, xdt=xdt, ydt=ydt,
+                           ios={M: X[M].numel() * X[M].element_size() + Y[M].numel() * Y[M].element_size()
+                                for M in Ms}))
+    need = max(qlin.qlin_w4_workspace_bytes(xdt, M, l["K"], l["N"], G, ydt) for l in layers for M in Ms)
     ws = zeros_ws(torch, need)
     for l in layers:
         l["ws"] = ws
@@ -171,18 +179,19 @@ def rotate(torch, layers):
     return R
 
 
-def w4_step_fns(qlin, layers):
+def w4_step_fns(qlin, layers, M):
     fns = []
     for l in layers:
         def f(i, l=l):
             qw, sc, qz = l["packed"][i % len(l["packed"])]
-            qlin.qlin_w4_forward(l["X"], l["xdt"], l["M"], l["K"], qw, sc, qz, l["N"], l["G"], l["Y"], l["ydt"],
+            qlin.qlin_w4_forward(l["Xs"][M], l["xdt"], M, l["K"], qw, sc, qz, l["N"], l["G"], l["Ys"][M], l["ydt"],
                                  workspace=l["ws"])
         fns.append(f)
     return fns
 
 
-def spqr_layers(torch, qlin, synth, M):
+def spqr_layers(torch, qlin, synth, Ms):
+    Ms = (Ms,) if isinstance(Ms, int) else tuple(Ms)
     cfg = synth.WORKLOADS["spqr_33b"]
     layers = []
     for li, (N, K) in enumerate(cfg["layers"]):
@@ -190,26 +199,28 @@ def spqr_layers(torch, qlin, synth, M):
         st = qlin.spqr_pack(W, cfg["outlier_frac"])
         del W
         packed = [to_dev(torch, st[k]) for k in ("codes", "stats1", "stats2", "row_ptr", "col_idx", "val")]
-        X = to_dev(torch, synth.activations("spqr_33b", li, M))
-        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        X = {M: to_dev(torch, synth.activations("spqr_33b", li, M)) for M in Ms}
+        Y = {M: torch.empty((M, N), dtype=torch.float16, device="cuda") for M in Ms}
         wbytes = sum(t.numel() * t.element_size() for t in packed)
-        layers.append(dict(N=N, K=K, M=M, nnz=len(st["val"]), packed=[packed], X=X, Y=Y, wbytes=wbytes,
-                           io=X.numel() * 2 + Y.numel() * 2))
+        layers.append(dict(N=N, K=K, nnz=len(st["val"]), packed=[packed], Xs=X, Ys=Y, wbytes=wbytes,
+                           ios={M: M * K * 2 + M * N * 2 for M in Ms}))
     rotate(torch, layers)
     return layers
 
 
-def spqr_step_fns(qlin, layers):
+def spqr_step_fns(qlin, layers, M):
     fns = []
     for l in layers:
         def f(i, l=l):
             c, s1, s2, rp, ci, v = l["packed"][i % len(l["packed"])]
-            qlin.spqr_forward(l["X"], l["M"], l["K"], c, s1, s2, rp, ci, v, l["nnz"], l["N"], l["Y"], qlin.QLIN_F16)
+            qlin.spqr_forward(l["Xs"][M], M, l["K"], c, s1, s2, rp, ci, v, l["nnz"], l["N"], l["Ys"][M],
+                              qlin.QLIN_F16)
         fns.append(f)
     return fns
 
 
-def sq_layers(torch, qlin, synth, M):
+def sq_layers(torch, qlin, synth, Ms):
+    Ms = (Ms,) if isinstance(Ms, int) else tuple(Ms)
     cfg = synth.WORKLOADS["sq_w8a8"]
     layers = []
     for li, (N, K) in enumerate(cfg["layers"]):
@@ -219,28 +230,29 @@ def sq_layers(torch, qlin, synth, M):
         Wq, ws = qlin.sq_pack_weight(W, s)
         del W
         packed = [to_dev(torch, Wq), to_dev(torch, ws)]
-        X = to_dev(torch, synth.activations("sq_w8a8", li, M))
-        layers.append(dict(N=N, K=K, M=M, packed=[packed], X=X, inv=to_dev(torch, inv),
-                           Xq=torch.empty((M, K), dtype=torch.int8, device="cuda"),
-                           xs=torch.empty((M,), dtype=torch.float32, device="cuda"),
-                           Y=torch.empty((M, N), dtype=torch.float16, device="cuda"),
+        layers.append(dict(N=N, K=K, packed=[packed], inv=to_dev(torch, inv),
+                           Xs={M: to_dev(torch, synth.activations("sq_w8a8", li, M)) for M in Ms},
+                           Xqs={M: torch.empty((M, K), dtype=torch.int8, device="cuda") for M in Ms},
+                           xss={M: torch.empty((M,), dtype=torch.float32, device="cuda") for M in Ms},
+                           Ys={M: torch.empty((M, N), dtype=torch.float16, device="cuda") for M in Ms},
                            wbytes=sum(t.numel() * t.element_size() for t in packed)))
-    ws = zeros_ws(torch, max(qlin.sq_int8_gemm_workspace_bytes(M, l["N"], l["K"], qlin.QLIN_F16) for l in layers))
+    ws = zeros_ws(torch, max(qlin.sq_int8_gemm_workspace_bytes(M, l["N"], l["K"], qlin.QLIN_F16)
+                             for l in layers for M in Ms))
     for l in layers:
         l["ws"] = ws
     rotate(torch, layers)
     return layers
 
 
-def sq_step_fns(qlin, layers):
+def sq_step_fns(qlin, layers, M):
     act, gemm = [], []
     for l in layers:
         def a(i, l=l):
-            qlin.sq_smooth_quant_act(l["X"], l["inv"], l["M"], l["K"], l["Xq"], l["xs"])
+            qlin.sq_smooth_quant_act(l["Xs"][M], l["inv"], M, l["K"], l["Xqs"][M], l["xss"][M])
 
         def g(i, l=l):
             Wq, ws = l["packed"][i % len(l["packed"])]
-            qlin.sq_int8_gemm(l["Xq"], l["xs"], Wq, ws, l["M"], l["N"], l["K"], l["Y"], qlin.QLIN_F16, None,
+            qlin.sq_int8_gemm(l["Xqs"][M], l["xss"][M], Wq, ws, M, l["N"], l["K"], l["Ys"][M], qlin.QLIN_F16, None,
                               workspace=l["ws"])
         act.append(a)
         gemm.append(g)
@@ -584,7 +596,10 @@ def summarize(d):
                 continue
             f_ = cnt.get("fetch", {}).get(k, float("nan"))
             w_ = cnt.get("write", {}).get(k, float("nan"))
-            out.append(f"  {k[0]:90s} grid {k[1]:9d} lds {k[2]:6d}  fetch {f_:12.1f}  write {w_:10.1f}")
+            fmb = f_ * 1024 * scale["fetch"] / 1e6 if scale.get("fetch") else float("nan")
+            wmb = w_ * 1024 * scale["write"] / 1e6 if scale.get("write") else float("nan")
+            out.append(f"  {k[0]:90s} grid {k[1]:9d} lds {k[2]:6d}  fetch {f_:12.1f}  write {w_:10.1f}"
+                       f"  -> {fmb:9.3f} MB read {wmb:8.3f} MB written")
         gemv = [k for k in keys if k[0].startswith("w4_gemv_kernel")]
         if gemv and scale.get("fetch") and scale.get("write"):
             fb = sum(cnt["fetch"][k] for k in gemv) * 1024 * scale["fetch"]
@@ -593,6 +608,43 @@ def summarize(d):
                    "write_bytes_per_step": round(wb), "scale_fetch": scale["fetch"], "scale_write": scale["write"],
                    "source_sha256": source_hash()}
             out.append("COUNTERS_JSON: " + json.dumps(rec))
+    # instruction / utilisation counters (passes "sq" and "tcc", several counters each)
+    multi = defaultdict(dict)
+    for c in ("sq", "tcc"):
+        p = os.path.join(d, c, "run_counter_collection.csv")
+        if not os.path.exists(p):
+            continue
+        groups = defaultdict(list)
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]), int(r["LDS_Block_Size"]))
+                groups[(key, r["Counter_Name"])].append(float(r["Counter_Value"]))
+        for (key, name), v in groups.items():
+            multi[key][name] = float(np.mean(v))
+    if multi:
+        out.append("")
+        out.append("instruction and utilisation counters (rocprofv3 --pmc, mean per dispatch); per wave = / SQ_WAVES;")
+        out.append("mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * 4 * CUs), then divided by the same ratio")
+        out.append("of the dense register-only MFMA loop (mfma_peak_kernel), so that loop reads 1.0;")
+        out.append("l2_hit = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum); lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE")
+        raw = {k: (v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / max(1.0, v.get("GRBM_GUI_ACTIVE", 0.0) * 4 * 256))
+               for k, v in multi.items()}
+        ref = [raw[k] for k in raw if k[0].startswith("mfma_peak_kernel")]
+        norm = max(ref) if ref else None
+        out.append(f"{'kernel':70s} {'grid':>8s} {'waves':>8s} {'VALU/w':>8s} {'SALU/w':>8s} {'MFMA/w':>8s} "
+                   f"{'LDS/w':>7s} {'mfma_busy':>9s} {'l2_hit':>7s} {'lds_cfl':>7s}")
+        for k, v in sorted(multi.items()):
+            if "FillFunctor" in k[0] or "stream_copy" in k[0]:
+                continue
+            w = max(1.0, v.get("SQ_WAVES", 0.0))
+            hit, miss = v.get("TCC_HIT_sum"), v.get("TCC_MISS_sum")
+            l2 = f"{hit / (hit + miss):7.3f}" if hit is not None and miss is not None and hit + miss > 0 else f"{'-':>7s}"
+            lc = v.get("SQ_LDS_BANK_CONFLICT"), v.get("SQ_LDS_IDX_ACTIVE")
+            lcs = f"{lc[0] / lc[1]:7.3f}" if lc[0] is not None and lc[1] else f"{'-':>7s}"
+            mb = f"{raw[k] / norm:9.3f}" if norm and "SQ_VALU_MFMA_BUSY_CYCLES" in v else f"{'-':>9s}"
+            out.append(f"{k[0][:70]:70s} {k[1]:8d} {w:8.0f} {v.get('SQ_INSTS_VALU', 0) / w:8.1f} "
+                       f"{v.get('SQ_INSTS_SALU', 0) / w:8.1f} {v.get('SQ_INSTS_MFMA', 0) / w:8.1f} "
+                       f"{v.get('SQ_INSTS_LDS', 0) / w:7.1f} {mb} {l2} {lcs}")
     return "\n".join(out)
 
 
@@ -634,6 +686,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.profile:
+        profile_path(torch, qlin, synth, args.profile, args.iters)
+        return
     if args.sweep == "batch":
         print(json.dumps(sweep_batch(torch, qlin, synth, max(20, args.steps // 4))), flush=True)
         return
@@ -646,18 +701,20 @@ def main():
 
     # ---- headline: W4 GEMV, Llama-7B-shaped layers, M = 1
     layers = w4_layers(torch, qlin, synth, "w4_llama7b", 1)
-    fns = w4_step_fns(qlin, layers)
+    fns = w4_step_fns(qlin, layers, 1)
     ms_step, per = time_steps(torch, fns, args.steps, args.warmup, len(layers[0]["packed"]))
-    step_bytes = sum(l["wbytes"] + l["io"] for l in layers)
+    step_bytes = sum(l["wbytes"] + l["ios"][1] for l in layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     kern_ms = sum(per)
     achieved = step_bytes / (kern_ms * 1e-3) / 1e9
-    per_layer = [{"shape": f"{l['N']}x{l['K']}", "bytes": l["wbytes"] + l["io"], "us": round(p * 1e3, 3),
-                  "GB/s": round((l["wbytes"] + l["io"]) / (p * 1e-3) / 1e9, 1)} for l, p in zip(layers, per)]
+    layer_bytes = [l["wbytes"] + l["ios"][1] for l in layers]
+    per_layer = [{"shape": f"{l['N']}x{l['K']}", "bytes": b, "us": round(p * 1e3, 3),
+                  "GB/s": round(b / (p * 1e-3) / 1e9, 1)} for l, b, p in zip(layers, layer_bytes, per)]
     rot = len(layers[0]["packed"])
     del layers, fns
     torch.cuda.empty_cache()
 
+    peaks = measured_peaks(torch, qlin, layer_bytes)
     out = {
         "metric": "quantized-linear GB/s at M=1 (% HBM peak); TOPS at M=256 (% MFMA peak)",
         "value": round(value, 1),
@@ -677,51 +734,190 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
                      "kernel": "w4_gemv_kernel", "per": "step of three launches (bytes per step / kernel time per step)",
-                     "algorithmic_bytes": step_bytes, "per_layer": per_layer},
+                     "algorithmic_bytes": step_bytes, "per_layer": per_layer,
+                     "measured_peak": peaks["hbm_read_GB/s"],
+                     "frac_measured_peak": round(achieved / peaks["hbm_read_GB/s"], 4),
+                     "stream_read_floor_us": peaks["floor_us"],
+                     "frac_of_floor": round(sum(peaks["floor_us"]) / (kern_ms * 1e3), 4)},
+        "measured_peaks": {k: v for k, v in peaks.items() if k != "floor_us"},
     }
 
     if not args.no_paths:
-        paths = {}
-        steps = max(20, args.steps // 4)
-        warm = max(5, args.warmup // 4)
-        # SpQR M=1
-        L = spqr_layers(torch, qlin, synth, 1)
-        ms, per = time_steps(torch, spqr_step_fns(qlin, L), steps, warm, len(L[0]["packed"]))
-        b = sum(l["wbytes"] + l["io"] for l in L)
-        paths["spqr_33b_M1"] = {"value": round(b / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                                "kernel_GB/s": round(b / (sum(per) * 1e-3) / 1e9, 1),
-                                "frac_hbm": round(b / (sum(per) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                "per_layer_us": [round(p * 1e3, 2) for p in per]}
-        del L
-        torch.cuda.empty_cache()
-        # W4 GEMM M=256
-        L = w4_layers(torch, qlin, synth, "w4_llama70b", 256)
-        ms, per = time_steps(torch, w4_step_fns(qlin, L), steps, warm, len(L[0]["packed"]))
-        fl = sum(2.0 * l["M"] * l["N"] * l["K"] for l in L)
-        tf = fl / (sum(per) * 1e-3) / 1e12
-        paths["w4_llama70b_M256"] = {"value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                                     "kernel_TFLOP/s": round(tf, 2), "frac_mfma_f16": round(tf / 2500.0, 4),
-                                     "per_layer_us": [round(p * 1e3, 2) for p in per]}
-        del L
-        torch.cuda.empty_cache()
-        # SmoothQuant M=256
-        L = sq_layers(torch, qlin, synth, 256)
-        act, gemm = sq_step_fns(qlin, L)
-        ms, per = time_steps(torch, [f for pair in zip(act, gemm) for f in pair], steps, warm, len(L[0]["packed"]))
-        ops = sum(2.0 * l["M"] * l["N"] * l["K"] for l in L)
-        gemm_ms = per[1] + per[3]
-        tops = ops / (gemm_ms * 1e-3) / 1e12
-        paths["sq_w8a8_M256"] = {"value": round(ops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS (act+gemm)",
-                                 "gemm_kernel_TOPS": round(tops, 2), "frac_mfma_i8": round(tops / 5000.0, 4),
-                                 "act_us": [round(per[0] * 1e3, 2), round(per[2] * 1e3, 2)],
-                                 "gemm_us": [round(per[1] * 1e3, 2), round(per[3] * 1e3, 2)]}
-        del L
-        torch.cuda.empty_cache()
-        out["paths"] = paths
+        out["paths"] = run_paths(torch, qlin, synth, max(20, args.steps // 4), max(5, args.warmup // 4), peaks)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(synth)
     print(json.dumps(out), flush=True)
+
+
+def profile_path(torch, qlin, synth, names, iters):
+    """Run workload points eagerly `iters` times each over their weight rotation
+    (every launch reads its weights from HBM), for rocprofv3.  names: comma-
+    separated, e.g. "spqr_33b_M1,spqr_33b_M16" (points of one workload share
+    its packed weights) or "mfma_peak_f16"."""
+    groups = {}
+    for name in names.split(","):
+        if name.startswith("mfma_peak_"):
+            kind = {"f16": 0, "bf16": 1, "i8": 2}[name[len("mfma_peak_"):]]
+            out = torch.empty(2048 * 4, dtype=torch.float32, device="cuda")
+            for _ in range(iters):
+                qlin.qlin_mfma_peak(kind, 2000, 2048, out)
+            torch.cuda.synchronize()
+            print(json.dumps({"profiled": name, "iters": iters}), flush=True)
+            continue
+        workload, M = name.rsplit("_M", 1)
+        groups.setdefault(workload, []).append(int(M))
+    for workload, Ms in groups.items():
+        if workload == "sq_w8a8":
+            L = sq_layers(torch, qlin, synth, Ms)
+        elif workload == "spqr_33b":
+            L = spqr_layers(torch, qlin, synth, Ms)
+        else:
+            L = w4_layers(torch, qlin, synth, workload, Ms)
+        copies = len(L[0]["packed"])
+        for M in Ms:
+            if workload == "sq_w8a8":
+                act, gemm = sq_step_fns(qlin, L, M)
+                fns = [f for pair in zip(act, gemm) for f in pair]
+            elif workload == "spqr_33b":
+                fns = spqr_step_fns(qlin, L, M)
+            else:
+                fns = w4_step_fns(qlin, L, M)
+            for i in range(iters):
+                for f in fns:
+                    f(i % copies)
+            torch.cuda.synchronize()
+            print(json.dumps({"profiled": f"{workload}_M{M}", "iters": iters, "launches": iters * len(fns)}),
+                  flush=True)
+        del L
+        torch.cuda.empty_cache()
+
+
+def measured_peaks(torch, qlin, floor_bytes):
+    """Achievable rates measured on this GPU, next to the datasheet figures:
+    a plain non-temporal streaming read of 2 GiB (16-byte loads, best of 5), the
+    same read at each headline layer's byte count from a rotation of 1 GiB of
+    buffers (the floor a single launch of that size can reach), and dense
+    register-only MFMA loops per data type (best of 5)."""
+    res = {}
+    nb = 2 << 30
+    buf = torch.empty(nb // 4, dtype=torch.int32, device="cuda")
+    out = torch.empty(1 << 16, dtype=torch.int32, device="cuda")
+    best = None
+    for _ in range(5):
+        ms = _event_ms(torch, lambda: qlin.qlin_stream_read(buf, nb, 8192, 8, 1, out))
+        best = ms if best is None else min(best, ms)
+    res["hbm_read_GB/s"] = round(nb / (best * 1e-3) / 1e9, 1)
+    del buf
+    floors = []
+    for b in floor_bytes:
+        b16 = (b + 15) // 16 * 16
+        copies = copies_for(b16)
+        bufs = [torch.empty(b16 // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
+        grid = max(256, min(8192, b16 // (16 * 256 * 8) + 1))
+        g = _graph(torch, lambda: [qlin.qlin_stream_read(x, b16, grid, 8, 1, out) for x in bufs])
+        floors.append(round(_replay_ms(torch, g, 10) / copies * 1e3, 3))
+        del g, bufs
+    res["floor_us"] = floors
+    flops = {0: 32768.0, 1: 32768.0, 2: 65536.0}
+    grid, iters = 2048, 2000
+    pk = torch.empty(grid * 4, dtype=torch.float32, device="cuda")
+    res["mfma_TFLOP/s"] = {}
+    for kind, name in ((0, "f16"), (1, "bf16"), (2, "i8")):
+        best = None
+        for _ in range(5):
+            ms = _event_ms(torch, lambda: qlin.qlin_mfma_peak(kind, iters, grid, pk))
+            best = ms if best is None else min(best, ms)
+        res["mfma_TFLOP/s"][name] = round(grid * 4 * iters * 4 * flops[kind] / (best * 1e-3) / 1e12, 1)
+    torch.cuda.empty_cache()
+    return res
+
+
+def _event_ms(torch, f):
+    f()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    f()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def _rate_record(bytes_, ops, kern_us, mfma_kind, peaks, extra=None):
+    """Rates of one timed kernel set against both rooflines: HBM (algorithmic
+    bytes at 8 TB/s) and MFMA (algorithmic ops at the dtype's dense peak), with
+    the binding one and the fraction of its ideal time reached; also against
+    the measured peaks."""
+    peak_tf = MFMA_PEAK_TFLOPS[mfma_kind] if mfma_kind else None
+    t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9) * 1e6
+    t_mfma = ops / (peak_tf * 1e12) * 1e6 if peak_tf else 0.0
+    mh = peaks["hbm_read_GB/s"]
+    mt = peaks["mfma_TFLOP/s"][mfma_kind] if mfma_kind else None
+    t_hbm_m = bytes_ / (mh * 1e9) * 1e6
+    t_mfma_m = ops / (mt * 1e12) * 1e6 if mt else 0.0
+    rec = {"kernel_us": round(kern_us, 2), "bytes": int(bytes_), "ops": int(ops),
+           "GB/s": round(bytes_ / (kern_us * 1e-6) / 1e9, 1),
+           "TOPS": round(ops / (kern_us * 1e-6) / 1e12, 2),
+           "frac_hbm": round(bytes_ / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+           "roofline_us": round(max(t_hbm, t_mfma), 3),
+           "frac_roofline": round(max(t_hbm, t_mfma) / kern_us, 4),
+           "frac_measured_roofline": round(max(t_hbm_m, t_mfma_m) / kern_us, 4)}
+    if peak_tf:
+        rec["frac_mfma"] = round(ops / (kern_us * 1e-6) / 1e12 / peak_tf, 4)
+    if extra:
+        rec.update(extra)
+    return rec
+
+
+# batch sizes timed per workload besides the headline (the configurations'
+# own M sets; 256 added for the int8 GEMM, where the metric is quoted)
+PATH_POINTS = (("w4_1k", (1, 4)), ("spqr_33b", (1, 4, 16)), ("w4_llama70b", (32, 64, 256)),
+               ("sq_w8a8", (256, 512, 2048)))
+
+
+def run_paths(torch, qlin, synth, steps, warm, peaks):
+    paths = {}
+    for workload, Ms in PATH_POINTS:
+        if workload == "sq_w8a8":
+            L = sq_layers(torch, qlin, synth, Ms)
+        elif workload == "spqr_33b":
+            L = spqr_layers(torch, qlin, synth, Ms)
+        else:
+            L = w4_layers(torch, qlin, synth, workload, Ms)
+        copies = len(L[0]["packed"])
+        for M in Ms:
+            key = f"{workload}_M{M}"
+            if workload == "sq_w8a8":
+                act, gemm = sq_step_fns(qlin, L, M)
+                ms, per = time_steps(torch, [f for pair in zip(act, gemm) for f in pair], steps, warm, copies)
+                act_us = [per[2 * i] * 1e3 for i in range(len(L))]
+                gemm_us = [per[2 * i + 1] * 1e3 for i in range(len(L))]
+                ops = sum(2.0 * M * l["N"] * l["K"] for l in L)
+                gb = sum(l["wbytes"] + M * l["K"] + 4 * M + 2 * M * l["N"] for l in L)
+                ab = sum(2 * M * l["K"] + 4 * l["K"] + M * l["K"] + 4 * M for l in L)
+                paths[key] = {"unit": "TOPS", "us_per_step": round(ms * 1e3, 2),
+                              "gemm": _rate_record(gb, ops, sum(gemm_us), "i8", peaks,
+                                                   {"per_layer_us": [round(x, 2) for x in gemm_us]}),
+                              "act": _rate_record(ab, 0, sum(act_us), None, peaks,
+                                                  {"per_layer_us": [round(x, 2) for x in act_us]}),
+                              "TOPS_act_plus_gemm": round(ops / (ms * 1e-3) / 1e12, 2)}
+            else:
+                fns = spqr_step_fns(qlin, L, M) if workload == "spqr_33b" else w4_step_fns(qlin, L, M)
+                ms, per = time_steps(torch, fns, steps, warm, copies)
+                us = [p * 1e3 for p in per]
+                bytes_ = sum(l["wbytes"] + l["ios"][M] for l in L)
+                ops = sum(2.0 * M * l["N"] * l["K"] + 2.0 * M * l.get("nnz", 0) for l in L)
+                kind = "bf16" if workload == "w4_llama70b" else "f16"
+                paths[key] = _rate_record(bytes_, ops, sum(us), kind, peaks,
+                                          {"us_per_step": round(ms * 1e3, 2),
+                                           "per_layer_us": [round(x, 2) for x in us]})
+            print(json.dumps({"path": key, **paths[key]}), file=sys.stderr, flush=True)
+        del L
+        torch.cuda.empty_cache()
+    return paths
 
 
 if __name__ == "__main__":

@@ -361,6 +361,13 @@ qlin_status qlin_stream_read(const void* buf, size_t bytes, int grid, int unroll
  * + bytes written) against which hardware fetch/write counters are scaled. */
 qlin_status qlin_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
+/* Dense matrix-core throughput reference: `grid` workgroups of 256 threads, each
+ * wave issuing `iters` rounds of 4 independent register-only instructions of
+ * kind 0 (v_mfma_f32_32x32x16_f16, 32768 flops each), 1 (..._bf16, 32768) or
+ * 2 (v_mfma_i32_32x32x32_i8, 65536 ops); out (device float [grid * 4]) gets one
+ * value per wave.  Not part of the layer computation. */
+qlin_status qlin_mfma_peak(int kind, int iters, int grid, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,6 +1,7 @@
 // Measurement aids: a plain streaming read of a device buffer (the achievable
-// bandwidth reference for the memory-bound kernels) and a plain copy (the
-// known-size reference that scales the hardware byte counters).  Each thread reads 16-byte
+// bandwidth reference for the memory-bound kernels), a plain copy (the
+// known-size reference that scales the hardware byte counters) and a dense
+// matrix-core loop per data type (the achievable MFMA rate).  Each thread reads 16-byte
 // vectors (coalesced, 64 lanes x 16 B per instruction) and folds them with XOR;
 // one word per workgroup is written so the loads cannot be removed.
 
@@ -44,10 +45,69 @@ __global__ __launch_bounds__(kThreads) void stream_copy_kernel(uint4* __restrict
   for (size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Every wave runs `iters` rounds of kChains independent matrix instructions on
+// register operands (no memory traffic; the chains hide the instruction's
+// latency) and writes one value, so nothing is removed.
+constexpr int kChains = 4;
+
+template <int KIND>   // 0: v_mfma_f32_32x32x16_f16, 1: _bf16, 2: v_mfma_i32_32x32x32_i8
+__global__ __launch_bounds__(kThreads) void mfma_peak_kernel(int iters, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t seed = 0x3C003C00u ^ static_cast<uint32_t>(lane);
+  if constexpr (KIND == 2) {
+    const i32x4_t a = {static_cast<int>(seed), static_cast<int>(seed >> 1), 3, 5};
+    const i32x4_t b = {7, static_cast<int>(seed >> 2), 11, 13};
+    i32x16_t acc[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) acc[c] = i32x16_t{};
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[c], 0, 0, 0);
+    int s = 0;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][15];
+    if (lane == 0) out[(blockIdx.x * kThreads + threadIdx.x) >> 6] = static_cast<float>(s);
+  } else {
+    typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+    h8_t ah, bh;
+    bf8_t ab, bb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ah[j] = static_cast<_Float16>(1.0f / static_cast<float>(lane + j + 1));
+      bh[j] = static_cast<_Float16>(0.5f);
+      ab[j] = static_cast<__bf16>(1.0f / static_cast<float>(lane + j + 1));
+      bb[j] = static_cast<__bf16>(0.5f);
+    }
+    f32x16_t acc[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) acc[c] = f32x16_t{};
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int c = 0; c < kChains; ++c) {
+        if constexpr (KIND == 0) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc[c], 0, 0, 0);
+        else acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, bb, acc[c], 0, 0, 0);
+      }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][15];
+    if (lane == 0) out[(blockIdx.x * kThreads + threadIdx.x) >> 6] = s;
+  }
+}
+
 }  // namespace
 }  // namespace qlin
 
 using namespace qlin;
+
+extern "C" qlin_status qlin_mfma_peak(int kind, int iters, int grid, float* out, hipStream_t stream) {
+  clear_error();
+  if (kind < 0 || kind > 2 || iters <= 0 || grid <= 0 || !out)
+    return fail(QLIN_EINVAL, "qlin_mfma_peak: kind 0..2, iters > 0, grid > 0, non-NULL out");
+  if (kind == 0) hipLaunchKernelGGL(mfma_peak_kernel<0>, dim3(grid), dim3(kThreads), 0, stream, iters, out);
+  else if (kind == 1) hipLaunchKernelGGL(mfma_peak_kernel<1>, dim3(grid), dim3(kThreads), 0, stream, iters, out);
+  else hipLaunchKernelGGL(mfma_peak_kernel<2>, dim3(grid), dim3(kThreads), 0, stream, iters, out);
+  return check_launch("qlin_mfma_peak");
+}
 
 extern "C" qlin_status qlin_stream_read(const void* buf, size_t bytes, int grid, int unroll, int nontemporal,
                                         uint32_t* out, hipStream_t stream) {

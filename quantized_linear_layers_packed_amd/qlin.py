@@ -47,6 +47,7 @@ EXPORTS = (
     "qlin_hessian", "qlin_w4_pack_gptq", "spqr_pack_hessian",
     "qlin_w4_pack_gptq_actorder", "qlin_w4_forward_perm",
     "qlin_w4_workspace_bytes", "sq_int8_gemm_workspace_bytes", "qlin_w4_forward_scratch",
+    "qlin_mfma_peak",
 )
 
 _vp, _i, _i64, _sz, _d = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.c_double
@@ -72,6 +73,7 @@ _sigs = {
     "sq_int8_gemm_workspace_bytes": ([_i, _i, _i, _i, _vp], _i),
     "qlin_stream_read": ([_vp, _sz, _i, _i, _i, _vp, _vp], _i),
     "qlin_stream_copy": ([_vp, _vp, _sz, _vp], _i),
+    "qlin_mfma_peak": ([_i, _i, _i, _vp, _vp], _i),
     "qlin_hessian": ([_vp, _i, _i, _vp], _i),
     "qlin_w4_pack_gptq": ([_vp, _i, _i, _i, _vp, _d, _vp, _vp, _vp], _i),
     "spqr_pack_hessian": ([_vp, _i, _i, _d, _vp, _d, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp], _i),
@@ -348,6 +350,10 @@ def sq_int8_gemm(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype=QLIN_F16, acc_out
 def qlin_stream_read(buf, nbytes, grid, unroll, nontemporal, out, stream=None):
     _check(_lib.qlin_stream_read(_ptr(buf), nbytes, grid, unroll, int(bool(nontemporal)), _ptr(out),
                                  _stream(stream)))
+
+
+def qlin_mfma_peak(kind, iters, grid, out, stream=None):
+    _check(_lib.qlin_mfma_peak(kind, iters, grid, _ptr(out), _stream(stream)))
 
 
 def qlin_stream_copy(dst, src, nbytes, stream=None):
