@@ -204,6 +204,9 @@ def spqr_layers(torch, qlin, synth, Ms):
         wbytes = sum(t.numel() * t.element_size() for t in packed)
         layers.append(dict(N=N, K=K, nnz=len(st["val"]), packed=[packed], Xs=X, Ys=Y, wbytes=wbytes,
                            ios={M: M * K * 2 + M * N * 2 for M in Ms}))
+    ws = zeros_ws(torch, max(qlin.spqr_workspace_bytes(M, l["K"], l["N"], qlin.QLIN_F16) for l in layers for M in Ms))
+    for l in layers:
+        l["ws"] = ws
     rotate(torch, layers)
     return layers
 
@@ -214,7 +217,7 @@ def spqr_step_fns(qlin, layers, M):
         def f(i, l=l):
             c, s1, s2, rp, ci, v = l["packed"][i % len(l["packed"])]
             qlin.spqr_forward(l["Xs"][M], M, l["K"], c, s1, s2, rp, ci, v, l["nnz"], l["N"], l["Ys"][M],
-                              qlin.QLIN_F16)
+                              qlin.QLIN_F16, workspace=l["ws"])
         fns.append(f)
     return fns
 
@@ -383,6 +386,7 @@ def sweep_outliers(torch, qlin, synth, steps):
     Ms = (1, 4)
     Xd = {M: [to_dev(torch, synth.activations("spqr_33b", li, M)) for li in range(len(shapes))] for M in Ms}
     Yd = {M: [torch.empty((M, N), dtype=torch.float16, device="cuda") for N, _ in shapes] for M in Ms}
+    wsp = zeros_ws(torch, max(qlin.spqr_workspace_bytes(M, K, N, qlin.QLIN_F16) for M in Ms for N, K in shapes))
     Ws = []
     for li in range(len(shapes)):
         Ws.append(synth.layer_weight("spqr_33b", li))
@@ -412,7 +416,8 @@ def sweep_outliers(torch, qlin, synth, steps):
             def f(i, M=M):
                 for li, (N, K) in enumerate(shapes):
                     c, s1, s2, rp, ci, v = sets[i % R][li]
-                    qlin.spqr_forward(Xd[M][li], M, K, c, s1, s2, rp, ci, v, nnz[li], N, Yd[M][li], qlin.QLIN_F16)
+                    qlin.spqr_forward(Xd[M][li], M, K, c, s1, s2, rp, ci, v, nnz[li], N, Yd[M][li], qlin.QLIN_F16,
+                                      workspace=wsp)
             ms = graph_step_ms(torch, [f], R, steps)
             if p == 0.0:
                 t0[M] = ms
@@ -874,7 +879,7 @@ def _rate_record(bytes_, ops, kern_us, mfma_kind, peaks, extra=None):
 
 # batch sizes timed per workload besides the headline (the configurations'
 # own M sets; 256 added for the int8 GEMM, where the metric is quoted)
-PATH_POINTS = (("w4_1k", (1, 4)), ("spqr_33b", (1, 4, 16)), ("w4_llama70b", (32, 64, 256)),
+PATH_POINTS = (("w4_1k", (1, 4)), ("spqr_33b", (1, 4, 8, 16)), ("w4_llama70b", (32, 64, 256)),
                ("sq_w8a8", (256, 512, 2048)))
 
 

@@ -38,14 +38,16 @@
  *   - Calls on distinct streams may run concurrently as long as they do not
  *     share a workspace.  The library keeps no state besides the thread-local
  *     error message and a per-device cache of the compute-unit count.
- *   - Workspace (qlin_w4_forward, qlin_w4_forward_perm, sq_int8_gemm): device
+ *   - Workspace (qlin_w4_forward, qlin_w4_forward_perm, spqr_forward,
+ *     sq_int8_gemm): device
  *     memory of at least the size the matching *_workspace_bytes call reports
  *     for the shape (0 means none is needed and NULL may be passed), 16-byte
- *     aligned.  Its first 16 KiB are arrival counters that must be zero before
- *     the first call using the workspace (fill the whole buffer with zeros
- *     once after allocating it); every call leaves them zero again when it
- *     completes, so one workspace, sized for the largest shape, can serve any
- *     sequence of calls and shapes on one stream.  Calls sharing a workspace
+ *     aligned.  Fill the whole buffer with zeros once after allocating it:
+ *     the split-K kernels keep arrival counters in its first 16 KiB, which
+ *     must be zero when a call starts; every call leaves them zero again when
+ *     it completes, and calls that need no counters keep their data after
+ *     them, so one workspace, sized for the largest shape, can serve any
+ *     sequence of calls, entry points and shapes on one stream.  Calls sharing a workspace
  *     must not overlap in time.  Everything else in it is scratch.  A too small
  *     or NULL workspace where one is needed gives EINVAL, with the needed size
  *     in qlin_last_error().
@@ -219,16 +221,28 @@ qlin_status spqr_pack(const float* W, int N, int K, double outlier_frac,
                       int32_t* row_ptr, int32_t* col_idx, uint16_t* vals,
                       int64_t nnz_cap, int64_t* nnz_out);
 
+/* Device workspace bytes spqr_forward needs for this batch size (0: none) on
+ * the current device.  Errors as spqr_forward's shape checks, EINVAL for a NULL
+ * bytes. */
+qlin_status spqr_workspace_bytes(int M, int K, int N, int y_dtype, size_t* bytes);
+
 /* Y = X . (W_dense + W_sparse)^T on the GPU.  X fp16 [M][K] (device), Y [M][N]
  * (device, y_dtype QLIN_F16 or QLIN_F32).  The CSR row of output n is added into
  * the same fp32 accumulator as the dense dot product, in the same kernel pass.
+ * 1 <= M <= 5 runs a fused GEMV on the exact codes (no workspace).  6 <= M <= 16
+ * runs a matrix-core kernel: a small prepass lays the activations out in the
+ * workspace (operand order, group sums and a transposed copy, K * 68 bytes),
+ * then each group's exact codes go through v_mfma_f32_16x16x16_f16 with the
+ * group statistics applied in fp32.  workspace / workspace_bytes: as for
+ * qlin_w4_forward (conventions at the top; size from spqr_workspace_bytes).
  * Requirements: 1 <= M <= 16, K % 256 == 0, row_ptr consistent with nnz
  * (row_ptr[0] = 0, row_ptr[N] = nnz, checked only for nnz >= 0 on the host:
  * the device arrays are trusted). */
 qlin_status spqr_forward(const uint16_t* X, int M, int K,
                          const uint32_t* codes, const uint32_t* stats1, const uint16_t* stats2,
                          const int32_t* row_ptr, const int32_t* col_idx, const uint16_t* vals,
-                         int64_t nnz, int N, void* Y, int y_dtype, hipStream_t stream);
+                         int64_t nnz, int N, void* Y, int y_dtype, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /* Debug: unpack the dense codes (uint8 [N][K]) and the first-level statistic
  * codes c_s, c_z (uint8 [N][K/16]) on the GPU with the forward kernel's routine. */

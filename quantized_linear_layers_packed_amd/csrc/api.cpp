@@ -206,10 +206,23 @@ qlin_status qlin_w4_unpack(const uint32_t* qweight, const uint32_t* qzeros, int 
   return check_launch(fn);
 }
 
+qlin_status spqr_workspace_bytes(int M, int K, int N, int y_dtype, size_t* bytes) {
+  static const char* fn = "spqr_workspace_bytes";
+  clear_error();
+  if (!bytes) return fail(QLIN_EINVAL, std::string(fn) + ": NULL bytes");
+  if (M <= 0 || N <= 0 || K <= 0) return fail(QLIN_EINVAL, std::string(fn) + ": M, N, K must be positive");
+  if (M > 16) return fail(QLIN_EUNSUPPORTED, std::string(fn) + ": M must be at most 16");
+  if (K % 256 != 0) return fail(QLIN_EINVAL, std::string(fn) + ": K must be a multiple of 256");
+  if (y_dtype != QLIN_F16 && y_dtype != QLIN_F32) return fail(QLIN_EINVAL, std::string(fn) + ": y_dtype must be F16 or F32");
+  *bytes = M >= QLIN_SPQR_MFMA_MIN_M ? kCounterBytes + spqr_prep_bytes(K) : 0;
+  return QLIN_OK;
+}
+
 qlin_status spqr_forward(const uint16_t* X, int M, int K,
                          const uint32_t* codes, const uint32_t* stats1, const uint16_t* stats2,
                          const int32_t* row_ptr, const int32_t* col_idx, const uint16_t* vals,
-                         int64_t nnz, int N, void* Y, int y_dtype, hipStream_t stream) {
+                         int64_t nnz, int N, void* Y, int y_dtype, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
   static const char* fn = "spqr_forward";
   clear_error();
   if (M <= 0 || N <= 0 || K <= 0) return fail(QLIN_EINVAL, std::string(fn) + ": M, N, K must be positive");
@@ -224,8 +237,13 @@ qlin_status spqr_forward(const uint16_t* X, int M, int K,
   QLIN_TRY(need_aligned(fn, "stats1", stats1));
   QLIN_TRY(need_aligned(fn, "stats2", stats2));
   QLIN_TRY(need_aligned(fn, "Y", Y));
+  // the prepass area starts after the counter slots, which stay untouched, so
+  // one workspace can serve this call and the split-K calls in any order
+  const size_t total = M >= QLIN_SPQR_MFMA_MIN_M ? kCounterBytes + spqr_prep_bytes(K) : 0;
+  QLIN_TRY(need_workspace(fn, workspace, workspace_bytes, total));
   SpqrArgs a{X, M, K, N, codes, stats1, stats2, row_ptr, col_idx, vals, Y, y_dtype};
-  spqr_gemv_launch(a, stream);
+  if (total) spqr_mfma_launch(a, spqr_prep_view(static_cast<char*>(workspace) + kCounterBytes, K), stream);
+  else spqr_gemv_launch(a, stream);
   return check_launch(fn);
 }
 

@@ -66,6 +66,20 @@ struct SpqrArgs {
 };
 
 void spqr_gemv_launch(const SpqrArgs& a, hipStream_t stream);
+
+// Matrix-core path for small batches: activations laid out by a prepass in the
+// workspace (Xp: MFMA operand order, Xs: group sums, XT: transposed copy).
+struct SpqrPrep {
+  const uint4* Xp;
+  const float* Xs;
+  const uint16_t* XT;
+};
+#ifndef QLIN_SPQR_MFMA_MIN_M
+#define QLIN_SPQR_MFMA_MIN_M 6        // batches from this size run the matrix-core path
+#endif
+size_t spqr_prep_bytes(int K);
+SpqrPrep spqr_prep_view(char* base, int K);
+void spqr_mfma_launch(const SpqrArgs& a, const SpqrPrep& p, hipStream_t stream);
 void spqr_unpack_launch(const uint32_t* codes, const uint32_t* stats1, int N, int K,
                         uint8_t* q, uint8_t* cs, uint8_t* cz, hipStream_t stream);
 

@@ -47,7 +47,7 @@ EXPORTS = (
     "qlin_hessian", "qlin_w4_pack_gptq", "spqr_pack_hessian",
     "qlin_w4_pack_gptq_actorder", "qlin_w4_forward_perm",
     "qlin_w4_workspace_bytes", "sq_int8_gemm_workspace_bytes", "qlin_w4_forward_scratch",
-    "qlin_mfma_peak",
+    "qlin_mfma_peak", "spqr_workspace_bytes",
 )
 
 _vp, _i, _i64, _sz, _d = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.c_double
@@ -63,7 +63,8 @@ _sigs = {
     "qlin_w4_unpack": ([_vp, _vp, _i, _i, _i, _vp, _vp, _vp], _i),
     "spqr_sizes": ([_i, _i, _d, _vp, _vp, _vp, _vp], _i),
     "spqr_pack": ([_vp, _i, _i, _d, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp], _i),
-    "spqr_forward": ([_vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i, _vp, _i, _vp], _i),
+    "spqr_forward": ([_vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i, _vp, _i, _vp, _sz, _vp], _i),
+    "spqr_workspace_bytes": ([_i, _i, _i, _i, _vp], _i),
     "spqr_unpack": ([_vp, _vp, _i, _i, _vp, _vp, _vp, _vp], _i),
     "sq_act_absmax": ([_vp, _i, _i, _vp], _i),
     "sq_compute_smoothing": ([_vp, _vp, _i, _i, _d, _vp, _vp], _i),
@@ -287,10 +288,17 @@ def spqr_pack_hessian(W: np.ndarray, outlier_frac: float, H: np.ndarray, damp: f
                 col_idx=ci[:n].copy(), val=vals[:n].view(np.float16).copy())
 
 
+def spqr_workspace_bytes(M, K, N, y_dtype=QLIN_F16):
+    b = C.c_size_t()
+    _check(_lib.spqr_workspace_bytes(M, K, N, y_dtype, C.byref(b)))
+    return b.value
+
+
 def spqr_forward(X, M, K, codes, stats1, stats2, row_ptr, col_idx, vals, nnz, N, Y, y_dtype=QLIN_F16,
-                 stream=None):
+                 workspace=None, workspace_bytes=None, stream=None):
     _check(_lib.spqr_forward(_ptr(X), M, K, _ptr(codes), _ptr(stats1), _ptr(stats2), _ptr(row_ptr),
-                             _ptr(col_idx), _ptr(vals), nnz, N, _ptr(Y), y_dtype, _stream(stream)))
+                             _ptr(col_idx), _ptr(vals), nnz, N, _ptr(Y), y_dtype, _ptr(workspace),
+                             _nbytes(workspace, workspace_bytes), _stream(stream)))
 
 
 def spqr_unpack(codes, stats1, N, K, q, cs, cz, stream=None):

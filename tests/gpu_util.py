@@ -68,6 +68,11 @@ def w4_ws(x_dtype, M, K, N, G, y_dtype):
     return workspace(qlin.qlin_w4_workspace_bytes(x_dtype, M, K, N, G, y_dtype))
 
 
+def spqr_ws(M, K, N, y_dtype):
+    from quantized_linear_layers_packed_amd import qlin
+    return workspace(qlin.spqr_workspace_bytes(M, K, N, y_dtype))
+
+
 def sq_ws(M, N, K, y_dtype):
     from quantized_linear_layers_packed_amd import qlin
     return workspace(qlin.sq_int8_gemm_workspace_bytes(M, N, K, y_dtype))

@@ -61,12 +61,20 @@ def test_w4_forward_rejects_bad_arguments():
 
 def test_spqr_forward_rejects_bad_arguments():
     fw = qlin.spqr_forward
-    _raises(qlin.QLIN_EINVAL, fw, FAKE, 1, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 64, FAKE, 1, 0)
-    _raises(qlin.QLIN_EUNSUPPORTED, fw, FAKE, 17, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 64, FAKE, 1, 0)
-    _raises(qlin.QLIN_EINVAL, fw, FAKE, 1, 1024, FAKE, FAKE, FAKE, FAKE, 0, 0, 10, 64, FAKE, 1, 0)
-    _raises(qlin.QLIN_EINVAL, fw, FAKE, 1, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 64, FAKE, 1, 0)
-    _raises(qlin.QLIN_EINVAL, fw, FAKE, 1, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 64, FAKE, 2, 0)
-    _raises(qlin.QLIN_EALIGN, fw, FAKE, 1, 1024, FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 64, FAKE, 1, 0)
+    _raises(qlin.QLIN_EINVAL, fw, FAKE, 1, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 64, FAKE, 1, stream=0)
+    _raises(qlin.QLIN_EUNSUPPORTED, fw, FAKE, 17, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 64, FAKE, 1, stream=0)
+    _raises(qlin.QLIN_EINVAL, fw, FAKE, 1, 1024, FAKE, FAKE, FAKE, FAKE, 0, 0, 10, 64, FAKE, 1, stream=0)
+    _raises(qlin.QLIN_EINVAL, fw, FAKE, 1, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 64, FAKE, 1, stream=0)
+    _raises(qlin.QLIN_EINVAL, fw, FAKE, 1, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 64, FAKE, 2, stream=0)
+    _raises(qlin.QLIN_EALIGN, fw, FAKE, 1, 1024, FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 64, FAKE, 1, stream=0)
+    # batches that take the matrix-core path need the prepass workspace (K * 68
+    # bytes), placed after the 16 KiB of split-K counters it leaves untouched
+    need = qlin.spqr_workspace_bytes(8, 1024, 64)
+    assert need == 16384 + 1024 * 32 + 1024 * 4 + 1024 * 32 and qlin.spqr_workspace_bytes(1, 1024, 64) == 0
+    msg = _raises(qlin.QLIN_EINVAL, fw, FAKE, 8, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 64, FAKE, 1, stream=0)
+    assert str(need) in msg
+    _raises(qlin.QLIN_EINVAL, fw, FAKE, 8, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 64, FAKE, 1, FAKE, need - 1,
+            stream=0)
 
 
 def test_sq_calls_reject_bad_arguments():

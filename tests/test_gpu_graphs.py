@@ -11,7 +11,7 @@ import pytest
 
 import synth
 from quantized_linear_layers_packed_amd import qlin
-from tests.gpu_util import dev, empty, host, say, sq_ws, torch_cuda, w4_ws
+from tests.gpu_util import dev, empty, host, say, spqr_ws, sq_ws, torch_cuda, w4_ws
 
 pytestmark = pytest.mark.gpu
 
@@ -31,17 +31,18 @@ def _calls():
         wsp = w4_ws(xd, M, 2048, 1536, 128, F32)
         out.append((f"w4 M={M}", lambda X=X, Y=Y, M=M, xd=xd, wsp=wsp: qlin.qlin_w4_forward(
             X, xd, M, 2048, qw, sc, qz, 1536, 128, Y, F32, workspace=wsp), Y))
-    # SpQR M=1 and 4
+    # SpQR M=1 (GEMV) and 8 (prepass + matrix-core kernel)
     Ws = synth.student_t3_f32((512, 2048), 0.02, "gpu/graph/spqr")
     st = qlin.spqr_pack(Ws, 0.01)
     d = {k: dev(np.ascontiguousarray(v)) for k, v in st.items()}
     nnz = len(st["val"])
-    for M in (1, 4):
+    for M in (1, 8):
         X = dev(synth.x_f16(M, 2048, f"gpu/graph/sx{M}"))
         Y = empty((M, 512), torch.float32)
-        out.append((f"spqr M={M}", lambda X=X, Y=Y, M=M: qlin.spqr_forward(
-            X, M, 2048, d["codes"], d["stats1"], d["stats2"], d["row_ptr"], d["col_idx"], d["val"], nnz, 512, Y, F32),
-            Y))
+        wsp = spqr_ws(M, 2048, 512, F32)
+        out.append((f"spqr M={M}", lambda X=X, Y=Y, M=M, wsp=wsp: qlin.spqr_forward(
+            X, M, 2048, d["codes"], d["stats1"], d["stats2"], d["row_ptr"], d["col_idx"], d["val"], nnz, 512, Y, F32,
+            workspace=wsp), Y))
     # W8A8: activation kernel + int8 GEMM (stream-K), M=200
     Wf = synth.normal_f32((1024, 2048), 0.02, "gpu/graph/sq")
     Xc = synth.x_f16(200, 2048, "gpu/graph/sqx")

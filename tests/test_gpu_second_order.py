@@ -11,7 +11,7 @@ import pytest
 from oracle import spqr as ospqr
 from oracle import w4 as ow4
 from quantized_linear_layers_packed_amd import qlin
-from tests.gpu_util import check_close, dev, empty, host, say, torch_cuda, w4_ws
+from tests.gpu_util import check_close, dev, empty, host, say, spqr_ws, torch_cuda, w4_ws
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +68,7 @@ def test_sensitivity_spqr_encode_through_the_fused_kernel():
         Y = empty((M, N), torch.float32)
         nnz = len(st["val"])
         qlin.spqr_forward(dev(X), M, K, d["codes"], d["stats1"], d["stats2"], d["row_ptr"],
-                          d["col_idx"], d["val"], nnz, N, Y, F32)
+                          d["col_idx"], d["val"], nnz, N, Y, F32, workspace=spqr_ws(M, K, N, F32))
         check_close(host(Y).astype(np.float64), ospqr.forward(X, st, K), f"spqr M={M}")
 
 

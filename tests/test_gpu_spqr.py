@@ -6,7 +6,7 @@ import pytest
 import synth
 from oracle import spqr as ospqr
 from quantized_linear_layers_packed_amd import qlin
-from tests.gpu_util import check_close, dev, empty, host, say, torch_cuda
+from tests.gpu_util import check_close, dev, empty, host, say, spqr_ws, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,8 @@ def gpu_spqr(X, d, N, K, y_dtype=F16):
     Y = empty((M, N), torch.float16 if y_dtype == F16 else torch.float32)
     nnz = int(d["col_idx"].numel())
     qlin.spqr_forward(dev(X), M, K, d["codes"], d["stats1"], d["stats2"], d["row_ptr"],
-                      d["col_idx"] if nnz else 0, d["val"] if nnz else 0, nnz, N, Y, y_dtype)
+                      d["col_idx"] if nnz else 0, d["val"] if nnz else 0, nnz, N, Y, y_dtype,
+                      workspace=spqr_ws(M, K, N, y_dtype))
     return host(Y).astype(np.float64)
 
 
@@ -49,7 +50,7 @@ def test_ragged_shapes(p):
         W = synth.student_t3_f32((N, K), 0.02, f"gpu/spqr/rag{N}")
         d = dev_pack(qlin.spqr_pack(W, p))
         st = ospqr.encode(W, p)
-        for M in (1, 2, 3, 4, 7, 16):
+        for M in (1, 2, 4, 5, 6, 7, 16):
             say(f"spqr N={N} K={K} p={p} M={M}")
             X = synth.x_f16(M, K, f"gpu/spqr/ragx{M}")
             ref = ospqr.forward(X, st, K)
@@ -68,7 +69,7 @@ def test_csr_part_alone_matches_sparse_product():
     s2[:, :, 2:] = 0.0
     st["stats2"] = s2
     d = dev_pack(st)
-    for M in (1, 4, 16):
+    for M in (1, 4, 8, 16):
         say(f"spqr csr-only M={M}")
         X = synth.x_f16(M, K, f"gpu/spqr/csrx{M}")
         ref = ospqr.forward(X, st, K)
@@ -88,8 +89,29 @@ def test_33b_full_layer_sampled_rows(layer):
     rows = np.unique(np.r_[0, N - 1, np.random.default_rng(layer).choice(N, 254, replace=False)])
     st = ospqr.encode_rows(W, 0.01, rows)
     del W
-    for M in (1, 4, 16):
+    for M in (1, 4, 8, 16):
         say(f"spqr_33b layer {layer} {N}x{K} M={M}")
         X = synth.activations("spqr_33b", layer, M)
         Y = gpu_spqr(X, d, N, K, F16)
         check_close(Y[:, rows], ospqr.forward(X, st, K), f"{N}x{K} M={M}")
+
+
+def test_matrix_core_path_leaves_the_counter_slots_zero():
+    """The prepass writes after the 16 KiB of split-K arrival counters, so a
+    workspace shared with the W4 and int8 GEMMs still has them zero."""
+    torch = torch_cuda()
+    N, K, M = 48, 1024, 8
+    W = synth.student_t3_f32((N, K), 0.02, "gpu/spqr/wsctr")
+    d = dev_pack(qlin.spqr_pack(W, 0.01))
+    need = qlin.spqr_workspace_bytes(M, K, N, F32)
+    assert need > 16384
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    X = synth.x_f16(M, K, "gpu/spqr/wsctrx")
+    Y = empty((M, N), torch.float32)
+    nnz = int(d["col_idx"].numel())
+    say(f"spqr workspace counters N={N} K={K} M={M}")
+    qlin.spqr_forward(dev(X), M, K, d["codes"], d["stats1"], d["stats2"], d["row_ptr"], d["col_idx"], d["val"], nnz,
+                      N, Y, F32, workspace=ws)
+    torch.cuda.synchronize()
+    assert not host(ws[:16384]).any()
+    assert host(ws[16384:]).any()
