@@ -293,9 +293,10 @@ def dense_f16_weights(torch, layers_w):
 
 def sweep_batch(torch, qlin, synth, steps):
     """W4A16 (GEMV up to M=16, MFMA GEMM above) vs SmoothQuant W8A8 (activation
-    kernel + int8 GEMM) vs dense fp16 (torch.matmul, the vendor GEMM) on the
-    Llama-7B-shaped layers, for M = 1 .. 2048.  Same fp16 activations for all
-    three (N(0,1), 1% of channels x100, the SmoothQuant workload's recipe)."""
+    kernel + int8 GEMM) vs dense fp16 (this library's qlin_f16_gemm) on the
+    Llama-7B-shaped layers, for M = 1 .. 2048, with the vendor fp16 GEMM
+    (torch.matmul) as a context column.  Same fp16 activations for all (N(0,1),
+    1% of channels x100, the SmoothQuant workload's recipe)."""
     shapes = synth.WORKLOADS["w4_llama7b"]["layers"]
     Mmax = max(SWEEP_M)
     Ws = [synth.layer_weight("w4_llama7b", li) for li in range(len(shapes))]
@@ -325,7 +326,8 @@ def sweep_batch(torch, qlin, synth, steps):
     f16_bytes = sum(t.numel() * 2 for t in f16[0])
     del Ws
     wsp = zeros_ws(torch, max(max(qlin.qlin_w4_workspace_bytes(qlin.QLIN_F16, M, K, N, 128, qlin.QLIN_F16),
-                                  qlin.sq_int8_gemm_workspace_bytes(M, N, K, qlin.QLIN_F16))
+                                  qlin.sq_int8_gemm_workspace_bytes(M, N, K, qlin.QLIN_F16),
+                                  qlin.qlin_f16_gemm_workspace_bytes(M, N, K, qlin.QLIN_F16))
                               for M in SWEEP_M for N, K in shapes))
 
     rows = []
@@ -353,6 +355,15 @@ def sweep_batch(torch, qlin, synth, steps):
 
         def f16_fns():
             out = []
+            for li, (N, K) in enumerate(shapes):
+                def f(i, li=li, N=N, K=K):
+                    qlin.qlin_f16_gemm(Xd[li][:M], f16[i % len(f16)][li], M, N, K, Yd[li][:M], qlin.QLIN_F16,
+                                       workspace=wsp)
+                out.append(f)
+            return out
+
+        def vendor_fns():
+            out = []
             for li in range(len(shapes)):
                 def f(i, li=li):
                     torch.matmul(Xd[li][:M], f16[i % len(f16)][li].t(), out=Yd[li][:M])
@@ -364,7 +375,9 @@ def sweep_batch(torch, qlin, synth, steps):
         rec = {"M": M}
         for name, fns, copies, wb, peak in (("w4a16", w4_fns(), len(w4), w4_bytes, MFMA_PEAK_TFLOPS["f16"]),
                                             ("w8a8", sq_fns(), len(sq), sq_bytes, MFMA_PEAK_TFLOPS["i8"]),
-                                            ("f16", f16_fns(), len(f16), f16_bytes, MFMA_PEAK_TFLOPS["f16"])):
+                                            ("f16", f16_fns(), len(f16), f16_bytes, MFMA_PEAK_TFLOPS["f16"]),
+                                            ("f16_vendor", vendor_fns(), len(f16), f16_bytes,
+                                             MFMA_PEAK_TFLOPS["f16"])):
             ms = graph_step_ms(torch, fns, copies, steps)
             floor_us = max((wb + io) / (HBM_PEAK_GBS * 1e9), flops / (peak * 1e12)) * 1e6
             rec[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),

@@ -39,7 +39,7 @@
  *     share a workspace.  The library keeps no state besides the thread-local
  *     error message and a per-device cache of the compute-unit count.
  *   - Workspace (qlin_w4_forward, qlin_w4_forward_perm, spqr_forward,
- *     sq_int8_gemm): device
+ *     sq_int8_gemm, qlin_f16_gemm): device
  *     memory of at least the size the matching *_workspace_bytes call reports
  *     for the shape (0 means none is needed and NULL may be passed), 16-byte
  *     aligned.  Fill the whole buffer with zeros once after allocating it:
@@ -293,6 +293,30 @@ qlin_status sq_int8_gemm(const int8_t* Xq, const float* x_scale,
                          int M, int N, int K, void* Y, int y_dtype,
                          int32_t* acc_out, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* ======================================================================== */
+/* Dense fp16 layer (the unquantized baseline)                               */
+/* ======================================================================== */
+/* The 16-bit layer the pages measure their formats against: the SpQR and
+ * SmoothQuant bulletins ("İddia ve Gerçeklik") quote speedups over 16-bit
+ * inference, and the GPTQ bulletin ("İddia ve Gerçeklik") and the SmoothQuant
+ * bulletin ("Ticari Etki") describe the weight-only gain fading as the batch
+ * grows and the layer turns compute bound.  Used for that batch comparison. */
+
+/* Device workspace bytes qlin_f16_gemm needs for this shape and output dtype
+ * on the current device (never 0: every shape runs split-K).  Errors as
+ * qlin_f16_gemm's shape checks, EINVAL for a NULL bytes. */
+qlin_status qlin_f16_gemm_workspace_bytes(int M, int N, int K, int y_dtype, size_t* bytes);
+
+/* GPU: Y[m][n] = y_dtype(sum_k X[m][k] W[n][k]), X fp16 [M][K], W fp16 [N][K]
+ * (device, row-major), fp32 accumulation on v_mfma_f32_32x32x16_f16 (every
+ * product exact), the K range of a tile split over workgroups (stream-K) with
+ * the fp32 partials summed in K order: the result does not depend on timing.
+ * Y device [M][N], y_dtype QLIN_F16, QLIN_BF16 or QLIN_F32, rounded once.
+ * Requirements: K % 64 == 0, K <= 2^29; X, W, Y 16-byte aligned; workspace as
+ * in the conventions at the top. */
+qlin_status qlin_f16_gemm(const uint16_t* X, const uint16_t* W, int M, int N, int K, void* Y, int y_dtype,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ======================================================================== */
 /* Second-order encoders (host, offline): same storage, same forward calls   */

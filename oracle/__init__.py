@@ -37,4 +37,4 @@ library's own readings where the pages are silent, so they are pinned only by
 the round-trip tests, not by any value on the pages ("parity unpinned" for the
 byte layout as such).
 """
-from . import gptq, metrics, smoothquant, spqr, w4  # noqa: F401
+from . import dense, gptq, metrics, smoothquant, spqr, w4  # noqa: F401

@@ -140,6 +140,21 @@ qlin_status sq_workspace_total(int M, int N, int K, int y_dtype, size_t* total) 
   return QLIN_OK;
 }
 
+qlin_status dense_check(const char* fn, int M, int N, int K, int y_dtype) {
+  if (M <= 0 || N <= 0 || K <= 0) return fail(QLIN_EINVAL, std::string(fn) + ": M, N, K must be positive");
+  if (K % 64 != 0) return fail(QLIN_EINVAL, std::string(fn) + ": K must be a multiple of 64");
+  if (K > (1 << 29)) return fail(QLIN_EUNSUPPORTED, std::string(fn) + ": K above 2^29");
+  if (!is_out_dtype(y_dtype)) return fail(QLIN_EINVAL, std::string(fn) + ": bad y_dtype");
+  return QLIN_OK;
+}
+
+qlin_status dense_workspace_total(int M, int N, int K, int y_dtype, size_t* total) {
+  size_t partial = 0;
+  QLIN_TRY(dense_f16_gemm_launch(nullptr, nullptr, M, N, K, nullptr, y_dtype, WsView{}, &partial, nullptr));
+  *total = kCounterBytes + ws_round(partial);
+  return QLIN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,6 +310,31 @@ qlin_status sq_int8_gemm(const int8_t* Xq, const float* x_scale, const int8_t* W
   QLIN_TRY(need_workspace(fn, workspace, workspace_bytes, total));
   QLIN_TRY(sq_gemm_launch(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out,
                           WsView{static_cast<char*>(workspace), workspace_bytes}, nullptr, stream));
+  return check_launch(fn);
+}
+
+qlin_status qlin_f16_gemm_workspace_bytes(int M, int N, int K, int y_dtype, size_t* bytes) {
+  static const char* fn = "qlin_f16_gemm_workspace_bytes";
+  clear_error();
+  if (!bytes) return fail(QLIN_EINVAL, std::string(fn) + ": NULL bytes");
+  QLIN_TRY(dense_check(fn, M, N, K, y_dtype));
+  return dense_workspace_total(M, N, K, y_dtype, bytes);
+}
+
+qlin_status qlin_f16_gemm(const uint16_t* X, const uint16_t* W, int M, int N, int K, void* Y, int y_dtype,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  static const char* fn = "qlin_f16_gemm";
+  clear_error();
+  QLIN_TRY(dense_check(fn, M, N, K, y_dtype));
+  if (!X || !W || !Y) return fail(QLIN_EINVAL, std::string(fn) + ": NULL pointer");
+  QLIN_TRY(need_aligned(fn, "X", X));
+  QLIN_TRY(need_aligned(fn, "W", W));
+  QLIN_TRY(need_aligned(fn, "Y", Y));
+  size_t total = 0;
+  QLIN_TRY(dense_workspace_total(M, N, K, y_dtype, &total));
+  QLIN_TRY(need_workspace(fn, workspace, workspace_bytes, total));
+  QLIN_TRY(dense_f16_gemm_launch(X, W, M, N, K, Y, y_dtype, WsView{static_cast<char*>(workspace), workspace_bytes},
+                                 nullptr, stream));
   return check_launch(fn);
 }
 

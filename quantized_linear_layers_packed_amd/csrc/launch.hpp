@@ -91,4 +91,8 @@ qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t*
                            int M, int N, int K, void* Y, int y_dtype, int32_t* acc_out, WsView ws, size_t* need,
                            hipStream_t stream);
 
+// Dense fp16 GEMM Y = X W^T (K % 64 == 0); need / workspace as for sq_gemm_launch.
+qlin_status dense_f16_gemm_launch(const uint16_t* X, const uint16_t* W, int M, int N, int K, void* Y, int y_dtype,
+                                  WsView ws, size_t* need, hipStream_t stream);
+
 }  // namespace qlin

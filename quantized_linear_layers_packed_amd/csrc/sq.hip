@@ -28,6 +28,7 @@
 #include "device.hpp"
 #include "launch.hpp"
 #include "splitk.hpp"
+#include "tile_gemm.hpp"
 #include "workspace.hpp"
 
 namespace qlin {
@@ -495,174 +496,37 @@ __global__ __launch_bounds__(kGemmThreads) void sq_gemm_sk_kernel(
   }
 }
 
-// Large tiles for large batches: a WM x WN grid of waves, each owning 32 TM rows
-// x 32 TN columns (TM x TN blocks of 32 x 32), so a tile is BM = 32 TM WM rows x
-// BN = 32 TN WN columns and every operand byte brought into LDS feeds BN (or BM)
-// multiply-adds instead of 128: at 256 x 256 the operand traffic per multiply-add
-// is half that of the 128 x 128 tiles above.  K steps of BK bytes (64 or 128;
-// K is a multiple of 64, and of BK here), rows of BK bytes in LDS with their
-// 16-byte chunks XOR-swizzled by row so that the 16 rows one quarter-wave of an
-// MFMA operand read touches fall in distinct banks; within a step, MFMA step st
-// and lane half h use chunk (BK / 32) h + st of both operands.  The rest (direct-
-// to-LDS ring, stream-K split, exact int32 fix-up, epilogue) is as above.
-template <int WM, int WN, int TM, int TN, int BK, int NS, int OUTK>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
-void sq_gemm_big_kernel(const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
-                        const int8_t* __restrict__ Wq, const float* __restrict__ w_scale, int M, int N, int K,
-                        int tiles_m, SkPlan plan, void* __restrict__ Y, int32_t* __restrict__ acc_out,
-                        int* __restrict__ ws, int* __restrict__ counters) {
-  constexpr int NW = WM * WN;
-  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
-  constexpr int CH = BK / 16;                                   // 16-byte chunks per row
-  constexpr int RPI = 64 / CH;                                  // rows per direct-load instruction
-  constexpr int RSH = RPI == 16 ? 2 : 1;                        // swizzle: chunk ^ (row >> RSH) % CH
-  constexpr int KST = BK / 32;                                  // MFMA steps per K step
-  constexpr int A_PIECES = BM * CH, B_PIECES = BN * CH;         // 16-byte pieces per stage
-  constexpr int STAGE = A_PIECES + B_PIECES;
-  constexpr int A_INS = BM / RPI / NW, B_INS = BN / RPI / NW;   // direct loads per wave per stage
-  static_assert(BK == 64 || BK == 128, "K step of 64 or 128 bytes");
-  static_assert(A_INS * RPI * NW == BM && B_INS * RPI * NW == BN, "row blocks split evenly over the waves");
-  static_assert((NS - 2) * (A_INS + B_INS) < 64, "vmcnt range");
-  extern __shared__ uint4 smem[];
-  __shared__ int s_last;
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv % WM, wn = wv / WM;
-  const int col = lane & 31, h = lane >> 5;
-  const int swz = (col >> RSH) & (CH - 1);                      // swizzle of every row this lane reads
-  const int lrow = lane / CH, lpos = lane % CH;                 // this lane's piece in a direct load
-
-  const int p = xcd_tile(blockIdx.x, gridDim.x);
-  long long u = sk_begin(plan, p);
-  const long long u_end = sk_begin(plan, p + 1);
-
-  while (u < u_end) {
-    const int t = static_cast<int>(u / plan.ksteps);
-    const int k0 = static_cast<int>(u - static_cast<long long>(t) * plan.ksteps);
-    const int k1 = static_cast<int>(std::min<long long>(plan.ksteps, k0 + (u_end - u)));
-    const int klast = k1 - 1;
-    const int m0 = (t % tiles_m) * BM;                          // M-blocks fastest: neighbours share weights
-    const int n0 = (t / tiles_m) * BN;
-
-    // Direct loads of step s = min(j, klast) into slot j % NS.  Wave wv loads the
-    // RPI-row blocks wv, wv + NW, ... of A and of B.  Rows past M / N read the
-    // last row (their results are never stored); positions past the range re-read
-    // its last step into slots no step of the range reads again.
-    auto issue = [&](int j) {
-      const int s = min(j, klast);
-      uint4* slot = smem + static_cast<size_t>(j % NS) * STAGE;
-#pragma unroll
-      for (int q = 0; q < A_INS; ++q) {
-        const int rb = wv + NW * q;
-        const int row = RPI * rb + lrow;
-        const int c = lpos ^ ((row >> RSH) & (CH - 1));         // logical chunk stored at this piece
-        const int m = min(m0 + row, M - 1);
-        dma16(Xq + static_cast<size_t>(m) * K + s * BK + 16 * c, slot + 64 * rb);
-      }
-#pragma unroll
-      for (int q = 0; q < B_INS; ++q) {
-        const int rb = wv + NW * q;
-        const int row = RPI * rb + lrow;
-        const int c = lpos ^ ((row >> RSH) & (CH - 1));
-        const int nn = min(n0 + row, N - 1);
-        dma16(Wq + static_cast<size_t>(nn) * K + s * BK + 16 * c, slot + A_PIECES + 64 * rb);
-      }
-    };
-
-    i32x16_t acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = i32x16_t{};
-
-    wait_vmcnt<0>();                                            // nothing but the ring in flight below
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j) issue(k0 + j);
-
-    for (int kk = k0; kk < k1; ++kk) {
-      wait_vmcnt<(NS - 2) * (A_INS + B_INS)>();                 // this wave's loads of step kk
-      barrier_raw();                                            // everyone's; step kk - 1 finished
-      issue(kk + NS - 1);
-      const uint4* As = smem + static_cast<size_t>(kk % NS) * STAGE + (32 * TM * wm + col) * CH;
-      const uint4* Bs = smem + static_cast<size_t>(kk % NS) * STAGE + A_PIECES + (32 * TN * wn + col) * CH;
-#pragma unroll
-      for (int st = 0; st < KST; ++st) {
-        const int c = (KST * h + st) ^ swz;
-        i32x4_t a[TM], b[TN];                                   // one MFMA step's operands first
-#pragma unroll
-        for (int i = 0; i < TM; ++i) a[i] = bitcast<i32x4_t>(As[32 * CH * i + c]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = bitcast<i32x4_t>(Bs[32 * CH * j + c]);
-        __builtin_amdgcn_sched_barrier(0);                      // keep its LDS reads ahead of its MFMAs
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-    }
-    wait_vmcnt<0>();                                            // loads past the range end
-    __syncthreads();
-
-    // ---- finish the tile: block (i, j) of this wave holds column n0 + 32 TN wn + 32 j + col,
-    // rows m0 + 32 TM wm + 32 i + 8 (r / 4) + 4 h + r % 4
-    bool write = true;
-    if (k0 != 0 || k1 != plan.ksteps) {
-      const int first = sk_owner(plan, static_cast<long long>(t) * plan.ksteps);
-      const int last = sk_owner(plan, static_cast<long long>(t + 1) * plan.ksteps - 1);
-      int* mine = ws + static_cast<size_t>(sk_slot(plan, p, t)) * (BM * BN);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sk_store(mine + (((wv * TM + i) * TN + j) * 16 + r) * 64 + lane, acc[i][j][r]);
-      write = sk_arrive_last(&counters[first], last - first, &s_last);
-      if (write) {
-        for (int q = first; q <= last; ++q) {
-          if (q == p) continue;
-          const int* other = ws + static_cast<size_t>(sk_slot(plan, q, t)) * (BM * BN);
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              int part[16];                     // one block's loads, then its adds
-#pragma unroll
-              for (int r = 0; r < 16; ++r) part[r] = sk_load(other + (((wv * TM + i) * TN + j) * 16 + r) * 64 + lane);
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[i][j][r] += part[r];
-            }
-        }
-        if (tid == 0) sk_reset(&counters[first]);
-      }
-    }
-    if (write) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + 32 * TN * wn + 32 * j + col;
-        if (n >= N) continue;
-        const float wsc = w_scale[n];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          float xsc[16];                        // row scales first (clamped rows, no branches)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            xsc[r] = x_scale[min(m0 + 32 * TM * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3), M - 1)];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = m0 + 32 * TM * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (m < M) {
-              const size_t idx = static_cast<size_t>(m) * N + n;
-              store_out<OUTK>(Y, idx, static_cast<float>(acc[i][j][r]) * xsc[r] * wsc);
-              if (acc_out) acc_out[idx] = acc[i][j][r];
-            }
-          }
-        }
-      }
-    }
-    u += k1 - k0;
+// Large tiles for large batches (tile_gemm.hpp): a WM x WN grid of waves,
+// each owning 32 TM rows x 32 TN columns, v_mfma_i32_32x32x32_i8 on rows of K
+// bytes, exact int32 split-K fix-up; epilogue as above.
+struct SqI8Op {
+  using acc_t = i32x16_t;
+  using part_t = int;
+  static constexpr bool kExact = true;
+  const float* x_scale;
+  const float* w_scale;
+  int32_t* acc_out;
+  __device__ __forceinline__ static acc_t mfma(i32x4_t a, i32x4_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
   }
-}
+  // one 32 x 32 block's column n, rows mb + 8 (r / 4) + r % 4
+  template <int OUTK>
+  __device__ __forceinline__ void store(void* Y, int M, int N, int mb, int n, const acc_t& acc) const {
+    const float wsc = w_scale[n];
+    float xsc[16];                              // row scales first (clamped rows, no branches)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xsc[r] = x_scale[min(mb + 8 * (r >> 2) + (r & 3), M - 1)];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = mb + 8 * (r >> 2) + (r & 3);
+      if (m < M) {
+        const size_t idx = static_cast<size_t>(m) * N + n;
+        store_out<OUTK>(Y, idx, static_cast<float>(acc[r]) * xsc[r] * wsc);
+        if (acc_out) acc_out[idx] = acc[r];
+      }
+    }
+  }
+};
 
 template <int TM, int NS, int OUTK>
 qlin_status gemm_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
@@ -700,49 +564,15 @@ qlin_status gemm_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const f
   return QLIN_OK;
 }
 
-template <int WM, int WN, int TM, int TN, int BK, int NS, int OUTK>
-qlin_status gemm_big_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
-                       void* Y, int32_t* acc_out, WsView ws, size_t* need, hipStream_t stream) {
-  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN, threads = 64 * WM * WN;
-  constexpr size_t lds = static_cast<size_t>(NS) * (BM + BN) * BK;
-  static_assert(lds + 16 <= 160 * 1024, "LDS ring within the 160 KB of a CU");
-  static const int occ = [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sq_gemm_big_kernel<WM, WN, TM, TN, BK, NS, OUTK>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, sq_gemm_big_kernel<WM, WN, TM, TN, BK, NS, OUTK>, threads,
-                                                     lds) != hipSuccess ||
-        o <= 0)
-      o = 1;
-    return std::min(o, 2);
-  }();
-  const int tiles_m = (M + BM - 1) / BM;
-  const int tiles_n = (N + BN - 1) / BN;
-  const long long tiles = static_cast<long long>(tiles_m) * tiles_n;
-  SkPlan plan;
-  plan.ksteps = K / BK;
-  plan.units = tiles * plan.ksteps;
-  plan.P = static_cast<int>(std::min<long long>(
-      std::min<long long>(static_cast<long long>(occ) * device_cus(), kCounterSlots), plan.units));
-  const size_t partial_bytes = static_cast<size_t>(2) * plan.P * BM * BN * sizeof(int);
-  if (need) {
-    *need = partial_bytes;
-    return QLIN_OK;
-  }
-  if (ws.bytes < kCounterBytes + partial_bytes)
-    return fail(QLIN_EINVAL, "sq_int8_gemm: workspace too small for the split-K GEMM");
-  hipLaunchKernelGGL((sq_gemm_big_kernel<WM, WN, TM, TN, BK, NS, OUTK>), dim3(plan.P), dim3(threads), lds, stream,
-                     Xq, xsc, Wq, wsc, M, N, K, tiles_m, plan, Y, acc_out, static_cast<int*>(ws.partials()),
-                     ws.counters());
-  return QLIN_OK;
-}
-
 template <int WM, int WN, int TM, int TN, int BK, int NS>
 qlin_status gemm_big_o(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
                        void* Y, int y_dtype, int32_t* acc_out, WsView ws, size_t* need, hipStream_t stream) {
+  const SqI8Op op{xsc, wsc, acc_out};
   return y_dtype == QLIN_F32
-             ? gemm_big_t<WM, WN, TM, TN, BK, NS, OUT_F32>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, ws, need, stream)
-             : gemm_big_t<WM, WN, TM, TN, BK, NS, OUT_F16>(Xq, xsc, Wq, wsc, M, N, K, Y, acc_out, ws, need, stream);
+             ? tile_gemm_launch<SqI8Op, WM, WN, TM, TN, BK, NS, OUT_F32>("sq_int8_gemm", Xq, Wq, M, N, K, op, Y, ws,
+                                                                          need, stream)
+             : tile_gemm_launch<SqI8Op, WM, WN, TM, TN, BK, NS, OUT_F16>("sq_int8_gemm", Xq, Wq, M, N, K, op, Y, ws,
+                                                                          need, stream);
 }
 
 template <int TM, int NS>

@@ -47,7 +47,7 @@ EXPORTS = (
     "qlin_hessian", "qlin_w4_pack_gptq", "spqr_pack_hessian",
     "qlin_w4_pack_gptq_actorder", "qlin_w4_forward_perm",
     "qlin_w4_workspace_bytes", "sq_int8_gemm_workspace_bytes", "qlin_w4_forward_scratch",
-    "qlin_mfma_peak", "spqr_workspace_bytes",
+    "qlin_mfma_peak", "spqr_workspace_bytes", "qlin_f16_gemm", "qlin_f16_gemm_workspace_bytes",
 )
 
 _vp, _i, _i64, _sz, _d = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.c_double
@@ -72,6 +72,8 @@ _sigs = {
     "sq_smooth_quant_act": ([_vp, _vp, _i, _i, _vp, _vp, _vp], _i),
     "sq_int8_gemm": ([_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _sz, _vp], _i),
     "sq_int8_gemm_workspace_bytes": ([_i, _i, _i, _i, _vp], _i),
+    "qlin_f16_gemm": ([_vp, _vp, _i, _i, _i, _vp, _i, _vp, _sz, _vp], _i),
+    "qlin_f16_gemm_workspace_bytes": ([_i, _i, _i, _i, _vp], _i),
     "qlin_stream_read": ([_vp, _sz, _i, _i, _i, _vp, _vp], _i),
     "qlin_stream_copy": ([_vp, _vp, _sz, _vp], _i),
     "qlin_mfma_peak": ([_i, _i, _i, _vp, _vp], _i),
@@ -350,6 +352,20 @@ def sq_int8_gemm(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype=QLIN_F16, acc_out
                  workspace=None, workspace_bytes=None, stream=None):
     _check(_lib.sq_int8_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y), y_dtype,
                              _ptr(acc_out), _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Dense fp16 layer
+
+def qlin_f16_gemm_workspace_bytes(M, N, K, y_dtype=QLIN_F16):
+    b = C.c_size_t()
+    _check(_lib.qlin_f16_gemm_workspace_bytes(M, N, K, y_dtype, C.byref(b)))
+    return b.value
+
+
+def qlin_f16_gemm(X, W, M, N, K, Y, y_dtype=QLIN_F16, workspace=None, workspace_bytes=None, stream=None):
+    _check(_lib.qlin_f16_gemm(_ptr(X), _ptr(W), M, N, K, _ptr(Y), y_dtype, _ptr(workspace),
+                              _nbytes(workspace, workspace_bytes), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

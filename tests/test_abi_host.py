@@ -77,6 +77,22 @@ def test_spqr_forward_rejects_bad_arguments():
             stream=0)
 
 
+def test_dense_gemm_rejects_bad_arguments():
+    fw = qlin.qlin_f16_gemm
+    need = qlin.qlin_f16_gemm_workspace_bytes(256, 1024, 4096, qlin.QLIN_F16)
+    assert need > 16384                                  # every shape runs split-K: counters + partials
+    _raises(qlin.QLIN_EINVAL, fw, FAKE, FAKE, 4, 64, 100, FAKE, 1, FAKE, need, 0)       # K % 64
+    _raises(qlin.QLIN_EINVAL, fw, FAKE, FAKE, 0, 64, 128, FAKE, 1, FAKE, need, 0)       # M
+    _raises(qlin.QLIN_EINVAL, fw, FAKE, FAKE, 4, 64, 128, FAKE, 7, FAKE, need, 0)       # y_dtype
+    _raises(qlin.QLIN_EINVAL, fw, 0, FAKE, 4, 64, 128, FAKE, 1, FAKE, need, 0)          # NULL X
+    _raises(qlin.QLIN_EALIGN, fw, FAKE, FAKE + 2, 4, 64, 128, FAKE, 1, FAKE, need, 0)   # W misaligned
+    msg = _raises(qlin.QLIN_EINVAL, fw, FAKE, FAKE, 256, 1024, 4096, FAKE, 1, None, None, 0)
+    assert str(need) in msg
+    _raises(qlin.QLIN_EINVAL, fw, FAKE, FAKE, 256, 1024, 4096, FAKE, 1, FAKE, need - 1, 0)
+    with pytest.raises(qlin.QlinError):
+        qlin.qlin_f16_gemm_workspace_bytes(4, 64, 96)
+
+
 def test_sq_calls_reject_bad_arguments():
     _raises(qlin.QLIN_EINVAL, qlin.sq_smooth_quant_act, FAKE, FAKE, 4, 100, FAKE, FAKE, 0)
     _raises(qlin.QLIN_EALIGN, qlin.sq_smooth_quant_act, FAKE + 2, FAKE, 4, 128, FAKE, FAKE, 0)
