@@ -69,6 +69,7 @@ def _compile(src: str):
     res = _resources(r.stderr)
     warn = "\n".join(l for l in r.stderr.splitlines()
                      if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l and l.strip()
+                     and not l.startswith("In file included from")
                      and not l.lstrip().startswith(("|", "^")) and not re.match(r"^\s*\d+ \|", l))
     if warn:
         print(warn, file=sys.stderr)

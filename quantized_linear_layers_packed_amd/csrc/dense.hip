@@ -38,19 +38,19 @@ struct DenseF16Op {
   }
 };
 
-template <int WM, int WN, int TM, int TN, int NS>
+template <int WM, int WN, int TM, int TN, int NS, int WPE = WM * WN / 4>
 qlin_status launch_o(const uint16_t* X, const uint16_t* W, int M, int N, int K, void* Y, int y_dtype, WsView ws,
                      size_t* need, hipStream_t stream) {
   static const char* fn = "qlin_f16_gemm";
   const DenseF16Op op{};
   const int Kb = 2 * K;
   if (y_dtype == QLIN_F32)
-    return tile_gemm_launch<DenseF16Op, WM, WN, TM, TN, 128, NS, OUT_F32>(fn, X, W, M, N, Kb, op, Y, ws, need,
+    return tile_gemm_launch<DenseF16Op, WM, WN, TM, TN, 128, NS, OUT_F32, WPE>(fn, X, W, M, N, Kb, op, Y, ws, need,
                                                                           stream);
   if (y_dtype == QLIN_BF16)
-    return tile_gemm_launch<DenseF16Op, WM, WN, TM, TN, 128, NS, OUT_BF16>(fn, X, W, M, N, Kb, op, Y, ws, need,
+    return tile_gemm_launch<DenseF16Op, WM, WN, TM, TN, 128, NS, OUT_BF16, WPE>(fn, X, W, M, N, Kb, op, Y, ws, need,
                                                                            stream);
-  return tile_gemm_launch<DenseF16Op, WM, WN, TM, TN, 128, NS, OUT_F16>(fn, X, W, M, N, Kb, op, Y, ws, need, stream);
+  return tile_gemm_launch<DenseF16Op, WM, WN, TM, TN, 128, NS, OUT_F16, WPE>(fn, X, W, M, N, Kb, op, Y, ws, need, stream);
 }
 
 }  // namespace
@@ -63,6 +63,9 @@ qlin_status dense_f16_gemm_launch(const uint16_t* X, const uint16_t* W, int M, i
   // 128 x 128 or 128 x 64 that still gives at least 160 tiles (the smallest one
   // otherwise), as for the int8 GEMM.
   if (M <= 64) return launch_o<2, 4, 1, 1, 6>(X, W, M, N, K, Y, y_dtype, ws, need, stream);
+#ifdef QLIN_DENSE_CFG
+  return launch_o<QLIN_DENSE_CFG>(X, W, M, N, K, Y, y_dtype, ws, need, stream);
+#endif
   auto tiles = [&](int bm, int bn) { return static_cast<long long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (tiles(256, 128) >= 160) return launch_o<4, 2, 2, 2, 3>(X, W, M, N, K, Y, y_dtype, ws, need, stream);
   if (tiles(128, 128) >= 160) return launch_o<4, 2, 1, 2, 4>(X, W, M, N, K, Y, y_dtype, ws, need, stream);

@@ -75,7 +75,7 @@ struct SpqrPrep {
   const uint16_t* XT;
 };
 #ifndef QLIN_SPQR_MFMA_MIN_M
-#define QLIN_SPQR_MFMA_MIN_M 6        // batches from this size run the matrix-core path
+#define QLIN_SPQR_MFMA_MIN_M 5        // batches from this size run the matrix-core path
 #endif
 size_t spqr_prep_bytes(int K);
 SpqrPrep spqr_prep_view(char* base, int K);

@@ -1,4 +1,4 @@
-// SpQR product for batches of 6..16 tokens on the matrix cores, gfx950.
+// SpQR product for batches of 5..16 tokens on the matrix cores, gfx950.
 //
 // Y[m][n] = sum_g s_hat[n][g] * (sum_{k in g} x[m][k] q[n][k] - z_hat[n][g] * sum_{k in g} x[m][k])
 //           + sum_{(n,k,v) in CSR} x[m][k] * v
@@ -9,7 +9,7 @@
 // GEMV's dot products (one v_dot2 per two weights per token) dominate; here
 // each group's exact integer codes go through one v_mfma_f32_16x16x16_f16 for
 // 16 tokens x 16 output columns, so the vector work per weight no longer grows
-// with the batch (measured: flat from 2 to 16 tokens, ahead of the GEMV from 6):
+// with the batch (measured: flat from 2 to 16 tokens, ahead of the GEMV from 5):
 //   * P = sum_{k in g} x (1024 + q): the codes enter as fp16 1024 + q built by
 //     a mask and an or (exact), and the 1024 is folded into the zero term
 //     below; one MFMA per group and column tile, then acc += s_hat * P in fp32
@@ -63,7 +63,8 @@ __host__ __device__ constexpr int order_b(int j, int e) {
   return t[j][e];
 }
 
-// One thread per (chunk c, batch row m < 16).
+// One thread per (chunk c, batch row m < 16).  (Four threads per (chunk, row),
+// one per lane quarter, measured slower: the pass is launch and latency bound.)
 //   Xp [K/32][4][16] x 8 fp16: chunk c, quarter j, row m: order_a(j, 0..3), order_b(j, 0..3)
 //   Xs [K/16][16] fp32: sum over the group's 16 x, in k order
 //   XT [K][16] fp16
@@ -132,24 +133,25 @@ __device__ __forceinline__ uint32_t pair_at(uint32_t w, uint32_t shift) {
 // quarters 0..2 (16 bytes each; quarter 3 repeats quarter 2's), and handed to
 // the quarters that need them with ds_bpermute, so every load instruction
 // brings 768 distinct bytes instead of four copies of 192.
+template <int CT>
 struct SuperStep {
-  uint4 cw;          // code bytes 16 min(j, 2) .. +15 of the super-step, this lane's column
-  uint32_t st[3];    // first-level statistic codes of the block (16 groups)
-  uint2 ss;          // second-level statistics of the block (4 fp16)
-  uint4 xa[4];       // operand fragments of the 4 chunks (row r16, quarter j)
-  float xs[2];       // group sums of groups 8u + j and 8u + 4 + j, row r16
+  uint4 cw[CT];          // code bytes 16 min(j, 2) .. +15 of the super-step, this lane's column of tile c
+  uint32_t st[CT][3];    // first-level statistic codes of the block (16 groups)
+  uint2 ss[CT];          // second-level statistics of the block (4 fp16)
+  uint4 xa[4];           // operand fragments of the 4 chunks (row r16, quarter j), shared by the tiles
+  float xs[2];           // group sums of groups 8u + j and 8u + 4 + j, row r16
 };
 
-template <int KSW, int D, int OUTK>
+template <int KSW, int D, int CT, int OUTK>
 __global__ __launch_bounds__(64 * KSW) void spqr_mfma_kernel(
     const uint32_t* codes, const uint32_t* stats1, const uint16_t* stats2, const int32_t* row_ptr,
     const int32_t* col_idx, const uint16_t* vals, const uint4* Xp, const float* Xs, const uint16_t* XT, int M, int K,
     int N, void* Y) {
-  __shared__ f32x4_t red[KSW][64];
+  __shared__ f32x4_t red[KSW][CT][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, j = lane >> 4;      // MFMA: A row / B,D column = r16; k quarter / D row quarter = j
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * CT;
   const int nchunk = K >> 5, nblk = K >> 8;
   const int nsup = K >> 7;                       // super-steps of 4 chunks
   const int u0 = (wv * nsup) / KSW, u1 = ((wv + 1) * nsup) / KSW;
@@ -160,8 +162,11 @@ __global__ __launch_bounds__(64 * KSW) void spqr_mfma_kernel(
   const uint32_t sa1 = j == 0 ? 3u : j == 1 ? 9u : j == 2 ? 0u : 6u;       // group a, second
   const uint32_t sb0 = j == 0 ? 9u : j == 1 ? 0u : j == 2 ? 6u : 12u;      // group b, first
   const uint32_t sb1 = j == 0 ? 12u : j == 1 ? 3u : 9u;                    // group b, second (j = 3: spare bits)
+  const uint32_t m3 = j == 3 ? ~0u : 0u;                                   // lane quarter 3
 
-  const int ncol = min(n0 + r16, N - 1);
+  int ncol[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) ncol[c] = min(n0 + 16 * c + r16, N - 1);
   // Buffer loads: each array is one resource (base and byte size in scalar
   // registers); a lane's loop-invariant byte offset is its VGPR operand and the
   // super-step's part is the wave-uniform scalar offset, so the loop keeps no
@@ -173,23 +178,32 @@ __global__ __launch_bounds__(64 * KSW) void spqr_mfma_kernel(
   const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(stats2, static_cast<uint32_t>(N) * static_cast<uint32_t>(nblk * 8));
   const __amdgpu_buffer_rsrc_t rxp = make_rsrc(Xp, static_cast<uint32_t>(K) * 32u);
   const __amdgpu_buffer_rsrc_t rxs = make_rsrc(Xs, static_cast<uint32_t>(K) * 4u);
-  const int voff_c = ncol * (nchunk * 12) + 16 * min(j, 2);     // code bytes of this lane's column and quarter
-  const int voff_s1 = ncol * (nblk * 12);
-  const int voff_s2 = ncol * (nblk * 8);
+  int voff_c[CT], voff_s1[CT], voff_s2[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    voff_c[c] = ncol[c] * (nchunk * 12) + 16 * min(j, 2);      // code bytes of this lane's column and quarter
+    voff_s1[c] = ncol[c] * (nblk * 12);
+    voff_s2[c] = ncol[c] * (nblk * 8);
+  }
   const int voff_xp = (j * 16 + r16) * 16;
   const int voff_xs = (j * 16 + r16) * 4;
 
-  f32x4_t acc = f32x4_t{}, corr = f32x4_t{};
+  f32x4_t acc[CT], corr[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) acc[c] = corr[c] = f32x4_t{};
 
   // every load of a super-step, unconditional (super-steps past the range re-read its last)
-  auto load = [&](int u, SuperStep& d) {
+  auto load = [&](int u, SuperStep<CT>& d) __attribute__((always_inline)) {
     const int blk = u >> 1;
-    d.cw = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(rc, voff_c, 48 * u, 0));
-    const u32x4_t st = __builtin_amdgcn_raw_buffer_load_b128(rs1, voff_s1, 12 * blk, 0);
-    d.st[0] = st[0];
-    d.st[1] = st[1];
-    d.st[2] = st[2];
-    d.ss = bitcast<uint2>(__builtin_amdgcn_raw_buffer_load_b64(rs2, voff_s2, 8 * blk, 0));
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      d.cw[c] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(rc, voff_c[c], 48 * u, 0));
+      const u32x4_t st = __builtin_amdgcn_raw_buffer_load_b128(rs1, voff_s1[c], 12 * blk, 0);
+      d.st[c][0] = st[0];
+      d.st[c][1] = st[1];
+      d.st[c][2] = st[2];
+      d.ss[c] = bitcast<uint2>(__builtin_amdgcn_raw_buffer_load_b64(rs2, voff_s2[c], 8 * blk, 0));
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       d.xa[t] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(rxp, voff_xp, (4 * u + t) * 1024, 0));
@@ -198,58 +212,117 @@ __global__ __launch_bounds__(64 * KSW) void spqr_mfma_kernel(
       d.xs[h] = bitcast<float>(__builtin_amdgcn_raw_buffer_load_b32(rxs, voff_xs, (8 * u + 4 * h) * 64, 0));
   };
 
-  auto compute = [&](int u, const SuperStep& d) {
+  auto compute = [&](int u, const SuperStep<CT>& d) __attribute__((always_inline)) {
     const int q = u & 1;                         // which half of the block
-    const float SSs = f16_bits_to_f32(static_cast<uint16_t>(d.ss.x & 0xFFFFu));
-    const float ZSs = f16_bits_to_f32(static_cast<uint16_t>(d.ss.x >> 16));
-    const float SSz = f16_bits_to_f32(static_cast<uint16_t>(d.ss.y & 0xFFFFu));
-    const float ZSz = f16_bits_to_f32(static_cast<uint16_t>(d.ss.y >> 16));
-    const uint32_t cwv[4] = {d.cw.x, d.cw.y, d.cw.z, d.cw.w};
+    float SSs[CT], ZSs[CT], SSz[CT], ZSz[CT];
+    uint32_t cwv[CT][4];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      SSs[c] = f16_bits_to_f32(static_cast<uint16_t>(d.ss[c].x & 0xFFFFu));
+      ZSs[c] = f16_bits_to_f32(static_cast<uint16_t>(d.ss[c].x >> 16));
+      SSz[c] = f16_bits_to_f32(static_cast<uint16_t>(d.ss[c].y & 0xFFFFu));
+      ZSz[c] = f16_bits_to_f32(static_cast<uint16_t>(d.ss[c].y >> 16));
+      cwv[c][0] = d.cw[c].x;
+      cwv[c][1] = d.cw[c].y;
+      cwv[c][2] = d.cw[c].z;
+      cwv[c][3] = d.cw[c].w;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       // statistics of group 8q + 4h + j of the block (this lane's column):
       // 6-bit field at bit 6 (8q + 4h + j) of the block's 96-bit stream
       const int bit = 6 * (8 * q + 4 * h + j);
       const uint32_t sh = static_cast<uint32_t>(bit & 31);
-      const uint32_t f0 = __builtin_amdgcn_alignbit(d.st[1], d.st[0], sh);     // bit < 32
-      const uint32_t f1 = __builtin_amdgcn_alignbit(d.st[2], d.st[1], sh);     // 32 <= bit < 64
-      const uint32_t f2 = d.st[2] >> sh;                                       // bit >= 64
-      const uint32_t f = (bit < 32 ? f0 : bit < 64 ? f1 : f2) & 63u;
-      const float s_hat = SSs * (static_cast<float>(f & 7u) - ZSs);
-      const float z_hat = SSz * (static_cast<float>(f >> 3) - ZSz);
-      corr = __builtin_amdgcn_mfma_f32_16x16x4f32(d.xs[h], s_hat * (1024.0f + z_hat), corr, 0, 0, 0);
+      float s_hat[CT];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        // the word holding the field's low bit and the next one (a field at
+        // bit >= 64 ends within the last word: 6 * 15 + 6 = 96); words selected
+        // first, then one funnel shift, so no lane takes a branch
+        // (copied to locals first: a select between elements of the ring
+        // became a dynamic index into it, which put the whole ring in scratch)
+        const uint32_t t0 = d.st[c][0], t1 = d.st[c][1], t2 = d.st[c][2];
+        const uint32_t lo = bit < 32 ? t0 : bit < 64 ? t1 : t2;
+        const uint32_t hi = bit < 32 ? t1 : t2;
+        const uint32_t f = __builtin_amdgcn_alignbit(hi, lo, sh) & 63u;
+        s_hat[c] = SSs[c] * (static_cast<float>(f & 7u) - ZSs[c]);
+        const float z_hat = SSz[c] * (static_cast<float>(f >> 3) - ZSz[c]);
+        corr[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(d.xs[h], s_hat[c] * (1024.0f + z_hat), corr[c], 0, 0, 0);
+      }
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const int t = 2 * h + cc;                // chunk of the super-step
         // its words 3t .. 3t+2 from the lane quarters that loaded them
-        uint32_t w[3];
+        uint32_t w[CT][3];
 #pragma unroll
-        for (int e = 0; e < 3; ++e) {
-          const int wi = 3 * t + e;
-          w[e] = static_cast<uint32_t>(
-              __builtin_amdgcn_ds_bpermute(4 * (r16 + 16 * (wi >> 2)), static_cast<int>(cwv[wi & 3])));
-        }
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int e = 0; e < 3; ++e) {
+            const int wi = 3 * t + e;
+            w[c][e] = static_cast<uint32_t>(
+                __builtin_amdgcn_ds_bpermute(4 * (r16 + 16 * (wi >> 2)), static_cast<int>(cwv[c][wi & 3])));
+          }
 #pragma unroll
         for (int ab = 0; ab < 2; ++ab) {
-          uint32_t p0, p1;
-          if (ab == 0) {                         // group a: words 0 / 1
-            p0 = pair_at(j < 3 ? w[0] : w[1], sa0);
-            p1 = pair_at(j < 2 ? w[0] : w[1], sa1);
-          } else {                               // group b: words 1 / 2, spare bits
-            p0 = pair_at(j == 0 ? w[1] : w[2], sb0);
-            const uint32_t sp0 = ((w[0] >> 15) & 0x00010001u) | 0x64006400u;
-            const uint32_t sp1 = ((w[1] >> 14) & 0x00020002u) | sp0;
-            const uint32_t spare = ((w[2] >> 13) & 0x00040004u) | sp1;
-            p1 = j == 3 ? spare : pair_at(j == 0 ? w[1] : w[2], sb1);
-          }
           const uint2 av = ab ? make_uint2(d.xa[t].z, d.xa[t].w) : make_uint2(d.xa[t].x, d.xa[t].y);
-          const f32x4_t P = __builtin_amdgcn_mfma_f32_16x16x16f16(bitcast<h4_t>(av),
-                                                                  bitcast<h4_t>(make_uint2(p0, p1)), f32x4_t{}, 0, 0, 0);
-          // s_hat of group 4h + 2cc + ab of the super-step: decoded by quarter 2cc + ab
-          const float sg = bitcast<float>(
-              __builtin_amdgcn_ds_bpermute(4 * (r16 + 16 * (2 * cc + ab)), bitcast<int>(s_hat)));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = fmaf(sg, P[i], acc[i]);
+          for (int c = 0; c < CT; ++c) {
+            uint32_t p0, p1;
+            if (ab == 0) {                       // group a: words 0 / 1
+              p0 = pair_at(j < 3 ? w[c][0] : w[c][1], sa0);
+              p1 = pair_at(j < 2 ? w[c][0] : w[c][1], sa1);
+            } else {                             // group b: words 1 / 2, spare bits
+              p0 = pair_at(j == 0 ? w[c][1] : w[c][2], sb0);
+              const uint32_t sp0 = ((w[c][0] >> 15) & 0x00010001u) | 0x64006400u;
+              const uint32_t sp1 = ((w[c][1] >> 14) & 0x00020002u) | sp0;
+              const uint32_t spare = ((w[c][2] >> 13) & 0x00040004u) | sp1;
+              // quarter 3 takes the spare bits: a bitwise select (one v_bfi),
+              // not a per-lane branch
+              const uint32_t reg = pair_at(j == 0 ? w[c][1] : w[c][2], sb1);
+              p1 = (spare & m3) | (reg & ~m3);
+            }
+            const f32x4_t P = __builtin_amdgcn_mfma_f32_16x16x16f16(bitcast<h4_t>(av),
+                                                                    bitcast<h4_t>(make_uint2(p0, p1)), f32x4_t{}, 0, 0, 0);
+            // s_hat of group 4h + 2cc + ab of the super-step: decoded by quarter 2cc + ab
+            const float sg = bitcast<float>(
+                __builtin_amdgcn_ds_bpermute(4 * (r16 + 16 * (2 * cc + ab)), bitcast<int>(s_hat[c])));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[c][i] = fmaf(sg, P[i], acc[c][i]);
+          }
+        }
+      }
+    }
+  };
+
+  // Outlier pass (after the dense loop): CSR bounds, then rounds of kU entries
+  // per lane quarter, each round's x loads issued before the next round's
+  // entries are fetched and before its own math.  (Fetching the bounds and the
+  // first round ahead of the dense loop kept 10 more registers live through it,
+  // 3 waves per SIMD instead of 4, and measured 10% slower.)
+  constexpr int kU = 4;
+  constexpr int kStreams = 4 * KSW;              // lane quarters of the workgroup, one entry stream each
+  int e1[CT], ef[CT], kk0[CT][kU];
+  float v0[CT][kU];
+
+  auto csr_round = [&](int c, int e, int (&kk)[kU], float (&v)[kU]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int uu = 0; uu < kU; ++uu) {
+      const int eu = e + kStreams * uu;
+      const int ec = min(eu, e1[c] - 1);
+      kk[uu] = col_idx[ec];
+      v[uu] = eu < e1[c] ? f16_bits_to_f32(vals[ec]) : 0.0f;
+    }
+  };
+  auto csr_first = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      if (ef[c] < e1[c]) {
+        csr_round(c, ef[c], kk0[c], v0[c]);
+      } else {
+#pragma unroll
+        for (int uu = 0; uu < kU; ++uu) {
+          kk0[c][uu] = 0;
+          v0[c][uu] = 0.0f;
         }
       }
     }
@@ -257,11 +330,11 @@ __global__ __launch_bounds__(64 * KSW) void spqr_mfma_kernel(
 
   if (u0 < u1) {
     const int ulast = u1 - 1;
-    SuperStep ring[D];
+    SuperStep<CT> ring[D];
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) load(min(u0 + i, ulast), ring[i]);
     // super-step u in slot S: fetch u + D - 1 into the slot u - 1 freed, then compute u
-    auto step = [&](auto slot_c, int u) {
+    auto step = [&](auto slot_c, int u) __attribute__((always_inline)) {
       constexpr int S = decltype(slot_c)::value;
       constexpr int SF = (S + D - 1) % D;
       load(min(u + D - 1, ulast), ring[SF]);
@@ -273,88 +346,104 @@ __global__ __launch_bounds__(64 * KSW) void spqr_mfma_kernel(
     }
   }
 
-  // outliers: lane quarter j of wave wv takes CSR entries (4 wv + j) + 4 KSW i
-  // of its column, for all 16 batch rows (x from XT), four entries per round with
-  // every load issued first; the quarters' partial rows are then added so that
-  // quarter j keeps rows 4j .. 4j+3 (the accumulator layout)
-  constexpr int kU = 4;
-  constexpr int kStreams = 4 * KSW;              // lane quarters of the workgroup, one entry stream each
-  float o[16];
+  // outliers, tile by tile: lane quarter j of wave wv takes CSR entries
+  // (4 wv + j) + 4 KSW i of its column, for all 16 batch rows (x from XT), four
+  // entries per round with every load issued first; the quarters' partial rows
+  // are then added so that quarter j keeps rows 4j .. 4j+3 (the accumulator
+  // layout)
 #pragma unroll
-  for (int r = 0; r < 16; ++r) o[r] = 0.0f;
-  const int e0 = row_ptr[ncol], e1 = n0 + r16 < N ? row_ptr[ncol + 1] : e0;
-  for (int e = e0 + 4 * wv + j; e < e1; e += kStreams * kU) {
+  for (int c = 0; c < CT; ++c) {
+    const int eb = row_ptr[ncol[c]];
+    e1[c] = n0 + 16 * c + r16 < N ? row_ptr[ncol[c] + 1] : eb;
+    ef[c] = eb + 4 * wv + j;                     // this quarter's first entry
+  }
+  csr_first();
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    float o[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[r] = 0.0f;
     int kk[kU];
     float v[kU];
 #pragma unroll
     for (int uu = 0; uu < kU; ++uu) {
-      const int eu = e + kStreams * uu;
-      const int ec = min(eu, e1 - 1);
-      kk[uu] = col_idx[ec];
-      v[uu] = eu < e1 ? f16_bits_to_f32(vals[ec]) : 0.0f;
+      kk[uu] = kk0[c][uu];
+      v[uu] = v0[c][uu];
     }
-    uint4 xt[kU][2];
+    for (int e = ef[c]; e < e1[c];) {
+      uint4 xt[kU][2];
 #pragma unroll
-    for (int uu = 0; uu < kU; ++uu) {
-      const uint4* src = reinterpret_cast<const uint4*>(XT + static_cast<size_t>(kk[uu]) * 16);
-      xt[uu][0] = src[0];
-      xt[uu][1] = src[1];
-    }
-#pragma unroll
-    for (int uu = 0; uu < kU; ++uu)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint32_t ww[4] = {xt[uu][hh].x, xt[uu][hh].y, xt[uu][hh].z, xt[uu][hh].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o[8 * hh + 2 * i] = fmaf(v[uu], f16_bits_to_f32(static_cast<uint16_t>(ww[i] & 0xFFFFu)), o[8 * hh + 2 * i]);
-          o[8 * hh + 2 * i + 1] = fmaf(v[uu], f16_bits_to_f32(static_cast<uint16_t>(ww[i] >> 16)), o[8 * hh + 2 * i + 1]);
-        }
+      for (int uu = 0; uu < kU; ++uu) {
+        const uint4* src = reinterpret_cast<const uint4*>(XT + static_cast<size_t>(kk[uu]) * 16);
+        xt[uu][0] = src[0];
+        xt[uu][1] = src[1];
       }
-  }
-  // quarters 0,1 keep rows 0..7 and quarters 2,3 rows 8..15, then even quarters
-  // the first four of those, odd quarters the last four
-  const bool upper = j >= 2;
-  float k8[8];
+      float vc[kU];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const float send = upper ? o[r] : o[r + 8];
-    const float keep = upper ? o[r + 8] : o[r];
-    k8[r] = keep + __shfl_xor(send, 32, 64);
-  }
-  const bool odd = (j & 1) != 0;
-  f32x4_t out4;
+      for (int uu = 0; uu < kU; ++uu) vc[uu] = v[uu];
+      // the next round's entries, loaded before this round's math (unconditional:
+      // inside the loop e1 - 1 is a valid entry, and entries past e1 weigh 0)
+      e += kStreams * kU;
+      csr_round(c, e, kk, v);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float send = odd ? k8[r] : k8[r + 4];
-    const float keep = odd ? k8[r + 4] : k8[r];
-    out4[r] = keep + __shfl_xor(send, 16, 64);
+      for (int uu = 0; uu < kU; ++uu)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t ww[4] = {xt[uu][hh].x, xt[uu][hh].y, xt[uu][hh].z, xt[uu][hh].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[8 * hh + 2 * i] = fmaf(vc[uu], f16_bits_to_f32(static_cast<uint16_t>(ww[i] & 0xFFFFu)), o[8 * hh + 2 * i]);
+            o[8 * hh + 2 * i + 1] = fmaf(vc[uu], f16_bits_to_f32(static_cast<uint16_t>(ww[i] >> 16)), o[8 * hh + 2 * i + 1]);
+          }
+        }
+    }
+    // quarters 0,1 keep rows 0..7 and quarters 2,3 rows 8..15, then even quarters
+    // the first four of those, odd quarters the last four
+    const bool upper = j >= 2;
+    float k8[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float send = upper ? o[r] : o[r + 8];
+      const float keep = upper ? o[r + 8] : o[r];
+      k8[r] = keep + __shfl_xor(send, 32, 64);
+    }
+    const bool odd = (j & 1) != 0;
+    f32x4_t out4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float send = odd ? k8[r] : k8[r + 4];
+      const float keep = odd ? k8[r + 4] : k8[r];
+      out4[r] = keep + __shfl_xor(send, 16, 64);
+    }
+    red[wv][c][lane] = (acc[c] - corr[c]) + out4;
   }
-  red[wv][lane] = (acc - corr) + out4;
   __syncthreads();
   if (wv == 0) {
-    f32x4_t tot = red[0][lane];
 #pragma unroll
-    for (int w2 = 1; w2 < KSW; ++w2) tot += red[w2][lane];
-    const int n = n0 + r16;
-    if (n < N) {
+    for (int c = 0; c < CT; ++c) {
+      f32x4_t tot = red[0][c][lane];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * j + i;
-        if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, tot[i]);
+      for (int w2 = 1; w2 < KSW; ++w2) tot += red[w2][c][lane];
+      const int n = n0 + 16 * c + r16;
+      if (n < N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * j + i;
+          if (m < M) store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, tot[i]);
+        }
       }
     }
   }
 }
 
-template <int KSW, int D>
+template <int KSW, int D, int CT>
 void launch_t(const SpqrArgs& a, const SpqrPrep& p, hipStream_t stream) {
-  const dim3 grid((a.N + 15) / 16);
+  const dim3 grid((a.N + 16 * CT - 1) / (16 * CT));
   if (a.y_dtype == QLIN_F16)
-    hipLaunchKernelGGL((spqr_mfma_kernel<KSW, D, OUT_F16>), grid, dim3(64 * KSW), 0, stream, a.codes, a.stats1,
+    hipLaunchKernelGGL((spqr_mfma_kernel<KSW, D, CT, OUT_F16>), grid, dim3(64 * KSW), 0, stream, a.codes, a.stats1,
                        a.stats2, a.row_ptr, a.col_idx, a.vals, p.Xp, p.Xs, p.XT, a.M, a.K, a.N, a.Y);
   else
-    hipLaunchKernelGGL((spqr_mfma_kernel<KSW, D, OUT_F32>), grid, dim3(64 * KSW), 0, stream, a.codes, a.stats1,
+    hipLaunchKernelGGL((spqr_mfma_kernel<KSW, D, CT, OUT_F32>), grid, dim3(64 * KSW), 0, stream, a.codes, a.stats1,
                        a.stats2, a.row_ptr, a.col_idx, a.vals, p.Xp, p.Xs, p.XT, a.M, a.K, a.N, a.Y);
 }
 
@@ -384,7 +473,10 @@ void spqr_mfma_launch(const SpqrArgs& a, const SpqrPrep& p, hipStream_t stream) 
 #ifndef QLIN_SPQR_RING
 #define QLIN_SPQR_RING 2
 #endif
-  launch_t<QLIN_SPQR_KSW, QLIN_SPQR_RING>(a, p, stream);
+#ifndef QLIN_SPQR_CT
+#define QLIN_SPQR_CT 1
+#endif
+  launch_t<QLIN_SPQR_KSW, QLIN_SPQR_RING, QLIN_SPQR_CT>(a, p, stream);
 }
 
 }  // namespace qlin

@@ -564,15 +564,15 @@ qlin_status gemm_t(const int8_t* Xq, const float* xsc, const int8_t* Wq, const f
   return QLIN_OK;
 }
 
-template <int WM, int WN, int TM, int TN, int BK, int NS>
+template <int WM, int WN, int TM, int TN, int BK, int NS, int WPE = WM * WN / 4>
 qlin_status gemm_big_o(const int8_t* Xq, const float* xsc, const int8_t* Wq, const float* wsc, int M, int N, int K,
                        void* Y, int y_dtype, int32_t* acc_out, WsView ws, size_t* need, hipStream_t stream) {
   const SqI8Op op{xsc, wsc, acc_out};
   return y_dtype == QLIN_F32
-             ? tile_gemm_launch<SqI8Op, WM, WN, TM, TN, BK, NS, OUT_F32>("sq_int8_gemm", Xq, Wq, M, N, K, op, Y, ws,
-                                                                          need, stream)
-             : tile_gemm_launch<SqI8Op, WM, WN, TM, TN, BK, NS, OUT_F16>("sq_int8_gemm", Xq, Wq, M, N, K, op, Y, ws,
-                                                                          need, stream);
+             ? tile_gemm_launch<SqI8Op, WM, WN, TM, TN, BK, NS, OUT_F32, WPE>("sq_int8_gemm", Xq, Wq, M, N, K, op, Y,
+                                                                               ws, need, stream)
+             : tile_gemm_launch<SqI8Op, WM, WN, TM, TN, BK, NS, OUT_F16, WPE>("sq_int8_gemm", Xq, Wq, M, N, K, op, Y,
+                                                                               ws, need, stream);
 }
 
 template <int TM, int NS>
@@ -631,6 +631,10 @@ qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t*
   }
   if (M > 32 && M <= 64 && K % 128 == 0)
     return gemm_big_o<2, 4, 1, 1, 128, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, ws, need, stream);
+#ifdef QLIN_BIG_CFG
+  if (M > 64 && K % 128 == 0)
+    return gemm_big_o<QLIN_BIG_CFG>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, ws, need, stream);
+#endif
   if (M > 64 && K % 128 == 0) {
     auto tiles = [&](int bm, int bn) { return static_cast<long long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 128) >= 160)

@@ -34,8 +34,10 @@
 
 namespace qlin {
 
-template <class Op, int WM, int WN, int TM, int TN, int BK, int NS, int OUTK>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
+// WPE: waves per SIMD the register budget is fitted to (WM WN / 4 per resident
+// workgroup).
+template <class Op, int WM, int WN, int TM, int TN, int BK, int NS, int OUTK, int WPE>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void tile_gemm_kernel(const char* __restrict__ A, const char* __restrict__ B, int M, int N, int Kb, int tiles_m,
                       SkPlan plan, Op op, void* __restrict__ Y, typename Op::part_t* __restrict__ ws,
                       int* __restrict__ counters) {
@@ -115,19 +117,25 @@ void tile_gemm_kernel(const char* __restrict__ A, const char* __restrict__ B, in
       issue(kk + NS - 1);
       const uint4* As = smem + static_cast<size_t>(kk % NS) * STAGE + (32 * TM * wm + col) * CH;
       const uint4* Bs = smem + static_cast<size_t>(kk % NS) * STAGE + A_PIECES + (32 * TN * wn + col) * CH;
+      // the operands of MFMA step st + 1 are read from LDS while step st runs,
+      // so no matrix instruction waits on a read issued just before it
+      i32x4_t a[2][TM], b[2][TN];
+      auto read = [&](int st, i32x4_t (&av)[TM], i32x4_t (&bv)[TN]) {
+        const int c = (KST * h + st) ^ swz;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) av[i] = bitcast<i32x4_t>(As[32 * CH * i + c]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bv[j] = bitcast<i32x4_t>(Bs[32 * CH * j + c]);
+      };
+      read(0, a[0], b[0]);
 #pragma unroll
       for (int st = 0; st < KST; ++st) {
-        const int c = (KST * h + st) ^ swz;
-        i32x4_t a[TM], b[TN];                                   // one MFMA step's operands first
-#pragma unroll
-        for (int i = 0; i < TM; ++i) a[i] = bitcast<i32x4_t>(As[32 * CH * i + c]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = bitcast<i32x4_t>(Bs[32 * CH * j + c]);
-        __builtin_amdgcn_sched_barrier(0);                      // keep its LDS reads ahead of its MFMAs
+        if (st + 1 < KST) read(st + 1, a[(st + 1) & 1], b[(st + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);                      // the next step's reads stay ahead of this one's MFMAs
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j) acc[i][j] = Op::mfma(a[i], b[j], acc[i][j]);
+          for (int j = 0; j < TN; ++j) acc[i][j] = Op::mfma(a[st & 1][i], b[st & 1][j], acc[i][j]);
       }
     }
     wait_vmcnt<0>();                                            // loads past the range end
@@ -197,14 +205,15 @@ void tile_gemm_kernel(const char* __restrict__ A, const char* __restrict__ B, in
 // Launch over a caller workspace: the plan gives every resident workgroup slot
 // of the device (at most kCounterSlots) an equal share of the (tile, K step)
 // units; need != NULL only reports the partial-tile bytes.  Kb % BK == 0.
-template <class Op, int WM, int WN, int TM, int TN, int BK, int NS, int OUTK>
+template <class Op, int WM, int WN, int TM, int TN, int BK, int NS, int OUTK, int WPE = WM * WN / 4>
 qlin_status tile_gemm_launch(const char* fn, const void* A, const void* B, int M, int N, int Kb, const Op& op,
                              void* Y, WsView ws, size_t* need, hipStream_t stream) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN, threads = 64 * WM * WN;
   constexpr size_t lds = static_cast<size_t>(NS) * (BM + BN) * BK;
   static_assert(lds + 16 <= 160 * 1024, "LDS ring within the 160 KB of a CU");
-  using K_t = decltype(&tile_gemm_kernel<Op, WM, WN, TM, TN, BK, NS, OUTK>);
-  const K_t kern = &tile_gemm_kernel<Op, WM, WN, TM, TN, BK, NS, OUTK>;
+  static_assert(WPE * 4 % (WM * WN) == 0, "whole workgroups per CU");
+  using K_t = decltype(&tile_gemm_kernel<Op, WM, WN, TM, TN, BK, NS, OUTK, WPE>);
+  const K_t kern = &tile_gemm_kernel<Op, WM, WN, TM, TN, BK, NS, OUTK, WPE>;
   // resident workgroups per CU, queried once per instantiation and process
   // (thread-safe initialisation of a function-local static), after raising the
   // dynamic LDS limit
@@ -213,7 +222,7 @@ qlin_status tile_gemm_launch(const char* fn, const void* A, const void* B, int M
                               static_cast<int>(lds));
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, threads, lds) != hipSuccess || o <= 0) o = 1;
-    return std::min(o, 2);
+    return std::min(o, WPE * 4 / (WM * WN));
   }();
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
