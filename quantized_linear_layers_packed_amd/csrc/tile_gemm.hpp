@@ -19,7 +19,8 @@
 // NS-stage LDS ring (direct-to-LDS loads, NS - 1 steps ahead, no registers
 // involved), the swizzle realised by choosing which global chunk each lane
 // fetches.  One explicit vmcnt wait and one barrier per step.  The (tile, K
-// step) space is split evenly over the workgroups (stream-K); a tile shared by
+// step) space is split evenly over the workgroups (stream-K, or one workgroup
+// per tile when the tiles nearly fill the device); a tile shared by
 // several workgroups is finished by the last to arrive: exact integer partials
 // are added to its own, float partials are all summed in K order, so the
 // result never depends on arrival order.
@@ -174,16 +175,21 @@ void tile_gemm_kernel(const char* __restrict__ A, const char* __restrict__ B, in
         for (int q = first; q <= last; ++q) {
           if (Op::kExact && q == p) continue;                   // integer partials: the others added to its own
           const part_t* other = part_of(q);
+          // every load of a contributor's part in flight at once, then the
+          // adds: one memory round trip per contributor, not one per block
+          part_t part[TM][TN][16];
 #pragma unroll
           for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              part_t part[16];                                  // one block's loads, then its adds
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) part[r] = sk_load(other + ((i * TN + j) * 16 + r) * 64);
+              for (int r = 0; r < 16; ++r) part[i][j][r] = sk_load(other + ((i * TN + j) * 16 + r) * 64);
 #pragma unroll
-              for (int r = 0; r < 16; ++r) acc[i][j][r] += part[r];
-            }
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[i][j][r] += part[i][j][r];
         }
         if (tid == 0) sk_reset(&counters[first]);
       }
@@ -232,6 +238,12 @@ qlin_status tile_gemm_launch(const char* fn, const void* A, const void* B, int M
   plan.units = tiles * plan.ksteps;
   plan.P = static_cast<int>(std::min<long long>(
       std::min<long long>(static_cast<long long>(occ) * device_cus(), kCounterSlots), plan.units));
+  // One workgroup per tile, no K split, when the tiles fill at least 2/3 of
+  // the resident slots: the split-K hand-off (partials written, counted, read
+  // back) costs more than the idle third.  Measured on the int8 product
+  // 256 x 11008 x 4096 (172 tiles of 128 x 128, 256 slots): 29.5 -> 25.6 us;
+  // at half fill (128 tiles of 128 x 64 on 4096 x 4096) the split stays ahead.
+  if (tiles <= plan.P && 3 * tiles >= 2 * static_cast<long long>(plan.P)) plan.P = static_cast<int>(tiles);
   const size_t partial_bytes = static_cast<size_t>(2) * plan.P * BM * BN * sizeof(typename Op::part_t);
   if (need) {
     *need = partial_bytes;
