@@ -292,6 +292,12 @@ qlin_status launch_sk(const W4Args& a, WsView ws, size_t* need, hipStream_t stre
   plan.units = tiles * plan.ksteps;
   plan.P = static_cast<int>(std::min<long long>(
       std::min<long long>(static_cast<long long>(occ) * device_cus(), kCounterSlots), plan.units));
+  // At least kMinSteps K steps per workgroup: a split tile costs a round of
+  // partial stores, an arrival and a read-back, which thin slices do not repay.
+  // And one workgroup per tile, no split, when the tiles fill 2/3 of the slots.
+  constexpr long long kMinSteps = 8;
+  plan.P = static_cast<int>(std::max<long long>(1, std::min<long long>(plan.P, plan.units / kMinSteps)));
+  if (tiles <= plan.P && 3 * tiles >= 2 * static_cast<long long>(plan.P)) plan.P = static_cast<int>(tiles);
   const size_t partial_bytes = static_cast<size_t>(2) * plan.P * BM * BN * sizeof(float);
   if (need) {
     *need = partial_bytes;
@@ -318,10 +324,33 @@ qlin_status launch_o(const W4Args& a, WsView ws, size_t* need, hipStream_t strea
 qlin_status w4_gemm_sk_launch(const W4Args& a, WsView ws, size_t* need, hipStream_t stream) {
   // RV: accumulator registers per 32-row block that can hold rows below M
   // (register r holds rows 8 (r / 4) + 4 h + r % 4, h the lane half)
+  //
+  // Tile width: 8 waves (256 columns) unless the layer is short along K
+  // (K <= 16384) and gives at most 96 such tiles; then 4 waves (128 columns),
+  // or 2 (64 columns) for batches of at most 64 rows and at most 48 tiles of
+  // 256.  A split of a tile into S parts costs partial traffic of about
+  // 8 BM S / K times its weight bytes, so short-K layers want more tiles and
+  // fewer splits, while long-K layers split cheaply and keep the wider tiles
+  // (fewer dequantized words per multiply-add).  Measured on the 7B-shaped
+  // layers (three, fp16): 65.5 -> 50.6 us at 32 rows, 83.8 -> 64.0 at 64,
+  // 130 -> 94 at 128, 128 -> 113 at 256; the 70B-shaped layers keep 8 waves
+  // except the 8192 x 8192 one below 256 rows (29.7 -> 27.7 us at 32).
   if (a.M <= 8) return launch_o<1, 8, 6, 4>(a, ws, need, stream);
   if (a.M <= 16) return launch_o<1, 8, 6, 8>(a, ws, need, stream);
-  if (a.M <= 32) return launch_o<1, 8, 6, 16>(a, ws, need, stream);
-  if (a.M <= 64) return launch_o<2, 8, 4, 16>(a, ws, need, stream);
+  const int TM = a.M <= 32 ? 1 : a.M <= 64 ? 2 : 4;
+  const long long tiles8 = static_cast<long long>((a.M + 32 * TM - 1) / (32 * TM)) * ((a.N + 255) / 256);
+  const int nw = (a.K > 16384 || tiles8 > 96) ? 8 : (TM <= 2 && tiles8 <= 48) ? 2 : 4;
+  if (TM == 1) {
+    if (nw == 2) return launch_o<1, 2, 6, 16>(a, ws, need, stream);
+    if (nw == 4) return launch_o<1, 4, 6, 16>(a, ws, need, stream);
+    return launch_o<1, 8, 6, 16>(a, ws, need, stream);
+  }
+  if (TM == 2) {
+    if (nw == 2) return launch_o<2, 2, 4, 16>(a, ws, need, stream);
+    if (nw == 4) return launch_o<2, 4, 4, 16>(a, ws, need, stream);
+    return launch_o<2, 8, 4, 16>(a, ws, need, stream);
+  }
+  if (nw == 4) return launch_o<4, 4, 3, 16>(a, ws, need, stream);
   return launch_o<4, 8, 3, 16>(a, ws, need, stream);
 }
 
