@@ -34,6 +34,12 @@ qlin_status need_workspace(const char* fn, const void* ws, size_t ws_bytes, size
   return need_aligned(fn, "workspace", ws);
 }
 
+// The W4 GEMM past the small-batch kernel: the direct-load tile kernel where
+// it measured faster, the register-ring stream-K kernel elsewhere.
+qlin_status w4_big_launch(const W4Args& a, WsView ws, size_t* need, hipStream_t stream) {
+  return w4_tile_supported(a) ? w4_tile_launch(a, ws, need, stream) : w4_gemm_sk_launch(a, ws, need, stream);
+}
+
 // Kernel choice of the W4 forward and the workspace it needs.
 enum class W4Path { kGemv, kSkinny, kSplitK, kGroup };
 
@@ -53,7 +59,7 @@ qlin_status w4_plan(const W4Args& a, W4Plan* p) {
   else p->path = W4Path::kGroup;
   p->prep = a.x_dtype == QLIN_BF16 && p->path != W4Path::kGemv;
   size_t partial = 0;
-  if (p->path == W4Path::kSplitK) QLIN_TRY(w4_gemm_sk_launch(a, WsView{}, &partial, nullptr));
+  if (p->path == W4Path::kSplitK) QLIN_TRY(w4_big_launch(a, WsView{}, &partial, nullptr));
   if (p->path != W4Path::kSplitK && !p->prep) {
     p->total = 0;
     return QLIN_OK;
@@ -117,7 +123,7 @@ qlin_status w4_forward_checked(const char* fn, const void* X, int x_dtype, int M
   switch (plan.path) {
     case W4Path::kGemv: w4_gemv_launch(a, stream); break;
     case W4Path::kSkinny: w4_skinny_launch(a, stream); break;
-    case W4Path::kSplitK: QLIN_TRY(w4_gemm_sk_launch(a, ws, nullptr, stream)); break;
+    case W4Path::kSplitK: QLIN_TRY(w4_big_launch(a, ws, nullptr, stream)); break;
     case W4Path::kGroup: w4_gemm_group_launch(a, stream); break;
   }
   return check_launch(fn);

@@ -31,6 +31,10 @@ void w4_gemv_launch(const W4Args& a, hipStream_t stream);
 // caller's workspace.  With need != NULL only the partial-tile bytes it needs
 // are reported (nothing is launched).
 qlin_status w4_gemm_sk_launch(const W4Args& a, WsView ws, size_t* need, hipStream_t stream);
+// The same product on an LDS ring fed by direct loads (same workspace
+// contract), for the shapes w4_tile_supported accepts.
+bool w4_tile_supported(const W4Args& a);
+qlin_status w4_tile_launch(const W4Args& a, WsView ws, size_t* need, hipStream_t stream);
 // Groups of 32 / 64: one K step per group, exact codes and an fp32 rescale.
 void w4_gemm_group_launch(const W4Args& a, hipStream_t stream);
 // bf16 X [M][K] -> fp16 Xh = X * 2^-e_m per row (round to nearest even) and
