@@ -80,12 +80,6 @@ __device__ __forceinline__ void dma16(const void* global_src, void* lds_wave_bas
                                    16, 0, 0);
 }
 
-// 4-byte form: lane l's dword lands at lds_wave_base + 4 l.
-__device__ __forceinline__ void dma4(const void* global_src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((global_void_ptr)(const_cast<void*>(global_src)), (lds_void_ptr)(lds_wave_base),
-                                   4, 0, 0);
-}
-
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt untouched).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -112,8 +112,8 @@ void w4_tile_kernel(const uint16_t* __restrict__ X, int M, int K, const uint32_t
     const int n0 = (t / tiles_m) * BN;
 
     // Step j (clamped to the range) goes to LDS slot (j - k0) % NS: activation
-    // rows, code rows, then per column the dword holding its fp16 group scale
-    // and its zero-point word.  Everything a step reads arrives by direct
+    // rows, code rows, then the 16-byte chunks of the scale and zero rows that
+    // hold each column's fp16 group scale and zero-point word.  Everything a step reads arrives by direct
     // loads, so the loop holds no loads into registers (whose waits the
     // compiler could not place precisely across the loop).  Rows past M /
     // columns past N read the last one (never stored); positions past the
