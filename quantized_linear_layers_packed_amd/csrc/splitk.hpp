@@ -118,4 +118,30 @@ __device__ __forceinline__ bool sk_run_steps(F& f, int& kk, int k1) {
   else return true;
 }
 
+template <int I, int R, class F>
+__device__ __forceinline__ void sk_group_steps(F& f, int kk) {
+  f(std::integral_constant<int, I>{}, kk + I);
+  if constexpr (I + 1 < R) sk_group_steps<I + 1, R>(f, kk);
+}
+
+template <int I, int R, class F>
+__device__ __forceinline__ void sk_tail_steps(F& f, int kk, int k1) {
+  if (kk + I < k1) {
+    f(std::integral_constant<int, I>{}, kk + I);
+    if constexpr (I + 1 < R) sk_tail_steps<I + 1, R>(f, kk, k1);
+  }
+}
+
+// The same steps kk .. k1-1, as a loop over whole groups of R steps whose body
+// has no exit, then the remaining (fewer than R) steps after it.  With an exit
+// after every step (sk_run_steps in a loop) the exit paths meet at the loop's
+// latch, and the compiler's wait counts at the loop head then assume the ring
+// order of the worst of them (a slot loaded last on one exit path), which for
+// rings deeper than 2 drains the ring once per group.
+template <int R, class F>
+__device__ __forceinline__ void sk_ring_steps(F& f, int kk, int k1) {
+  for (; kk + R <= k1; kk += R) sk_group_steps<0, R>(f, kk);
+  sk_tail_steps<0, R>(f, kk, k1);
+}
+
 }  // namespace qlin

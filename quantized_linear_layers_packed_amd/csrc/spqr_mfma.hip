@@ -331,8 +331,14 @@ __global__ __launch_bounds__(64 * KSW) void spqr_mfma_kernel(
   if (u0 < u1) {
     const int ulast = u1 - 1;
     SuperStep<CT> ring[D];
+    // the prologue's slots are issued in slot order (no interleaving by the
+    // scheduler): the wait counts at the loop head hold for this entry and for
+    // the back edge alike only if both leave the slots' loads in that order
 #pragma unroll
-    for (int i = 0; i < D - 1; ++i) load(min(u0 + i, ulast), ring[i]);
+    for (int i = 0; i < D - 1; ++i) {
+      load(min(u0 + i, ulast), ring[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // super-step u in slot S: fetch u + D - 1 into the slot u - 1 freed, then compute u
     auto step = [&](auto slot_c, int u) __attribute__((always_inline)) {
       constexpr int S = decltype(slot_c)::value;
@@ -341,9 +347,7 @@ __global__ __launch_bounds__(64 * KSW) void spqr_mfma_kernel(
       __builtin_amdgcn_sched_barrier(0);
       compute(u, ring[S]);
     };
-    int u = u0;
-    while (sk_run_steps<0, D>(step, u, u1)) {
-    }
+    sk_ring_steps<D>(step, u0, u1);
   }
 
   // outliers, tile by tile: lane quarter j of wave wv takes CSR entries

@@ -198,8 +198,18 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
       __syncthreads();
     };
 
-    int kk = k0;
-    while (sk_run_steps<0, R>(step, kk, k1)) {
+    // Whole groups of R steps in an exit-free loop (no ring drain at the loop
+    // head), except for two tiles that keep the step-by-step exits: the
+    // 4 x 32-row, 8-wave tile, whose registers do not hold the duplicated tail
+    // steps (it would spill), and the 32-row, 2-wave tile, which measured
+    // 10% slower with the group loop on the long-K layers (more registers
+    // freed for occupancy, but more K splits per tile).
+    if constexpr ((TM == 4 && NW == 8) || (TM == 1 && NW == 2)) {
+      int kk = k0;
+      while (sk_run_steps<0, R>(step, kk, k1)) {
+      }
+    } else {
+      sk_ring_steps<R>(step, k0, k1);
     }
 
     // ---- finish the tile: lane holds column n, rows 8*(r/4) + 4*h + r%4 of each

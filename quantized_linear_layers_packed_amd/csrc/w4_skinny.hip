@@ -150,9 +150,7 @@ __global__ __launch_bounds__(64 * NWV) void w4_skinny_kernel(const uint16_t* X, 
       __builtin_amdgcn_sched_barrier(0);     // keep the prefetch issued ahead of the math
       compute(b, wq[S], av[S], sv[S], zv[S]);
     };
-    int b = b0;
-    while (sk_run_steps<0, D>(step, b, b1)) {
-    }
+    sk_ring_steps<D>(step, b0, b1);
   }
 
   // fixed-order sum of the waves' tiles; lane l of a tile holds column
