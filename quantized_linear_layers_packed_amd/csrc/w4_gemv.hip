@@ -81,6 +81,13 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
     const uint32_t* __restrict__ qzeros, int N, int gshift, void* __restrict__ Y) {
   constexpr int RPW = 64 / LPR;
   static_assert(KS == 1 || LPR == 64, "K split across waves needs whole-wave rows");
+  // With three or more blocks per lane the codes are unpacked after the
+  // barrier, block by block: unpacked early they hold 16 registers per block
+  // (74 / 93 VGPRs at 3 / 4 blocks, 6 / 5 waves per SIMD), late the kernel fits
+  // 8 waves per SIMD, and the 4096 x 11008 layer measured 8.5 -> 8.15 us.
+  // With one or two blocks the early unpack, overlapping the staging, is
+  // faster.
+  constexpr bool kLateUnpack = BPL >= 3;
   extern __shared__ uint4 smem[];
   __shared__ float red[kWaves][MT];            // per-wave partial sums (K split)
   const int C = K >> 5;                        // chunks per row
@@ -196,11 +203,13 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
     const uint32_t zw = lane_value(zv, base + (g >> 3));
     s[b] = f16_bits_to_f32(static_cast<uint16_t>(sbits));
     zf[b] = static_cast<float>((zw >> (4 * (g & 7))) & 15u);
-    if (c < C) {
-      Codec::unpack(w[b].x, p[b][0]);
-      Codec::unpack(w[b].y, p[b][1]);
-      Codec::unpack(w[b].z, p[b][2]);
-      Codec::unpack(w[b].w, p[b][3]);
+    if constexpr (!kLateUnpack) {
+      if (c < C) {
+        Codec::unpack(w[b].x, p[b][0]);
+        Codec::unpack(w[b].y, p[b][1]);
+        Codec::unpack(w[b].z, p[b][2]);
+        Codec::unpack(w[b].w, p[b][3]);
+      }
     }
   }
   __syncthreads();                             // staged activations visible
@@ -212,6 +221,12 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
   for (int b = 0; b < BPL; ++b) {
     const int c = LPR * (KS * b + part) + sl;
     if (c < C) {
+      if constexpr (kLateUnpack) {
+        Codec::unpack(w[b].x, p[b][0]);
+        Codec::unpack(w[b].y, p[b][1]);
+        Codec::unpack(w[b].z, p[b][2]);
+        Codec::unpack(w[b].w, p[b][3]);
+      }
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m < M) {
