@@ -235,7 +235,7 @@ qlin_status spqr_workspace_bytes(int M, int K, int N, int y_dtype, size_t* bytes
   if (M > 16) return fail(QLIN_EUNSUPPORTED, std::string(fn) + ": M must be at most 16");
   if (K % 256 != 0) return fail(QLIN_EINVAL, std::string(fn) + ": K must be a multiple of 256");
   if (y_dtype != QLIN_F16 && y_dtype != QLIN_F32) return fail(QLIN_EINVAL, std::string(fn) + ": y_dtype must be F16 or F32");
-  *bytes = M >= QLIN_SPQR_MFMA_MIN_M ? kCounterBytes + spqr_prep_bytes(K) : 0;
+  *bytes = spqr_use_mfma(M, K, N) ? kCounterBytes + spqr_prep_bytes(K) : 0;
   return QLIN_OK;
 }
 
@@ -260,7 +260,7 @@ qlin_status spqr_forward(const uint16_t* X, int M, int K,
   QLIN_TRY(need_aligned(fn, "Y", Y));
   // the prepass area starts after the counter slots, which stay untouched, so
   // one workspace can serve this call and the split-K calls in any order
-  const size_t total = M >= QLIN_SPQR_MFMA_MIN_M ? kCounterBytes + spqr_prep_bytes(K) : 0;
+  const size_t total = spqr_use_mfma(M, K, N) ? kCounterBytes + spqr_prep_bytes(K) : 0;
   QLIN_TRY(need_workspace(fn, workspace, workspace_bytes, total));
   SpqrArgs a{X, M, K, N, codes, stats1, stats2, row_ptr, col_idx, vals, Y, y_dtype};
   if (total) spqr_mfma_launch(a, spqr_prep_view(static_cast<char*>(workspace) + kCounterBytes, K), stream);

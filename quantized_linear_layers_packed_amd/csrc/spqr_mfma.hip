@@ -1,4 +1,4 @@
-// SpQR product for batches of 5..16 tokens on the matrix cores, gfx950.
+// SpQR product for batches of 4..16 tokens on the matrix cores, gfx950.
 //
 // Y[m][n] = sum_g s_hat[n][g] * (sum_{k in g} x[m][k] q[n][k] - z_hat[n][g] * sum_{k in g} x[m][k])
 //           + sum_{(n,k,v) in CSR} x[m][k] * v
@@ -9,7 +9,8 @@
 // GEMV's dot products (one v_dot2 per two weights per token) dominate; here
 // each group's exact integer codes go through one v_mfma_f32_16x16x16_f16 for
 // 16 tokens x 16 output columns, so the vector work per weight no longer grows
-// with the batch (measured: flat from 2 to 16 tokens, ahead of the GEMV from 5):
+// with the batch (measured: flat from 2 to 16 tokens, ahead of the GEMV from 4
+// tokens, or from 6 on layers with K >= 2N):
 //   * P = sum_{k in g} x (1024 + q): the codes enter as fp16 1024 + q built by
 //     a mask and an or (exact), and the 1024 is folded into the zero term
 //     below; one MFMA per group and column tile, then acc += s_hat * P in fp32
