@@ -50,7 +50,7 @@ namespace {
 
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kPrepThreads = 256;
+constexpr int kPrepThreads = 64;          // small workgroups spread the short pass over more CUs
 
 // Within-chunk offsets (k % 32) of the four codes lane quarter j unpacks for
 // group a (codes 0..15 of the chunk) and group b (16..31), in unpack order: the

@@ -47,7 +47,7 @@ def test_unpack_is_bit_exact():
 @pytest.mark.parametrize("p", [0.0, 0.01, 0.05])
 def test_ragged_shapes(p):
     # K >= 2N runs two column tiles per wave on the matrix-core path, K < 2N one
-    for (N, K) in ((37, 512), (16, 256), (50, 2560), (21, 26624), (133, 256), (600, 768)):
+    for (N, K) in ((37, 512), (16, 256), (50, 2560), (21, 26624), (133, 256), (600, 768), (1100, 2048)):
         W = synth.student_t3_f32((N, K), 0.02, f"gpu/spqr/rag{N}")
         d = dev_pack(qlin.spqr_pack(W, p))
         st = ospqr.encode(W, p)
@@ -97,11 +97,13 @@ def test_33b_full_layer_sampled_rows(layer):
         check_close(Y[:, rows], ospqr.forward(X, st, K), f"{N}x{K} M={M}")
 
 
-def test_matrix_core_path_leaves_the_counter_slots_zero():
-    """The prepass writes after the 16 KiB of split-K arrival counters, so a
-    workspace shared with the W4 and int8 GEMMs still has them zero."""
+@pytest.mark.parametrize("N,K", [(48, 1024), (1100, 2048)])
+def test_matrix_core_path_leaves_the_counter_slots_zero(N, K):
+    """The prepass writes after the 16 KiB of split-K arrival counters (on both
+    routes of the matrix-core path: K >= 2N and K < 2N), so a workspace shared
+    with the W4 and int8 GEMMs still has them zero."""
     torch = torch_cuda()
-    N, K, M = 48, 1024, 8
+    M = 8
     W = synth.student_t3_f32((N, K), 0.02, "gpu/spqr/wsctr")
     d = dev_pack(qlin.spqr_pack(W, 0.01))
     need = qlin.spqr_workspace_bytes(M, K, N, F32)
