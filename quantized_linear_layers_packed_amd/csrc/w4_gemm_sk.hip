@@ -350,18 +350,19 @@ qlin_status w4_gemm_sk_launch(const W4Args& a, WsView ws, size_t* need, hipStrea
   const int TM = a.M <= 32 ? 1 : a.M <= 64 ? 2 : 4;
   const long long tiles8 = static_cast<long long>((a.M + 32 * TM - 1) / (32 * TM)) * ((a.N + 255) / 256);
   const int nw = (a.K > 16384 || tiles8 > 96) ? 8 : (TM <= 2 && tiles8 <= 48) ? 2 : 4;
-  // The 8-wave tiles of 32 and 64 rows (the long-K or wide layers) keep a
-  // 3-deep ring: measured on the 70B-shaped layers against 6 / 4 deep,
-  // 151 -> 145 us at 32 rows and 174 -> 171 us at 64 (a 2-deep ring: 166 / 170;
-  // a 4-deep one capped at 128 VGPRs for two workgroups per CU: 172 at 32 rows).
+  // Register rings 3 deep at every tile height: measured against the former
+  // 6 / 4 deep at 32 / 64 rows, 70B-shaped layers 151 -> 145 us at 32 rows and
+  // 174 -> 166 at 64, 7B-shaped layers 52.4 -> 51.0 and 65.1 -> 63.2 (a 2-deep
+  // ring: 166 / 170 on the 70B-shaped layers; a 4-deep one capped at 128 VGPRs
+  // for two workgroups per CU: 172 at 32 rows).
   if (TM == 1) {
-    if (nw == 2) return launch_o<1, 2, 6, 16>(a, ws, need, stream);
-    if (nw == 4) return launch_o<1, 4, 6, 16>(a, ws, need, stream);
+    if (nw == 2) return launch_o<1, 2, 3, 16>(a, ws, need, stream);
+    if (nw == 4) return launch_o<1, 4, 3, 16>(a, ws, need, stream);
     return launch_o<1, 8, 3, 16>(a, ws, need, stream);
   }
   if (TM == 2) {
-    if (nw == 2) return launch_o<2, 2, 4, 16>(a, ws, need, stream);
-    if (nw == 4) return launch_o<2, 4, 4, 16>(a, ws, need, stream);
+    if (nw == 2) return launch_o<2, 2, 3, 16>(a, ws, need, stream);
+    if (nw == 4) return launch_o<2, 4, 3, 16>(a, ws, need, stream);
     return launch_o<2, 8, 3, 16>(a, ws, need, stream);
   }
   if (nw == 4) return launch_o<4, 4, 3, 16>(a, ws, need, stream);
