@@ -206,12 +206,16 @@ bool w4_skinny_supported(int M, int K, int G) { return M >= 1 && M <= 16 && (G =
 // Wide layers: 4 or 2 column tiles per workgroup (each activation fragment then
 // feeds 4 or 2 matrix instructions, so the activations are re-read from cache 4
 // or 2 times less) as long as that leaves at least 160 workgroups; one tile
-// otherwise (a 4096-column layer keeps its 256 workgroups).
+// otherwise (a 4096-column layer keeps its 256 workgroups), with a ring 3 deep,
+// or 2 deep on long rows: measured at 8 / 16 rows against the former 4 deep,
+// 4096 x 4096 8.3 -> 6.9 / 10.0 -> 8.2 us (3 deep), 4096 x 11008 13.5 -> 13.1 /
+// 18.1 -> 17.1 us (2 deep).
 void w4_skinny_launch(const W4Args& a, hipStream_t stream) {
   const long long wg4 = (a.N + 4 * kCols - 1) / (4 * kCols), wg2 = (a.N + 2 * kCols - 1) / (2 * kCols);
   if (wg4 >= 160) launch_o<4, 1, 3, 4>(a, stream);
   else if (wg2 >= 160) launch_o<4, 1, 2, 2>(a, stream);
-  else launch_o<4, 1, 4, 1>(a, stream);
+  else if (a.K > 8192) launch_o<4, 1, 2, 1>(a, stream);
+  else launch_o<4, 1, 3, 1>(a, stream);
 }
 
 }  // namespace qlin

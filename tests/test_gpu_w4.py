@@ -217,8 +217,9 @@ def test_small_batches_through_the_mfma_kernels(x_dtype):
     staging: 4..16 rows run the small-batch kernel (K split over the waves of a
     workgroup, 16 columns each, ragged N), 17 and more the stream-K GEMM with
     few output tiles, so every tile's K range is split over many workgroups and
-    the fix-up sums only the accumulator registers that can hold rows below M."""
-    for (N, K, G) in ((512, 8192, 128), (300, 6144, 256)):
+    the fix-up sums only the accumulator registers that can hold rows below M.
+    K = 10240 takes the small-batch kernel's shallower ring for long rows."""
+    for (N, K, G) in ((512, 8192, 128), (300, 6144, 256), (130, 10240, 128)):
         W = synth.normal_f32((N, K), 0.02, f"gpu/w4/smallm{N}")
         packed = dev_pack(W, G)
         st = ow4.encode(W, G)
