@@ -116,7 +116,9 @@ def time_steps(torch, step_fns, steps, warmup, copies):
     rotation (``copies`` steps), so host launch overhead stays out of the
     measurement.  Each kernel's average duration comes from a graph of that
     kernel alone over the same rotation, launched back to back (the events
-    bracket ``copies`` launches on the stream they run on)."""
+    bracket ``copies`` launches on the stream they run on).  Per-dispatch
+    medians come from the rocprofv3 kernel trace (bench.py --summarize):
+    events around single replays add the replay launch gap."""
     for i in range(warmup):
         for f in step_fns:
             f(i)
@@ -583,11 +585,12 @@ def summarize(d):
                 key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["LDS_Block_Size"]))
                 groups[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
         out.append("kernel trace (rocprofv3 --kernel-trace --stats): per kernel and launch shape")
-        out.append(f"{'kernel':92s} {'grid':>9s} {'lds':>6s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s}")
+        out.append(f"{'kernel':92s} {'grid':>9s} {'lds':>6s} {'calls':>6s} {'avg_us':>9s} {'med_us':>9s} {'min_us':>9s}")
         for (k, g, l), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
             if "spin_kernel" in k or "FillFunctor" in k:
                 continue
-            out.append(f"{k:92s} {g:9d} {l:6d} {len(v):6d} {np.mean(v) / 1e3:9.3f} {np.min(v) / 1e3:9.3f}")
+            out.append(f"{k:92s} {g:9d} {l:6d} {len(v):6d} {np.mean(v) / 1e3:9.3f} {np.median(v) / 1e3:9.3f} "
+                       f"{np.min(v) / 1e3:9.3f}")
     cnt = {}
     for c in ("fetch", "write"):
         p = os.path.join(d, c, "run_counter_collection.csv")
@@ -728,6 +731,14 @@ def main():
     layer_bytes = [l["wbytes"] + l["ios"][1] for l in layers]
     per_layer = [{"shape": f"{l['N']}x{l['K']}", "bytes": b, "us": round(p * 1e3, 3),
                   "GB/s": round(b / (p * 1e-3) / 1e9, 1)} for l, b, p in zip(layers, layer_bytes, per)]
+    # the same steps all on the first weight copy: served from the 256 MB
+    # last-level cache, not from HBM (a labelled cache-resident figure, never
+    # the value); graphs of the same length as the rotation
+    hot_ms, hot_per = time_steps(torch, [lambda i, f=f: f(0) for f in fns], args.steps, args.warmup,
+                                 len(layers[0]["packed"]))
+    hot = {"note": "one weight copy, cache-resident (256 MB last-level cache), not an HBM figure",
+           "ms_per_step": round(hot_ms, 5), "GB/s_per_step": round(step_bytes / (hot_ms * 1e-3) / 1e9, 1),
+           "per_layer_us": [round(p * 1e3, 3) for p in hot_per]}
     rot = len(layers[0]["packed"])
     del layers, fns
     torch.cuda.empty_cache()
@@ -758,6 +769,7 @@ def main():
                      "stream_read_floor_us": peaks["floor_us"],
                      "frac_of_floor": round(sum(peaks["floor_us"]) / (kern_ms * 1e3), 4)},
         "measured_peaks": {k: v for k, v in peaks.items() if k != "floor_us"},
+        "hot_cache_resident": hot,
     }
 
     if not args.no_paths:
