@@ -104,20 +104,23 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
   const int ng = K >> gshift, nzw = (ng + 7) >> 3;
   const int cshift = gshift - 5;               // chunk -> group
 
-  // ---- 1. activation loads for the staging: chunk tid of batch rows 0 and 1
-  //      (C <= 512 = threads, so each thread stages at most one chunk per row).
-  //      Every load up to the staging is unconditional (threads past the row
-  //      read its last chunk, lanes past it the last valid address), so the
-  //      count of loads issued after these is fixed and the staging waits for
-  //      the activations alone, not for the weight stream behind them.
+  // ---- 1. activation loads for the staging of batch rows 0 and 1, coalesced:
+  //      thread tid loads the 16-byte pieces tid + 512 r (r < RX) of the row,
+  //      so each instruction covers 1 KB contiguous and the four pieces of a
+  //      32-code chunk land in four adjacent lanes.  Every load up to the
+  //      staging is unconditional (pieces past the row re-read its last one,
+  //      lanes past it the last valid address), so the count of loads issued
+  //      after these is fixed and the staging waits for the activations alone,
+  //      not for the weight stream behind them.
   constexpr int XR = MT < 2 ? MT : 2;          // batch rows staged from these registers (M >= XR)
-  const bool stager = tid < C;
-  uint4 xv[XR][4];
+  constexpr int RX = (KS * BPL + 1) / 2;       // rounds: a row has 4 C <= 256 KS BPL pieces
+  const int P4 = 4 * C;
+  uint4 xv[XR][RX];
 #pragma unroll
   for (int m = 0; m < XR; ++m) {
-    const uint4* src = reinterpret_cast<const uint4*>(X + m * K) + 4 * min(tid, C - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(X + m * K);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xv[m][i] = src[i];
+    for (int r = 0; r < RX; ++r) xv[m][r] = src[min(tid + 512 * r, P4 - 1)];
   }
 
   // ---- 2. weights, then the row's scales and zero words (rows past N read row N - 1)
@@ -138,28 +141,46 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
   uint32_t sv[SV];
   const uint16_t* srow = scales + nn * ng;
 #pragma unroll
-  for (int t = 0; t < SV; ++t) sv[t] = static_cast<uint32_t>(srow[min(LPR * t + sl, ng - 1)]);
+  for (int t = 0; t < SV; ++t)                 // registers past the row's groups are never read: not loaded
+    sv[t] = LPR * t < ng ? static_cast<uint32_t>(srow[min(LPR * t + sl, ng - 1)]) : 0u;
   // nzw <= LPR for the shapes that pick LPR; lanes past it hold the last word
   const uint32_t zv = qzeros[nn * nzw + min(sl, nzw - 1)];
 
-  // ---- 3. finish staging the activations: rows 0 and 1 from the registers
-  //      above, any further rows (batches of three or more) loaded here.  The
-  //      branch condition reads every loaded activation word (its second term
-  //      is never true: M >= 1), so the compiler cannot sink those loads into
-  //      the branch, behind the weight stream.
-  uint32_t xfold = 0u;
+  // ---- 3. staging.  Rows 0 and 1 from the registers above: each lane pairs
+  //      its piece, the quad adds the chunk's two sums (the same values as a
+  //      sequential sum up to the order of four fp32 additions).  Further rows
+  //      (batches of three or more): chunk tid per thread, loaded here.
+  auto quad_sum = [](float v) {
+    v += bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(v), 0xB1, 0xF, 0xF, true));   // pairs
+    v += bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(v), 0x4E, 0xF, 0xF, true));   // quads
+    return v;
+  };
 #pragma unroll
   for (int m = 0; m < XR; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xfold ^= xv[m][i].x ^ xv[m][i].y ^ xv[m][i].z ^ xv[m][i].w;
-  const bool stage_here = stager | ((M <= 0) & (xfold == 0u));
-  if (stage_here) {
-    auto stage_row = [&](int m, const uint4 (&v4)[4]) {
+    for (int r = 0; r < RX; ++r) {
+      const int piece = tid + 512 * r;
+      const uint32_t u[4] = {xv[m][r].x, xv[m][r].y, xv[m][r].z, xv[m][r].w};
+      uint32_t P[4];
+      pair_up(u, P);
+      float2 es = make_float2(0.0f, 0.0f);
+      Codec::stage(P, es);
+      es.x = quad_sum(es.x);
+      es.y = quad_sum(es.y);
+      if (piece < P4) {                          // whole quads: P4 and 512 r are multiples of 4
+        xl[(m * 4 + (piece & 3)) * C + (piece >> 2)] = make_uint4(P[0], P[1], P[2], P[3]);
+        if ((piece & 3) == 0) xs[m * C + (piece >> 2)] = Codec::sums(es);
+      }
+    }
+  if (tid < C) {
+    for (int m = XR; m < MT && m < M; ++m) {
+      const uint4* src = reinterpret_cast<const uint4*>(X + m * K) + 4 * tid;
       float2 es = make_float2(0.0f, 0.0f);
       uint4 pq[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t u[4] = {v4[i].x, v4[i].y, v4[i].z, v4[i].w};
+        const uint4 v = src[i];
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
         uint32_t P[4];
         pair_up(u, P);
         Codec::stage(P, es);
@@ -168,15 +189,6 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) xl[(m * 4 + i) * C + tid] = pq[i];
       xs[m * C + tid] = Codec::sums(es);
-    };
-#pragma unroll
-    for (int m = 0; m < XR; ++m) stage_row(m, xv[m]);
-    for (int m = XR; m < MT && m < M; ++m) {
-      uint4 v4[4];
-      const uint4* src = reinterpret_cast<const uint4*>(X + m * K) + 4 * tid;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v4[i] = src[i];
-      stage_row(m, v4);
     }
   }
   // ---- 4. unpack the codes and look up the groups' scales and zero points
