@@ -90,6 +90,7 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
   constexpr bool kLateUnpack = BPL >= 3;
   extern __shared__ uint4 smem[];
   __shared__ float red[kWaves][MT];            // per-wave partial sums (K split)
+  constexpr int ROWS = kWaves / KS * RPW;      // output rows of the workgroup
   const int C = K >> 5;                        // chunks per row
   uint4* xl = smem;                            // [MT][4][C] activation pairs
   float2* xs = reinterpret_cast<float2*>(smem + MT * 4 * C);   // [MT][C] (E, S)
@@ -102,6 +103,8 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
   const int n = (blockIdx.x * (kWaves / KS) + wv / KS) * RPW + sub;
   const bool nok = n < N;
   const int ng = K >> gshift, nzw = (ng + 7) >> 3;
+  uint32_t* lz = reinterpret_cast<uint32_t*>(xs + MT * C);       // [ROWS][nzw] zero words
+  uint16_t* ls = reinterpret_cast<uint16_t*>(lz + ROWS * nzw);   // [ROWS][ng] scales
   const int cshift = gshift - 5;               // chunk -> group
 
   // ---- 1. activation loads for the staging of batch rows 0 and 1, coalesced:
@@ -123,7 +126,24 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
     for (int r = 0; r < RX; ++r) xv[m][r] = src[min(tid + 512 * r, P4 - 1)];
   }
 
-  // ---- 2. weights, then the row's scales and zero words (rows past N read row N - 1)
+  // ---- 2. the scales and zero words of the workgroup's rows (contiguous in
+  //      memory: one 2- / 4-byte piece per thread, only waves holding pieces
+  //      load, indices clamped into the arrays), staged in LDS with the
+  //      activations; issued before the weights so that the staging waits
+  //      never wait for the weight stream.  Then the weights (rows past N read
+  //      row N - 1).
+  constexpr int RS = (ROWS * 64 * KS * BPL + kThreads - 1) / kThreads;   // rounds for up to one group per chunk
+  const int n0 = blockIdx.x * ROWS;
+  const int ns = ROWS * ng, nz = ROWS * nzw;
+  const int wfirst = __builtin_amdgcn_readfirstlane(64 * wv);      // wave-uniform: whole waves skip
+  const size_t slast = static_cast<size_t>(N) * ng - 1, zlast = static_cast<size_t>(N) * nzw - 1;
+  uint32_t lsv[RS];
+#pragma unroll
+  for (int r = 0; r < RS; ++r)
+    lsv[r] = wfirst + kThreads * r < ns
+                 ? static_cast<uint32_t>(scales[min(static_cast<size_t>(n0) * ng + tid + kThreads * r, slast)])
+                 : 0u;
+  const uint32_t lzv = wfirst < nz ? qzeros[min(static_cast<size_t>(n0) * nzw + tid, zlast)] : 0u;
   const size_t nn = static_cast<size_t>(min(n, N - 1));
   const uint4* qrow = reinterpret_cast<const uint4*>(qweight + nn * (K >> 3));
   // chunk of block b: LPR (KS b + part) + sl (the KS waves of a row interleave
@@ -134,17 +154,6 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
     const int c = LPR * (KS * b + part) + sl;
     w[b] = load_stream16(qrow + min(c, C - 1));
   }
-  // scale registers: lane i of the row, register t, holds the scale of group
-  // LPR t + i (a row has at most one group per chunk, so KS * BPL registers
-  // suffice; lanes past the row's groups hold its last scale, never read)
-  constexpr int SV = KS * BPL;
-  uint32_t sv[SV];
-  const uint16_t* srow = scales + nn * ng;
-#pragma unroll
-  for (int t = 0; t < SV; ++t)                 // registers past the row's groups are never read: not loaded
-    sv[t] = LPR * t < ng ? static_cast<uint32_t>(srow[min(LPR * t + sl, ng - 1)]) : 0u;
-  // nzw <= LPR for the shapes that pick LPR; lanes past it hold the last word
-  const uint32_t zv = qzeros[nn * nzw + min(sl, nzw - 1)];
 
   // ---- 3. staging.  Rows 0 and 1 from the registers above: each lane pairs
   //      its piece, the quad adds the chunk's two sums (the same values as a
@@ -191,30 +200,18 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
       xs[m * C + tid] = Codec::sums(es);
     }
   }
+#pragma unroll
+  for (int r = 0; r < RS; ++r)
+    if (tid + kThreads * r < ns) ls[tid + kThreads * r] = static_cast<uint16_t>(lsv[r]);
+  if (tid < nz) lz[tid] = lzv;
   // ---- 4. unpack the codes and look up the groups' scales and zero points
   //      while the activation staging is still in flight (this needs only the
   //      weights), then the dot products once the staged activations are visible
-  const int base = sub * LPR;                  // first lane of this row
+  const int rowl = (wv / KS) * RPW + sub;     // this row within the workgroup
   uint32_t p[BPL][4][4];
-  float s[BPL], zf[BPL];
 #pragma unroll
   for (int b = 0; b < BPL; ++b) {
     const int c = LPR * (KS * b + part) + sl;
-    // cross-lane reads with every lane active (a read from a lane that is
-    // inactive in a divergent branch returns 0): lanes past the row end read
-    // the last group's values and discard them
-    const int g = min(c, C - 1) >> cshift;
-    uint32_t sbits = 0;
-#pragma unroll
-    for (int t = 0; t < SV; ++t) {
-      if (LPR * t < ng) {                            // uniform: registers holding real groups
-        const uint32_t v = lane_value(sv[t], base + g % LPR);
-        if (g / LPR == t) sbits = v;
-      }
-    }
-    const uint32_t zw = lane_value(zv, base + (g >> 3));
-    s[b] = f16_bits_to_f32(static_cast<uint16_t>(sbits));
-    zf[b] = static_cast<float>((zw >> (4 * (g & 7))) & 15u);
     if constexpr (!kLateUnpack) {
       if (c < C) {
         Codec::unpack(w[b].x, p[b][0]);
@@ -224,7 +221,14 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(
       }
     }
   }
-  __syncthreads();                             // staged activations visible
+  __syncthreads();                             // staged activations and statistics visible
+  float s[BPL], zf[BPL];
+#pragma unroll
+  for (int b = 0; b < BPL; ++b) {               // lanes past the row end read its last group, discarded
+    const int g = min(LPR * (KS * b + part) + sl, C - 1) >> cshift;
+    s[b] = f16_bits_to_f32(ls[rowl * ng + g]);
+    zf[b] = static_cast<float>((lz[rowl * nzw + (g >> 3)] >> (4 * (g & 7))) & 15u);
+  }
 
   float res[MT];
 #pragma unroll
@@ -290,7 +294,9 @@ void launch_t(const W4Args& a, hipStream_t stream) {
   constexpr int RPW = 64 / LPR;
   constexpr int ROWS = kWaves / KS * RPW;      // output rows per workgroup
   const int C = a.K >> 5;
-  const size_t lds = static_cast<size_t>(MT) * 4 * C * 16 + static_cast<size_t>(MT) * C * 8;
+  const int ng = a.K / a.G, nzw = (ng + 7) / 8;
+  const size_t lds = static_cast<size_t>(MT) * 4 * C * 16 + static_cast<size_t>(MT) * C * 8 +
+                     static_cast<size_t>(ROWS) * (4 * nzw + 2 * ng);
   const int grid = (a.N + ROWS - 1) / ROWS;
   const int gshift = __builtin_ctz(static_cast<unsigned>(a.G));
   hipLaunchKernelGGL((w4_gemv_kernel<MT, LPR, KS, BPL, Codec, OUTK>), dim3(grid), dim3(kThreads), lds, stream,
@@ -363,7 +369,9 @@ void w4_unpack_launch(const uint32_t* qweight, const uint32_t* qzeros, int N, in
 size_t w4_gemv_lds_bytes(int M, int K) {
   const size_t MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
   const size_t C = static_cast<size_t>(K) / 32;
-  return MT * 4 * C * 16 + MT * C * 8;
+  // activations and their sums, and the statistics of up to 8 rows at one
+  // group per chunk (the smallest group size)
+  return MT * 4 * C * 16 + MT * C * 8 + 8 * (4 * ((C + 7) / 8) + 2 * C);
 }
 
 bool w4_gemv_supported(int M, int K, int G) {
