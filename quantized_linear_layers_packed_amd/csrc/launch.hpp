@@ -78,13 +78,17 @@ struct SpqrPrep {
   const float* Xs;
   const uint16_t* XT;
 };
-// Batches that run the matrix-core path (the rest run the GEMV): from 4
-// tokens where rows are short against the column count (K < 2N), from 6 where
-// they are long, which the GEMV streams with fewer, longer waves.  Measured per
-// layer on the 33B-shaped layers (GEMV vs matrix-core, us): 6656 x 6656 27.0 vs
-// 22.3 at M = 4; 17920 x 6656 62.4 vs 56.3 at M = 4, 54.7 vs 56.5 at M = 3;
-// 6656 x 17920 45.5 vs 55.2 at M = 4, about +5.5 per token above that.
-inline bool spqr_use_mfma(int M, int K, int N) { return M >= (K >= 2 * N ? 6 : 4); }
+// Batches that run the matrix-core path (the rest run the GEMV): from 5
+// tokens.  Measured per layer on the 33B-shaped layers (GEMV vs matrix-core,
+// us): 6656 x 6656 21.8 vs 22.9 at M = 4; 17920 x 6656 44.8 vs 58.8 at M = 4;
+// 6656 x 17920 59.2 at M = 5 vs 56.0 at M = 6 (the matrix-core time hardly
+// moves with M: 55.9 at M = 8, 56.0 at M = 12).  From 5 rows the GEMV stages a
+// batch of 8, which halves its K slices.
+inline bool spqr_use_mfma(int M, int K, int N) {
+  (void)K;
+  (void)N;
+  return M >= 5;
+}
 size_t spqr_prep_bytes(int K);
 SpqrPrep spqr_prep_view(char* base, int K);
 void spqr_mfma_launch(const SpqrArgs& a, const SpqrPrep& p, hipStream_t stream);

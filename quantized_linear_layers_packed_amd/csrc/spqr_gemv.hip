@@ -114,11 +114,14 @@ __device__ __forceinline__ float row_sum64(float v) {
 // contiguous bytes per load instruction).  Per slice, in this order:
 //   1. the activation loads for the LDS staging (one 32-value piece per
 //      thread; vector loads return in order, so these arrive first),
-//   2. everything the wave needs from HBM: its chunks, the statistics of its
-//      blocks and, on the first slice, up to 4 CSR entries per lane (no load
-//      waits for another before the stream is issued),
+//   2. everything else the workgroup needs from HBM: the statistics of its
+//      rows' blocks in the slice (one 4-byte piece per thread: a row's blocks
+//      are contiguous, so this takes a few wide requests per workgroup rather
+//      than gathers by every wave), the wave's chunks and, on the first slice,
+//      up to 4 CSR entries per lane (no load waits for another before the
+//      stream is issued),
 //   3. the staging (pairs in the unpack order + two per-chunk sums), then
-//      the wave's statistics into LDS,
+//      the statistic pieces into LDS,
 //   4. the code unpack, while other waves' staging may still be in flight,
 //   5. after the barrier, the dot products, then the row's CSR entries of the
 //      slice into the same accumulators.
@@ -141,17 +144,18 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int part = wv % KSW;
-  uint4* st4 = reinterpret_cast<uint4*>(xs + static_cast<size_t>(MT) * 2 * CS) + static_cast<size_t>(wv) * BS;
-  uint32_t* st1 = reinterpret_cast<uint32_t*>(reinterpret_cast<uint4*>(xs + static_cast<size_t>(MT) * 2 * CS) +
-                                              static_cast<size_t>(kWaves) * BS) + static_cast<size_t>(wv) * BS;
+  // the slice's statistics of the workgroup's rows: [ROWS][bs][3] first-level
+  // words, then [ROWS][bs][2] second-level words
+  constexpr int ROWS = kWaves / KSW;
+  uint32_t* ls1 = reinterpret_cast<uint32_t*>(xs + static_cast<size_t>(MT) * 2 * CS);
+  uint32_t* ls2 = ls1 + static_cast<size_t>(ROWS) * BS * 3;
 
   const int n = blockIdx.x * (kWaves / KSW) + wv / KSW;
+  const int rowl = wv / KSW;                          // this row within the workgroup
   const bool nok = n < N;
   const int C = K >> 5, nb = K >> 8;
   const size_t nrow = static_cast<size_t>(min(n, N - 1));
   const uint32_t* crow = codes + nrow * C * 3;
-  const uint32_t* s1row = stats1 + nrow * nb * 3;
-  const uint2* s2row = reinterpret_cast<const uint2*>(stats2) + nrow * nb;
   const int e0 = nok ? row_ptr[n] : 0;
   const int e1 = nok ? row_ptr[n + 1] : 0;
 
@@ -176,7 +180,6 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
     const int cbase = k0 >> 5, bbase = k0 >> 8;
     const int cp = ((cs + KSW - 1) / KSW + 7) & ~7;   // chunks per part, a multiple of 8
     const int c0 = part * cp, c1 = min(cs, c0 + cp);
-    const int b0 = c0 >> 3, b1 = min(bs, (c1 + 7) >> 3);
 
     // ---- 1. first staging piece of this thread (item it = tid; clamped)
     const int items = M * cs;
@@ -188,20 +191,44 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) xv[i] = src[i];
     }
-    // ---- 2. this wave's chunks and statistics (clamped into the row)
+    // ---- 2. the slice's statistics of the workgroup's rows (contiguous per
+    //      row: one 4-byte piece per thread, 768 and 512 at most, only waves
+    //      holding pieces load, rows past N read row N - 1), issued before the
+    //      chunks so that the staging stores never wait for the chunk stream;
+    //      then this wave's chunks (clamped into the row)
+    //      (the row of piece i is floor(i / (w bs)), w = 3 or 2, taken as
+    //      (i + 1/2) times a rounded reciprocal: i < 1024 and w bs <= 384, so
+    //      the quotient stays at least 1 / 768 from an integer while the
+    //      rounding moves it by less than 1024 * 2^-22)
+    const int n0 = blockIdx.x * ROWS;
+    const int it1 = ROWS * bs * 3, it2 = ROWS * bs * 2;
+    const float inv1 = 1.0f / static_cast<float>(bs * 3), inv2 = 1.0f / static_cast<float>(bs * 2);
+    const int wfirst = 64 * wv;
+    uint32_t v1[2], v2;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (wfirst + kThreads * r < it1) {
+        const int i = min(tid + kThreads * r, it1 - 1);
+        const int row = static_cast<int>((static_cast<float>(i) + 0.5f) * inv1);
+        const int wi = i - row * (bs * 3);
+        v1[r] = stats1[static_cast<size_t>(min(n0 + row, N - 1)) * nb * 3 + bbase * 3 + wi];
+      } else {
+        v1[r] = 0u;
+      }
+    }
+    if (wfirst < it2) {
+      const int i = min(tid, it2 - 1);
+      const int row = static_cast<int>((static_cast<float>(i) + 0.5f) * inv2);
+      const int wi = i - row * (bs * 2);
+      v2 = reinterpret_cast<const uint32_t*>(stats2)[static_cast<size_t>(min(n0 + row, N - 1)) * nb * 2 + bbase * 2 + wi];
+    } else {
+      v2 = 0u;
+    }
     uint3 w[BPL];
 #pragma unroll
     for (int b = 0; b < BPL; ++b) {
       const int c = min(c0 + 64 * b + lane, cs - 1);
       w[b] = *reinterpret_cast<const uint3*>(crow + 3 * (cbase + c));
-    }
-    uint3 s1[2];
-    uint2 s2[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int blk = min(b0 + 64 * t + lane, bs - 1);
-      s1[t] = *reinterpret_cast<const uint3*>(s1row + 3 * (bbase + blk));
-      s2[t] = s2row[bbase + blk];
     }
     if (k0 == 0) {
 #pragma unroll
@@ -215,8 +242,7 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
     }
     // ---- 3. staging (the previous slice's readers are done after this barrier);
     //      the activations first: they were loaded first, so this VALU work
-    //      overlaps the weight loads still in flight, while the statistics
-    //      below were loaded last and wait for this wave's whole stream
+    //      overlaps the weight loads still in flight
     __syncthreads();
     for (int it = tid; it < items; it += kThreads) {
       const int m = it / cs, c = it - m * cs;
@@ -251,13 +277,9 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
       xs[m * 2 * CS + 2 * c + 1] = sb;
     }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int blk = b0 + 64 * t + lane;
-      if (blk < b1) {
-        st4[blk] = make_uint4(s1[t].x, s1[t].y, s1[t].z, s2[t].x);
-        st1[blk] = s2[t].y;
-      }
-    }
+    for (int r = 0; r < 2; ++r)
+      if (tid + kThreads * r < it1) ls1[tid + kThreads * r] = v1[r];
+    if (tid < it2) ls2[tid] = v2;
     // ---- 4. unpack this wave's chunks while the staging completes
     uint32_t pk[BPL][16];
 #pragma unroll
@@ -270,8 +292,10 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
       const int c = c0 + 64 * b + lane;
       if (nok && c < c1) {
         const int blk = c >> 3, j = c & 7;             // block within the slice; chunk within the block
-        const uint4 sb4 = st4[blk];
-        const uint32_t szw = st1[blk];
+        const uint32_t* r1 = ls1 + (rowl * bs + blk) * 3;
+        const uint32_t* r2 = ls2 + (rowl * bs + blk) * 2;
+        const uint4 sb4 = make_uint4(r1[0], r1[1], r1[2], r2[0]);
+        const uint32_t szw = r2[1];
         const int off = 12 * j;                         // bit offset of the chunk's two 6-bit fields
         const uint32_t lo = off < 32 ? sb4.x : (off < 64 ? sb4.y : sb4.z);
         const uint32_t hi = off < 32 ? sb4.y : sb4.z;
@@ -370,7 +394,7 @@ template <int MT, int KSW, int BPL>
 void launch_k(const SpqrArgs& a, int KS, hipStream_t stream) {
   const int CS = KS / 32, BS = KS / 256;
   const size_t lds = static_cast<size_t>(MT) * 4 * CS * 16 + static_cast<size_t>(MT) * 2 * CS * 4 +
-                     static_cast<size_t>(kWaves) * BS * 20;
+                     static_cast<size_t>(kWaves / KSW) * BS * 20;
   const int rows = kWaves / KSW;
   const int grid = (a.N + rows - 1) / rows;
   // more than 64 KB of dynamic LDS must be allowed per kernel (once per process,
@@ -394,9 +418,11 @@ void launch_k(const SpqrArgs& a, int KS, hipStream_t stream) {
 template <int MT>
 void launch_m(const SpqrArgs& a, hipStream_t stream) {
   // K slice (multiple of 256): staged activations (2.25 bytes per value and batch
-  // row) plus the waves' statistics (20 bytes per 256 values and wave) within
-  // the LDS budget, at most 32768 values (so a wave's part of a slice has at
-  // most 128 statistic blocks, two per lane, for any split below)
+  // row) plus the rows' statistics (20 bytes per 256 values and row, priced at
+  // one row per wave) within the LDS budget, at most 32768 values (with the
+  // split below a workgroup's rows then hold at most 768 first-level and 512
+  // second-level statistic words per slice: 8 rows x 32 blocks, 4 x 64 or 2 x
+  // 128, two and one pieces per thread)
   const double per_k = 2.25 * MT + 20.0 * kWaves / 256.0;
   int KS = static_cast<int>(static_cast<double>(kLdsBudget) / per_k);
   if (KS > 32768) KS = 32768;

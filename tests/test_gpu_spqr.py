@@ -51,7 +51,7 @@ def test_ragged_shapes(p):
         W = synth.student_t3_f32((N, K), 0.02, f"gpu/spqr/rag{N}")
         d = dev_pack(qlin.spqr_pack(W, p))
         st = ospqr.encode(W, p)
-        for M in (1, 2, 4, 5, 6, 7, 16):
+        for M in (1, 2, 3, 4, 5, 6, 7, 16):
             say(f"spqr N={N} K={K} p={p} M={M}")
             X = synth.x_f16(M, K, f"gpu/spqr/ragx{M}")
             ref = ospqr.forward(X, st, K)
