@@ -229,8 +229,10 @@ qlin_status spqr_workspace_bytes(int M, int K, int N, int y_dtype, size_t* bytes
 /* Y = X . (W_dense + W_sparse)^T on the GPU.  X fp16 [M][K] (device), Y [M][N]
  * (device, y_dtype QLIN_F16 or QLIN_F32).  The CSR row of output n is added into
  * the same fp32 accumulator as the dense dot product, in the same kernel pass.
- * Small batches run a fused GEMV on the exact codes (no workspace): M <= 4.
- * Larger batches up to M = 16 run a matrix-core kernel:
+ * Small batches run fused kernels on the exact codes (no workspace): M = 1 a
+ * GEMV (v_dot2 on fp16 code pairs), M = 2..6 four rows per wave on the 4x4x4
+ * matrix instruction (16 chunks x 4 tokens x 4 rows per instruction), both with
+ * the group statistics applied in fp32.  M = 7..16 run a matrix-core kernel:
  * a small prepass lays the activations out in the
  * workspace (operand order, group sums and a transposed copy, K * 68 bytes),
  * then each group's exact codes go through v_mfma_f32_16x16x16_f16 with the

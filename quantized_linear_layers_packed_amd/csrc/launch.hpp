@@ -70,6 +70,9 @@ struct SpqrArgs {
 };
 
 void spqr_gemv_launch(const SpqrArgs& a, hipStream_t stream);
+// 2 .. 8 tokens: four rows per wave on the 4 x 4 x 4 matrix instruction (no
+// workspace); the forward routes 2 .. 6 here.
+void spqr_quad_launch(const SpqrArgs& a, hipStream_t stream);
 
 // Matrix-core path for small batches: activations laid out by a prepass in the
 // workspace (Xp: MFMA operand order, Xs: group sums, XT: transposed copy).
@@ -78,17 +81,18 @@ struct SpqrPrep {
   const float* Xs;
   const uint16_t* XT;
 };
-// Batches that run the matrix-core path (the rest run the GEMV): from 5
-// tokens.  Measured per layer on the 33B-shaped layers (GEMV vs matrix-core,
-// us): 6656 x 6656 21.8 vs 22.9 at M = 4; 17920 x 6656 44.8 vs 58.8 at M = 4;
-// 6656 x 17920 59.2 at M = 5 vs 56.0 at M = 6 (the matrix-core time hardly
-// moves with M: 55.9 at M = 8, 56.0 at M = 12).  From 5 rows the GEMV stages a
-// batch of 8, which halves its K slices.
+// Routing of the SpQR forward by batch: one token runs the GEMV (spqr_gemv),
+// 2 .. 6 the four-rows-per-wave kernel on the 4 x 4 x 4 matrix instruction
+// (spqr_quad), 7 .. 16 the matrix-core path (16 tokens per 16 x 16 x 16
+// instruction, spqr_mfma).  Three 33B-shaped layers (us): M = 2: 84.8 GEMV,
+// 81.2 quad; M = 4: 107.6 GEMV, 91.9 quad; M = 6: 132.8 quad, 138.1 matrix-core;
+// M = 8: 145.6 quad, 137.9 matrix-core (whose time hardly moves with M).
 inline bool spqr_use_mfma(int M, int K, int N) {
   (void)K;
   (void)N;
-  return M >= 5;
+  return M >= 7;
 }
+inline bool spqr_use_quad(int M) { return M >= 2 && M <= 6; }
 size_t spqr_prep_bytes(int K);
 SpqrPrep spqr_prep_view(char* base, int K);
 void spqr_mfma_launch(const SpqrArgs& a, const SpqrPrep& p, hipStream_t stream);

@@ -46,7 +46,9 @@ def test_unpack_is_bit_exact():
 
 @pytest.mark.parametrize("p", [0.0, 0.01, 0.05])
 def test_ragged_shapes(p):
-    # K >= 2N runs two column tiles per wave on the matrix-core path, K < 2N one
+    # M = 1 runs the GEMV, 2..6 the four-rows-per-wave kernel (one token group
+    # up to 4, two beyond), 7 and 16 the matrix-core path (two column tiles per
+    # wave where K >= 2N, one where K < 2N)
     for (N, K) in ((37, 512), (16, 256), (50, 2560), (21, 26624), (133, 256), (600, 768), (1100, 2048)):
         W = synth.student_t3_f32((N, K), 0.02, f"gpu/spqr/rag{N}")
         d = dev_pack(qlin.spqr_pack(W, p))
@@ -70,7 +72,7 @@ def test_csr_part_alone_matches_sparse_product():
     s2[:, :, 2:] = 0.0
     st["stats2"] = s2
     d = dev_pack(st)
-    for M in (1, 4, 8, 16):
+    for M in (1, 2, 4, 6, 8, 16):
         say(f"spqr csr-only M={M}")
         X = synth.x_f16(M, K, f"gpu/spqr/csrx{M}")
         ref = ospqr.forward(X, st, K)
@@ -90,7 +92,7 @@ def test_33b_full_layer_sampled_rows(layer):
     rows = np.unique(np.r_[0, N - 1, np.random.default_rng(layer).choice(N, 254, replace=False)])
     st = ospqr.encode_rows(W, 0.01, rows)
     del W
-    for M in (1, 4, 8, 16):
+    for M in (1, 4, 6, 8, 16):
         say(f"spqr_33b layer {layer} {N}x{K} M={M}")
         X = synth.activations("spqr_33b", layer, M)
         Y = gpu_spqr(X, d, N, K, F16)
@@ -103,7 +105,7 @@ def test_matrix_core_path_leaves_the_counter_slots_zero(N, K):
     routes of the matrix-core path: K >= 2N and K < 2N), so a workspace shared
     with the W4 and int8 GEMMs still has them zero."""
     torch = torch_cuda()
-    M = 8
+    M = 12
     W = synth.student_t3_f32((N, K), 0.02, "gpu/spqr/wsctr")
     d = dev_pack(qlin.spqr_pack(W, 0.01))
     need = qlin.spqr_workspace_bytes(M, K, N, F32)
