@@ -131,12 +131,15 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
     const int cp = ((cs + KSW - 1) / KSW + 7) & ~7;   // chunks per part, a multiple of 8
     const int c0 = part * cp, c1 = min(cs, c0 + cp);
 
-    // ---- 1. first staging piece of this thread (item it = tid; clamped)
+    // ---- 1. first staging piece of this thread (item it = tid; clamped; its
+    //      token floor(it / cs) taken as (it + 1/2) times the hardware
+    //      reciprocal, exact for it < 2048 and cs <= 1024 as above)
     const int items = M * cs;
+    const float invcs = __builtin_amdgcn_rcpf(static_cast<float>(cs));
     uint4 xv[4];
     {
       const int it = min(tid, items - 1);
-      const int m = it / cs, c = it - m * cs;
+      const int m = static_cast<int>((static_cast<float>(it) + 0.5f) * invcs), c = it - m * cs;
       const uint4* src = reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K + k0) + 4 * c;
 #pragma unroll
       for (int i = 0; i < 4; ++i) xv[i] = src[i];
@@ -147,12 +150,15 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
     //      chunks so that the staging stores never wait for the chunk stream;
     //      then this wave's chunks (clamped into the row)
     //      (the row of piece i is floor(i / (w bs)), w = 3 or 2, taken as
-    //      (i + 1/2) times a rounded reciprocal: i < 1024 and w bs <= 384, so
-    //      the quotient stays at least 1 / 768 from an integer while the
-    //      rounding moves it by less than 1024 * 2^-22)
+    //      (i + 1/2) times the hardware reciprocal, which is within 1 ulp: i <
+    //      1024 and w bs <= 384 keep the quotient at least 1 / 768 from an
+    //      integer while the error moves it by less than 1024 * 2^-21; a host
+    //      check over every reachable size with the reciprocal moved by up to
+    //      2 ulp either way finds no mismatch)
     const int n0 = blockIdx.x * ROWS;
     const int it1 = ROWS * bs * 3, it2 = ROWS * bs * 2;
-    const float inv1 = 1.0f / static_cast<float>(bs * 3), inv2 = 1.0f / static_cast<float>(bs * 2);
+    const float inv1 = __builtin_amdgcn_rcpf(static_cast<float>(bs * 3));
+    const float inv2 = __builtin_amdgcn_rcpf(static_cast<float>(bs * 2));
     const int wfirst = 64 * wv;
     uint32_t v1[2], v2;
 #pragma unroll
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
     //      overlaps the weight loads still in flight
     __syncthreads();
     for (int it = tid; it < items; it += kThreads) {
-      const int m = it / cs, c = it - m * cs;
+      const int m = static_cast<int>((static_cast<float>(it) + 0.5f) * invcs), c = it - m * cs;
       uint32_t u[16];
       if (it == tid) {
 #pragma unroll

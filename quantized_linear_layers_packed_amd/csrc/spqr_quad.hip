@@ -124,10 +124,10 @@ __global__ __launch_bounds__(kThreads) void spqr_quad_kernel(
     // ---- 1. the staging pieces of this thread (items tid and tid + 512,
     //      at most 2 * 512 >= 8 * 112 and 4 * 224; the second only in waves
     //      that have one; clamped).  An item's token is floor(it / cs), taken
-    //      as (it + 1/2) times a rounded reciprocal (exact for it < 8 cs, cs <= 256)
+    //      as (it + 1/2) times the hardware reciprocal (exact for it < 2048, cs <= 1024)
     const int items = M * cs;
     const int wfirst = 64 * wv;
-    const float invcs = 1.0f / static_cast<float>(cs);
+    const float invcs = __builtin_amdgcn_rcpf(static_cast<float>(cs));
     uint4 xv[2][4];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -145,10 +145,12 @@ __global__ __launch_bounds__(kThreads) void spqr_quad_kernel(
     // ---- 2. statistics of the workgroup's rows in the slice (a row's blocks
     //      are contiguous: one 4-byte piece per thread, only waves holding
     //      pieces load, rows past N read row N - 1; piece i's row is
-    //      floor(i / (w bs)), w = 3 or 2, taken as (i + 1/2) times a rounded
-    //      reciprocal, exact for i < 1024 and w bs <= 384), then the codes
+    //      floor(i / (w bs)), w = 3 or 2, taken as (i + 1/2) times the hardware
+    //      reciprocal (within 1 ulp), exact for i < 1024 and w bs <= 384), then
+    //      the codes
     const int it1 = kRows * bs * 3, it2 = kRows * bs * 2;
-    const float inv1 = 1.0f / static_cast<float>(bs * 3), inv2 = 1.0f / static_cast<float>(bs * 2);
+    const float inv1 = __builtin_amdgcn_rcpf(static_cast<float>(bs * 3));
+    const float inv2 = __builtin_amdgcn_rcpf(static_cast<float>(bs * 2));
     uint32_t v1[2], v2;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
