@@ -97,8 +97,8 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
   // the slice's statistics of the workgroup's rows: [ROWS][bs][3] first-level
   // words, then [ROWS][bs][2] second-level words
   constexpr int ROWS = kWaves / KSW;
-  uint32_t* ls1 = reinterpret_cast<uint32_t*>(xs + static_cast<size_t>(MT) * 2 * CS);
-  uint32_t* ls2 = ls1 + static_cast<size_t>(ROWS) * BS * 3;
+  float4* ls2f = reinterpret_cast<float4*>(xs + static_cast<size_t>(MT) * 2 * CS);   // [ROWS][bs] combined second level
+  uint32_t* ls1 = reinterpret_cast<uint32_t*>(ls2f + static_cast<size_t>(ROWS) * BS);  // [ROWS][bs][3] first-level words
 
   const int n = blockIdx.x * (kWaves / KSW) + wv / KSW;
   const int rowl = wv / KSW;                          // this row within the workgroup
@@ -235,7 +235,16 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
 #pragma unroll
     for (int r = 0; r < 2; ++r)
       if (tid + kThreads * r < it1) ls1[tid + kThreads * r] = v1[r];
-    if (tid < it2) ls2[tid] = v2;
+    // second-level pairs go to LDS already combined into what a chunk's decode
+    // needs, per (row, block): scale pair (SS, ZS) -> SS, -SS ZS and zero pair
+    // -> -SS, SS ZS - 128, so that s_hat = SS c + (-SS ZS) and -(128 + z_hat)
+    // = (-SS) c + (SS ZS - 128) are one fma each (piece i -> floats 2i, 2i + 1)
+    if (tid < it2) {
+      const float S2 = f16_bits_to_f32(static_cast<uint16_t>(v2));
+      const float Z2 = f16_bits_to_f32(static_cast<uint16_t>(v2 >> 16));
+      reinterpret_cast<float2*>(ls2f)[tid] =
+          (tid & 1) ? make_float2(-S2, fmaf(S2, Z2, -128.0f)) : make_float2(S2, -(S2 * Z2));
+    }
     // ---- 4. unpack this wave's chunks while the staging completes
     uint32_t pk[BPL][16];
 #pragma unroll
@@ -249,21 +258,16 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
       if (nok && c < c1) {
         const int blk = c >> 3, j = c & 7;             // block within the slice; chunk within the block
         const uint32_t* r1 = ls1 + (rowl * bs + blk) * 3;
-        const uint32_t* r2 = ls2 + (rowl * bs + blk) * 2;
-        const uint4 sb4 = make_uint4(r1[0], r1[1], r1[2], r2[0]);
-        const uint32_t szw = r2[1];
+        const float4 d = ls2f[rowl * bs + blk];
         const int off = 12 * j;                         // bit offset of the chunk's two 6-bit fields
-        const uint32_t lo = off < 32 ? sb4.x : (off < 64 ? sb4.y : sb4.z);
-        const uint32_t hi = off < 32 ? sb4.y : sb4.z;
+        const uint32_t lo = off < 32 ? r1[0] : (off < 64 ? r1[1] : r1[2]);
+        const uint32_t hi = off < 32 ? r1[1] : r1[2];
         const uint32_t f = static_cast<uint32_t>(((static_cast<uint64_t>(hi) << 32) | lo) >> (off & 31)) & 0xFFFu;
-        const float SSs = f16_bits_to_f32(static_cast<uint16_t>(sb4.w));
-        const float ZSs = f16_bits_to_f32(static_cast<uint16_t>(sb4.w >> 16));
-        const float SSz = f16_bits_to_f32(static_cast<uint16_t>(szw));
-        const float ZSz = f16_bits_to_f32(static_cast<uint16_t>(szw >> 16));
-        const float sA = SSs * (static_cast<float>(f & 7u) - ZSs);
-        const float zA = SSz * (static_cast<float>((f >> 3) & 7u) - ZSz);
-        const float sB = SSs * (static_cast<float>((f >> 6) & 7u) - ZSs);
-        const float zB = SSz * (static_cast<float>((f >> 9) & 7u) - ZSz);
+        // s_hat and -(128 + z_hat) of the chunk's two groups
+        const float sA = fmaf(d.x, static_cast<float>(f & 7u), d.y);
+        const float cA = fmaf(d.z, static_cast<float>((f >> 3) & 7u), d.w);
+        const float sB = fmaf(d.x, static_cast<float>((f >> 6) & 7u), d.y);
+        const float cB = fmaf(d.z, static_cast<float>((f >> 9) & 7u), d.w);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m < M) {
@@ -285,8 +289,8 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
             }
             // sum x (c - z_hat) = acc / 8 - (128 + z_hat) * sum(x)
             const float2 xab = reinterpret_cast<const float2*>(xs)[static_cast<size_t>(m) * CS + c];
-            const float tA = fmaf(aA, 0.125f, -(128.0f + zA) * xab.x);
-            const float tB = fmaf(aB, 0.125f, -(128.0f + zB) * xab.y);
+            const float tA = fmaf(aA, 0.125f, cA * xab.x);
+            const float tB = fmaf(aB, 0.125f, cB * xab.y);
             res[m] = fmaf(sA, tA, res[m]);
             res[m] = fmaf(sB, tB, res[m]);
           }
@@ -350,7 +354,7 @@ template <int MT, int KSW, int BPL>
 void launch_k(const SpqrArgs& a, int KS, hipStream_t stream) {
   const int CS = KS / 32, BS = KS / 256;
   const size_t lds = static_cast<size_t>(MT) * 4 * CS * 16 + static_cast<size_t>(MT) * 2 * CS * 4 +
-                     static_cast<size_t>(kWaves / KSW) * BS * 20;
+                     static_cast<size_t>(kWaves / KSW) * BS * 28;
   const int rows = kWaves / KSW;
   const int grid = (a.N + rows - 1) / rows;
   // more than 64 KB of dynamic LDS must be allowed per kernel (once per process,
@@ -374,12 +378,12 @@ void launch_k(const SpqrArgs& a, int KS, hipStream_t stream) {
 template <int MT>
 void launch_m(const SpqrArgs& a, hipStream_t stream) {
   // K slice (multiple of 256): staged activations (2.25 bytes per value and batch
-  // row) plus the rows' statistics (20 bytes per 256 values and row, priced at
+  // row) plus the rows' statistics (28 bytes per 256 values and row, priced at
   // one row per wave) within the LDS budget, at most 32768 values (with the
   // split below a workgroup's rows then hold at most 768 first-level and 512
   // second-level statistic words per slice: 8 rows x 32 blocks, 4 x 64 or 2 x
   // 128, two and one pieces per thread)
-  const double per_k = 2.25 * MT + 20.0 * kWaves / 256.0;
+  const double per_k = 2.25 * MT + 28.0 * kWaves / 256.0;
   int KS = static_cast<int>(static_cast<double>(kLdsBudget) / per_k);
   if (KS > 32768) KS = 32768;
   KS = KS / 256 * 256;

@@ -82,8 +82,8 @@ __global__ __launch_bounds__(kThreads) void spqr_quad_kernel(
   const int T = 4 * CS + (CS >> 2) + 1;
   uint4* xl = smem;                                                                    // [MT][T] pair quads
   float2* xs = reinterpret_cast<float2*>(smem + static_cast<size_t>(MT) * T);          // [CS][MT] group sums
-  uint32_t* ls1 = reinterpret_cast<uint32_t*>(xs + static_cast<size_t>(CS) * MT);      // [rows][bs][3]
-  uint32_t* ls2 = ls1 + static_cast<size_t>(kRows) * BS * 3;                            // [rows][bs][2]
+  float4* ls2f = reinterpret_cast<float4*>(xs + static_cast<size_t>(CS) * MT);          // [rows][bs] combined second level
+  uint32_t* ls1 = reinterpret_cast<uint32_t*>(ls2f + static_cast<size_t>(kRows) * BS);  // [rows][bs][3] first-level words
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int part = wv % kKsw;
@@ -217,7 +217,16 @@ __global__ __launch_bounds__(kThreads) void spqr_quad_kernel(
 #pragma unroll
     for (int r = 0; r < 2; ++r)
       if (tid + kThreads * r < it1) ls1[tid + kThreads * r] = v1[r];
-    if (tid < it2) ls2[tid] = v2;
+    // second-level pairs go to LDS already combined into what a chunk's decode
+    // needs, per (row, block): scale pair (SS, ZS) -> SS, -SS ZS and zero pair
+    // -> -SS, SS ZS - 128, so that s_hat = SS c + (-SS ZS) and -(128 + z_hat)
+    // = (-SS) c + (SS ZS - 128) are one fma each (piece i -> floats 2i, 2i + 1)
+    if (tid < it2) {
+      const float S2 = f16_bits_to_f32(static_cast<uint16_t>(v2));
+      const float Z2 = f16_bits_to_f32(static_cast<uint16_t>(v2 >> 16));
+      reinterpret_cast<float2*>(ls2f)[tid] =
+          (tid & 1) ? make_float2(-S2, fmaf(S2, Z2, -128.0f)) : make_float2(S2, -(S2 * Z2));
+    }
     __syncthreads();
 
     // ---- 4. dense 3-bit part: 16 chunks of 4 rows per step
@@ -230,23 +239,19 @@ __global__ __launch_bounds__(kThreads) void spqr_quad_kernel(
         unpack_chunk(w[s].x, w[s].y, w[s].z, pk);
         const int blk = cc >> 3, jj = cc & 7;          // block within the slice; chunk within the block
         const uint32_t* r1 = ls1 + (rowl * bs + blk) * 3;
-        const uint32_t* r2 = ls2 + (rowl * bs + blk) * 2;
-        const uint32_t sw0 = r1[0], sw1 = r1[1], sw2 = r1[2], ssw = r2[0], szw = r2[1];
+        const float4 d = ls2f[rowl * bs + blk];
+        const uint32_t sw0 = r1[0], sw1 = r1[1], sw2 = r1[2];
         const int off = 12 * jj;                       // bit offset of the chunk's two 6-bit fields
         const uint32_t lo = off < 32 ? sw0 : (off < 64 ? sw1 : sw2);
         const uint32_t hi = off < 32 ? sw1 : sw2;
         const uint32_t f = static_cast<uint32_t>(((static_cast<uint64_t>(hi) << 32) | lo) >> (off & 31)) & 0xFFFu;
-        const float SSs = f16_bits_to_f32(static_cast<uint16_t>(ssw));
-        const float ZSs = f16_bits_to_f32(static_cast<uint16_t>(ssw >> 16));
-        const float SSz = f16_bits_to_f32(static_cast<uint16_t>(szw));
-        const float ZSz = f16_bits_to_f32(static_cast<uint16_t>(szw >> 16));
-        // slots past the wave's run hold clamped codes: their scale is zeroed
+        // s_hat and -(128 + z_hat) of the chunk's two groups; slots past the
+        // wave's run hold clamped codes: their scale is zeroed
         const bool act = c < c1;
-        const float sA = act ? SSs * (static_cast<float>(f & 7u) - ZSs) : 0.0f;
-        const float zA = SSz * (static_cast<float>((f >> 3) & 7u) - ZSz);
-        const float sB = act ? SSs * (static_cast<float>((f >> 6) & 7u) - ZSs) : 0.0f;
-        const float zB = SSz * (static_cast<float>((f >> 9) & 7u) - ZSz);
-        const float cA = -(128.0f + zA), cB = -(128.0f + zB);
+        const float sA = act ? fmaf(d.x, static_cast<float>(f & 7u), d.y) : 0.0f;
+        const float cA = fmaf(d.z, static_cast<float>((f >> 3) & 7u), d.w);
+        const float sB = act ? fmaf(d.x, static_cast<float>((f >> 6) & 7u), d.y) : 0.0f;
+        const float cB = fmaf(d.z, static_cast<float>((f >> 9) & 7u), d.w);
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
           const uint4* xa = xl + static_cast<size_t>(tok[g]) * T + 4 * cc + (cc >> 2);
@@ -328,7 +333,7 @@ template <int MT, int S>
 void launch_k(const SpqrArgs& a, int KS, hipStream_t stream) {
   const int CS = KS / 32, BS = KS / 256;
   const size_t lds = static_cast<size_t>(MT) * (4 * CS + CS / 4 + 1) * 16 + static_cast<size_t>(CS) * MT * 8 +
-                     static_cast<size_t>(kRows) * BS * 20;
+                     static_cast<size_t>(kRows) * BS * 28;
   const int grid = (a.N + kRows - 1) / kRows;
   // more than 64 KB of dynamic LDS must be allowed per kernel (once per process,
   // thread-safe initialisation of function-local statics)
@@ -351,11 +356,12 @@ void launch_k(const SpqrArgs& a, int KS, hipStream_t stream) {
 template <int MT>
 void launch_m(const SpqrArgs& a, hipStream_t stream) {
   // K slice (multiple of 256): staged activations (2.375 bytes per value and
-  // token with the bank skew, plus 16 per token) and the rows' statistics (20
-  // bytes per 256 values and row) within the LDS budget, at most 8192 values (so the workgroup's 8 rows hold at most
-  // 768 first-level and 512 second-level statistic words per slice, two and
-  // one per thread), in slices of equal size
-  const double per_k = 2.375 * MT + 20.0 * kRows / 256.0;
+  // token with the bank skew, plus 16 per token) and the rows' statistics (28
+  // bytes per 256 values and row) within the LDS budget, at most 8192 values
+  // (so the workgroup's 8 rows hold at most 768 first-level and 512
+  // second-level statistic words per slice, two and one per thread), in slices
+  // of equal size
+  const double per_k = 2.375 * MT + 28.0 * kRows / 256.0;
   int KS = static_cast<int>(static_cast<double>(kLdsBudget - 16 * MT) / per_k);
   if (KS > 8192) KS = 8192;
   KS = KS / 256 * 256;
