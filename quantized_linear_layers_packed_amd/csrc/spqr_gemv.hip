@@ -196,10 +196,11 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
         }
       }
     }
-    // ---- 3. staging (the previous slice's readers are done after this barrier);
-    //      the activations first: they were loaded first, so this VALU work
-    //      overlaps the weight loads still in flight
-    __syncthreads();
+    // ---- 3. staging (after a barrier from the second slice on: the previous
+    //      slice's readers must be done); the activations first: they were
+    //      loaded first, so this VALU work overlaps the weight loads still in
+    //      flight
+    if (k0 > 0) __syncthreads();
     for (int it = tid; it < items; it += kThreads) {
       const int m = static_cast<int>((static_cast<float>(it) + 0.5f) * invcs), c = it - m * cs;
       uint32_t u[16];

@@ -187,8 +187,9 @@ __global__ __launch_bounds__(kThreads) void spqr_quad_kernel(
         }
       }
     }
-    // ---- 3. staging (the previous slice's readers are done after this barrier)
-    __syncthreads();
+    // ---- 3. staging (after a barrier from the second slice on: the previous
+    //      slice's readers must be done)
+    if (k0 > 0) __syncthreads();
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int it = tid + kThreads * r;
@@ -306,11 +307,14 @@ __global__ __launch_bounds__(kThreads) void spqr_quad_kernel(
 
   // ---- sum over the 16 lanes of row j (lanes j, j + 4, ..., j + 60), then over
   //      the row's waves in a fixed order through LDS
+  //      (rotations by 8 and 4 within each row of 16 lanes leave every lane
+  //      with the sum of its row's lanes of the same j; two cross-row
+  //      exchanges finish)
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     float v = res[m];
-    v += __shfl_xor(v, 4, 64);
-    v += __shfl_xor(v, 8, 64);
+    v += bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(v), 0x128, 0xF, 0xF, false));   // row_ror:8
+    v += bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(v), 0x124, 0xF, 0xF, false));   // row_ror:4
     v += __shfl_xor(v, 16, 64);
     v += __shfl_xor(v, 32, 64);
     if (b == 0) red[wv][m][j] = v;
