@@ -55,24 +55,32 @@ __device__ __forceinline__ f32x4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, 
 
 // Per K slice, in this order:
 //   1. the activation loads of the LDS staging (one 32-value piece per thread),
-//   2. the slice's statistics of the workgroup's rows (4-byte pieces, at most
-//      two and one per thread), the wave's code chunks for all its steps and,
-//      on the first slice, up to 4 CSR entries per lane,
+//   2. the slice's statistics of the workgroup's rows (4-byte pieces, up to
+//      three and two per thread), the wave's code chunks of the first row
+//      group for all its steps and, on the first slice, the first CSR entries
+//      of each row,
 //   3. the staging (pairs in the unpack order, the per-chunk group sums) and
 //      the statistics into LDS,
-//   4. after the barrier, per step: unpack, statistics decode, the matrix
-//      instructions, the rescale; then the row's CSR entries of the slice.
-template <int MT, int S, int OUTK>
-__global__ __launch_bounds__(kThreads) void spqr_quad_kernel(
+//   4. after the barrier, per row group: per step unpack, statistics decode,
+//      the matrix instructions and the rescale; then the next group's codes
+//      are issued into the same registers, and the group's CSR entries are
+//      added while they arrive.
+// A workgroup serves R groups of 8 rows: one activation staging and one pass
+// of barriers for all of them.
+template <int MT, int S, int R, int OUTK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void spqr_quad_kernel(
     const uint16_t* X, int M, int K, int KS,
     const uint32_t* codes, const uint32_t* stats1,
     const uint16_t* stats2, const int32_t* row_ptr,
     const int32_t* col_idx, const uint16_t* vals,
     int N, void* Y) {
-  constexpr int kCsr = 4;                             // CSR entries per lane held in registers
+  constexpr int kCsr = R == 1 ? 4 : 1;                // CSR entries per lane and row held in registers
   constexpr int NG = MT / 4;                          // token groups of 4
+  constexpr int ROWS = R * kRows;                     // rows of the workgroup
+  constexpr int NR1 = (ROWS * 32 * 3 + kThreads - 1) / kThreads;   // statistic piece rounds (bs <= 32)
+  constexpr int NR2 = (ROWS * 32 * 2 + kThreads - 1) / kThreads;
   extern __shared__ uint4 smem[];
-  __shared__ float red[kWaves][MT][4];
+  __shared__ float red[kWaves][R][MT][4];
   const int CS = KS >> 5;                             // chunks per slice
   const int BS = KS >> 8;                             // statistic blocks per slice
   // staged pair quads: chunk c of token m at 16-byte unit m T + 4 c + c / 4 (its
@@ -83,36 +91,41 @@ __global__ __launch_bounds__(kThreads) void spqr_quad_kernel(
   uint4* xl = smem;                                                                    // [MT][T] pair quads
   float2* xs = reinterpret_cast<float2*>(smem + static_cast<size_t>(MT) * T);          // [CS][MT] group sums
   float4* ls2f = reinterpret_cast<float4*>(xs + static_cast<size_t>(CS) * MT);          // [rows][bs] combined second level
-  uint32_t* ls1 = reinterpret_cast<uint32_t*>(ls2f + static_cast<size_t>(kRows) * BS);  // [rows][bs][3] first-level words
+  uint32_t* ls1 = reinterpret_cast<uint32_t*>(ls2f + static_cast<size_t>(ROWS) * BS);   // [rows][bs][3] first-level words
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int part = wv % kKsw;
   const int b = lane >> 2, j = lane & 3;              // chunk slot of the step; row of the quad and token of the group
-  const int rowl = 4 * (wv / kKsw) + j;               // row within the workgroup
-  const int n0 = blockIdx.x * kRows;
-  const int n = n0 + rowl;
-  const bool nok = n < N;
+  const int n0 = blockIdx.x * ROWS;
   const int C = K >> 5, nb = K >> 8;
-  const uint32_t* crow = codes + static_cast<size_t>(min(n, N - 1)) * C * 3;
-  const int e0 = nok ? row_ptr[n] : 0;
-  const int e1 = nok ? row_ptr[n + 1] : 0;
+  int rowl[R], n[R], e0[R], e1[R];                    // row of group r within the workgroup, its index, its CSR range
+  bool nok[R];
+  const uint32_t* crow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    rowl[r] = r * kRows + 4 * (wv / kKsw) + j;
+    n[r] = n0 + rowl[r];
+    nok[r] = n[r] < N;
+    crow[r] = codes + static_cast<size_t>(min(n[r], N - 1)) * C * 3;
+    e0[r] = nok[r] ? row_ptr[n[r]] : 0;
+    e1[r] = nok[r] ? row_ptr[n[r] + 1] : 0;
+  }
   int tok[NG];                                        // this lane's A-operand token per group (rows past M re-read M - 1)
 #pragma unroll
   for (int g = 0; g < NG; ++g) tok[g] = min(4 * g + j, M - 1);
 
-  // CSR entries of row j held by this lane: e0 + 16 (KSW i + part) + b, loaded
-  // on the first slice behind the dense stream, kept as raw fp16 bits
-  int ccol[kCsr];
-  uint32_t cbits[kCsr];
-#pragma unroll
-  for (int i = 0; i < kCsr; ++i) {
-    ccol[i] = -1;
-    cbits[i] = 0u;
-  }
+  // CSR entries of each row held by this lane: e0 + 16 (KSW i + part) + b,
+  // loaded on the first slice behind the dense stream, kept as raw bits; bit
+  // r kCsr + i of cvalid flags a loaded entry
+  int ccol[R][kCsr];
+  uint32_t cbits[R][kCsr];
+  uint32_t cvalid = 0u;
 
-  float res[MT];
+  float res[R][MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) res[m] = 0.0f;
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) res[r][m] = 0.0f;
 
   for (int k0 = 0; k0 < K; k0 += KS) {
     const int ks = min(KS, K - k0);
@@ -143,49 +156,55 @@ __global__ __launch_bounds__(kThreads) void spqr_quad_kernel(
       }
     }
     // ---- 2. statistics of the workgroup's rows in the slice (a row's blocks
-    //      are contiguous: one 4-byte piece per thread, only waves holding
-    //      pieces load, rows past N read row N - 1; piece i's row is
-    //      floor(i / (w bs)), w = 3 or 2, taken as (i + 1/2) times the hardware
-    //      reciprocal (within 1 ulp), exact for i < 1024 and w bs <= 384), then
-    //      the codes
-    const int it1 = kRows * bs * 3, it2 = kRows * bs * 2;
+    //      are contiguous: 4-byte pieces, only waves holding pieces load, rows
+    //      past N read row N - 1; piece i's row is floor(i / (w bs)), w = 3 or
+    //      2, taken as (i + 1/2) times the hardware reciprocal (within 1 ulp),
+    //      exact for i < 2048 and w bs <= 96), then the codes
+    const int it1 = ROWS * bs * 3, it2 = ROWS * bs * 2;
     const float inv1 = __builtin_amdgcn_rcpf(static_cast<float>(bs * 3));
     const float inv2 = __builtin_amdgcn_rcpf(static_cast<float>(bs * 2));
-    uint32_t v1[2], v2;
+    uint32_t v1[NR1], v2[NR2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      if (wfirst + kThreads * r < it1) {
-        const int i = min(tid + kThreads * r, it1 - 1);
+    for (int q = 0; q < NR1; ++q) {
+      if (wfirst + kThreads * q < it1) {
+        const int i = min(tid + kThreads * q, it1 - 1);
         const int row = static_cast<int>((static_cast<float>(i) + 0.5f) * inv1);
         const int wi = i - row * (bs * 3);
-        v1[r] = stats1[static_cast<size_t>(min(n0 + row, N - 1)) * nb * 3 + bbase * 3 + wi];
+        v1[q] = stats1[static_cast<size_t>(min(n0 + row, N - 1)) * nb * 3 + bbase * 3 + wi];
       } else {
-        v1[r] = 0u;
+        v1[q] = 0u;
       }
     }
-    if (wfirst < it2) {
-      const int i = min(tid, it2 - 1);
-      const int row = static_cast<int>((static_cast<float>(i) + 0.5f) * inv2);
-      const int wi = i - row * (bs * 2);
-      v2 = reinterpret_cast<const uint32_t*>(stats2)[static_cast<size_t>(min(n0 + row, N - 1)) * nb * 2 + bbase * 2 + wi];
-    } else {
-      v2 = 0u;
+#pragma unroll
+    for (int q = 0; q < NR2; ++q) {
+      if (wfirst + kThreads * q < it2) {
+        const int i = min(tid + kThreads * q, it2 - 1);
+        const int row = static_cast<int>((static_cast<float>(i) + 0.5f) * inv2);
+        const int wi = i - row * (bs * 2);
+        v2[q] = reinterpret_cast<const uint32_t*>(stats2)[static_cast<size_t>(min(n0 + row, N - 1)) * nb * 2 +
+                                                           bbase * 2 + wi];
+      } else {
+        v2[q] = 0u;
+      }
     }
     uint3 w[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int c = min(c0 + 16 * s + b, cs - 1);
-      w[s] = *reinterpret_cast<const uint3*>(crow + 3 * (cbase + c));
+      w[s] = *reinterpret_cast<const uint3*>(crow[0] + 3 * (cbase + c));
     }
     if (k0 == 0) {
 #pragma unroll
-      for (int i = 0; i < kCsr; ++i) {
-        const int e = e0 + 16 * (kKsw * i + part) + b;
-        if (e < e1) {
-          ccol[i] = col_idx[e];
-          cbits[i] = vals[e];
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < kCsr; ++i) {
+          const int e = e0[r] + 16 * (kKsw * i + part) + b;
+          if (e < e1[r]) {
+            ccol[r][i] = col_idx[e];
+            cbits[r][i] = vals[e];
+            cvalid |= 1u << (r * kCsr + i);
+          }
         }
-      }
     }
     // ---- 3. staging (after a barrier from the second slice on: the previous
     //      slice's readers must be done)
@@ -216,171 +235,214 @@ __global__ __launch_bounds__(kThreads) void spqr_quad_kernel(
       xs[static_cast<size_t>(c) * MT + m] = make_float2(sa, sb);
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-      if (tid + kThreads * r < it1) ls1[tid + kThreads * r] = v1[r];
+    for (int q = 0; q < NR1; ++q)
+      if (tid + kThreads * q < it1) ls1[tid + kThreads * q] = v1[q];
     // second-level pairs go to LDS already combined into what a chunk's decode
     // needs, per (row, block): scale pair (SS, ZS) -> SS, -SS ZS and zero pair
     // -> -SS, SS ZS - 128, so that s_hat = SS c + (-SS ZS) and -(128 + z_hat)
     // = (-SS) c + (SS ZS - 128) are one fma each (piece i -> floats 2i, 2i + 1)
-    if (tid < it2) {
-      const float S2 = f16_bits_to_f32(static_cast<uint16_t>(v2));
-      const float Z2 = f16_bits_to_f32(static_cast<uint16_t>(v2 >> 16));
-      reinterpret_cast<float2*>(ls2f)[tid] =
-          (tid & 1) ? make_float2(-S2, fmaf(S2, Z2, -128.0f)) : make_float2(S2, -(S2 * Z2));
+#pragma unroll
+    for (int q = 0; q < NR2; ++q) {
+      const int i = tid + kThreads * q;
+      if (i < it2) {
+        const float S2 = f16_bits_to_f32(static_cast<uint16_t>(v2[q]));
+        const float Z2 = f16_bits_to_f32(static_cast<uint16_t>(v2[q] >> 16));
+        reinterpret_cast<float2*>(ls2f)[i] =
+            (i & 1) ? make_float2(-S2, fmaf(S2, Z2, -128.0f)) : make_float2(S2, -(S2 * Z2));
+      }
     }
     __syncthreads();
 
-    // ---- 4. dense 3-bit part: 16 chunks of 4 rows per step
+    // ---- 4. per row group: the dense 3-bit part (16 chunks of 4 rows per
+    //      step), the next group's codes, the group's CSR outliers
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (c0 + 16 * s < c1) {                          // wave-uniform: the matrix instructions run with every lane
-        const int c = c0 + 16 * s + b;
-        const int cc = min(c, cs - 1);
-        uint32_t pk[16];
-        unpack_chunk(w[s].x, w[s].y, w[s].z, pk);
-        const int blk = cc >> 3, jj = cc & 7;          // block within the slice; chunk within the block
-        const uint32_t* r1 = ls1 + (rowl * bs + blk) * 3;
-        const float4 d = ls2f[rowl * bs + blk];
-        const uint32_t sw0 = r1[0], sw1 = r1[1], sw2 = r1[2];
-        const int off = 12 * jj;                       // bit offset of the chunk's two 6-bit fields
-        const uint32_t lo = off < 32 ? sw0 : (off < 64 ? sw1 : sw2);
-        const uint32_t hi = off < 32 ? sw1 : sw2;
-        const uint32_t f = static_cast<uint32_t>(((static_cast<uint64_t>(hi) << 32) | lo) >> (off & 31)) & 0xFFFu;
-        // s_hat and -(128 + z_hat) of the chunk's two groups; slots past the
-        // wave's run hold clamped codes: their scale is zeroed
-        const bool act = c < c1;
-        const float sA = act ? fmaf(d.x, static_cast<float>(f & 7u), d.y) : 0.0f;
-        const float cA = fmaf(d.z, static_cast<float>((f >> 3) & 7u), d.w);
-        const float sB = act ? fmaf(d.x, static_cast<float>((f >> 6) & 7u), d.y) : 0.0f;
-        const float cB = fmaf(d.z, static_cast<float>((f >> 9) & 7u), d.w);
+    for (int r = 0; r < R; ++r) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          const uint4* xa = xl + static_cast<size_t>(tok[g]) * T + 4 * cc + (cc >> 2);
-          const uint4 a0 = xa[0], a1 = xa[1], a2 = xa[2], a3 = xa[3];
-          const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-          f32x4_t dA = mfma4(a0.x, a0.y, pk[0], pk[1], zero);
-          f32x4_t dB = mfma4(a2.x, a2.y, pk[8], pk[9], zero);
-          dA = mfma4(a0.z, a0.w, pk[2], pk[3], dA);
-          dB = mfma4(a2.z, a2.w, pk[10], pk[11], dB);
-          dA = mfma4(a1.x, a1.y, pk[4], pk[5], dA);
-          dB = mfma4(a3.x, a3.y, pk[12], pk[13], dB);
-          dA = mfma4(a1.z, a1.w, pk[6], pk[7], dA);
-          dB = mfma4(a3.z, a3.w, pk[14], pk[15], dB);
-          // the group sums of tokens 4 g .. 4 g + 3 at this chunk: (A, B) per token
-          const float4* xq = reinterpret_cast<const float4*>(xs + static_cast<size_t>(cc) * MT + 4 * g);
-          const float4 s01 = xq[0], s23 = xq[1];
-          const float xA[4] = {s01.x, s01.z, s23.x, s23.z};
-          const float xB[4] = {s01.y, s01.w, s23.y, s23.w};
+      for (int s = 0; s < S; ++s) {
+        if (c0 + 16 * s < c1) {                        // wave-uniform: the matrix instructions run with every lane
+          const int c = c0 + 16 * s + b;
+          const int cc = min(c, cs - 1);
+          uint32_t pk[16];
+          unpack_chunk(w[s].x, w[s].y, w[s].z, pk);
+          const int blk = cc >> 3, jj = cc & 7;        // block within the slice; chunk within the block
+          const uint32_t* r1 = ls1 + (rowl[r] * bs + blk) * 3;
+          const float4 d = ls2f[rowl[r] * bs + blk];
+          const uint32_t sw0 = r1[0], sw1 = r1[1], sw2 = r1[2];
+          const int off = 12 * jj;                     // bit offset of the chunk's two 6-bit fields
+          const uint32_t lo = off < 32 ? sw0 : (off < 64 ? sw1 : sw2);
+          const uint32_t hi = off < 32 ? sw1 : sw2;
+          const uint32_t f = static_cast<uint32_t>(((static_cast<uint64_t>(hi) << 32) | lo) >> (off & 31)) & 0xFFFu;
+          // s_hat and -(128 + z_hat) of the chunk's two groups; slots past the
+          // wave's run hold clamped codes: their scale is zeroed
+          const bool act = c < c1;
+          const float sA = act ? fmaf(d.x, static_cast<float>(f & 7u), d.y) : 0.0f;
+          const float cA = fmaf(d.z, static_cast<float>((f >> 3) & 7u), d.w);
+          const float sB = act ? fmaf(d.x, static_cast<float>((f >> 6) & 7u), d.y) : 0.0f;
+          const float cB = fmaf(d.z, static_cast<float>((f >> 9) & 7u), d.w);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            // sum x (c - z_hat) = acc / 8 - (128 + z_hat) * sum(x)
-            res[4 * g + r] = fmaf(sA, fmaf(dA[r], 0.125f, cA * xA[r]), res[4 * g + r]);
-            res[4 * g + r] = fmaf(sB, fmaf(dB[r], 0.125f, cB * xB[r]), res[4 * g + r]);
+          for (int g = 0; g < NG; ++g) {
+            const uint4* xa = xl + static_cast<size_t>(tok[g]) * T + 4 * cc + (cc >> 2);
+            const uint4 a0 = xa[0], a1 = xa[1], a2 = xa[2], a3 = xa[3];
+            const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4_t dA = mfma4(a0.x, a0.y, pk[0], pk[1], zero);
+            f32x4_t dB = mfma4(a2.x, a2.y, pk[8], pk[9], zero);
+            dA = mfma4(a0.z, a0.w, pk[2], pk[3], dA);
+            dB = mfma4(a2.z, a2.w, pk[10], pk[11], dB);
+            dA = mfma4(a1.x, a1.y, pk[4], pk[5], dA);
+            dB = mfma4(a3.x, a3.y, pk[12], pk[13], dB);
+            dA = mfma4(a1.z, a1.w, pk[6], pk[7], dA);
+            dB = mfma4(a3.z, a3.w, pk[14], pk[15], dB);
+            // the group sums of tokens 4 g .. 4 g + 3 at this chunk: (A, B) per token
+            const float4* xq = reinterpret_cast<const float4*>(xs + static_cast<size_t>(cc) * MT + 4 * g);
+            const float4 s01 = xq[0], s23 = xq[1];
+            const float xA[4] = {s01.x, s01.z, s23.x, s23.z};
+            const float xB[4] = {s01.y, s01.w, s23.y, s23.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              // sum x (c - z_hat) = acc / 8 - (128 + z_hat) * sum(x)
+              res[r][4 * g + t] = fmaf(sA, fmaf(dA[t], 0.125f, cA * xA[t]), res[r][4 * g + t]);
+              res[r][4 * g + t] = fmaf(sB, fmaf(dB[t], 0.125f, cB * xB[t]), res[r][4 * g + t]);
+            }
           }
         }
       }
-    }
-
-    // ---- CSR outliers of row j whose column falls in the slice
-    auto outlier = [&](int colg, float v) {
-      const int col = colg - k0;
-      if (col < 0 || col >= ks) return;
-      const int c = col >> 5, slot = pair_slot(col & 31);
-      const int q = slot >> 3, wi = (slot >> 1) & 3, hh = slot & 1;
+      if (r + 1 < R) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < M) {
-          const uint32_t* quad = reinterpret_cast<const uint32_t*>(xl + static_cast<size_t>(m) * T + 4 * c + (c >> 2) + q);
-          const uint16_t xh = static_cast<uint16_t>(quad[wi] >> (16 * hh));
-          res[m] = fmaf(f16_bits_to_f32(xh), v, res[m]);
+        for (int s = 0; s < S; ++s) {
+          const int c = min(c0 + 16 * s + b, cs - 1);
+          w[s] = *reinterpret_cast<const uint3*>(crow[r + 1] + 3 * (cbase + c));
         }
       }
-    };
-    if (nok) {
+      // CSR outliers of the lane's row of this group whose column falls in the slice
+      auto outlier = [&](int colg, float v) {
+        const int col = colg - k0;
+        if (col < 0 || col >= ks) return;
+        const int c = col >> 5, slot = pair_slot(col & 31);
+        const int q = slot >> 3, wi = (slot >> 1) & 3, hh = slot & 1;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m < M) {
+            const uint32_t* quad = reinterpret_cast<const uint32_t*>(xl + static_cast<size_t>(m) * T + 4 * c + (c >> 2) + q);
+            const uint16_t xh = static_cast<uint16_t>(quad[wi] >> (16 * hh));
+            res[r][m] = fmaf(f16_bits_to_f32(xh), v, res[r][m]);
+          }
+        }
+      };
 #pragma unroll
       for (int i = 0; i < kCsr; ++i)
-        if (ccol[i] >= 0) outlier(ccol[i], f16_bits_to_f32(static_cast<uint16_t>(cbits[i])));
-      for (int e = e0 + 16 * (kKsw * kCsr + part) + b; e < e1; e += 16 * kKsw)
+        if ((cvalid >> (r * kCsr + i)) & 1u) outlier(ccol[r][i], f16_bits_to_f32(static_cast<uint16_t>(cbits[r][i])));
+      for (int e = e0[r] + 16 * (kKsw * kCsr + part) + b; e < e1[r]; e += 16 * kKsw)
         outlier(col_idx[e], f16_bits_to_f32(vals[e]));
     }
   }
 
-  // ---- sum over the 16 lanes of row j (lanes j, j + 4, ..., j + 60), then over
-  //      the row's waves in a fixed order through LDS
-  //      (rotations by 8 and 4 within each row of 16 lanes leave every lane
-  //      with the sum of its row's lanes of the same j; two cross-row
-  //      exchanges finish)
+  // ---- sum over the 16 lanes of each row (lanes j, j + 4, ..., j + 60), then
+  //      over the row's waves in a fixed order through LDS (rotations by 8 and
+  //      4 within each row of 16 lanes leave every lane with the sum of its
+  //      row's lanes of the same j; two cross-row exchanges finish)
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    float v = res[m];
-    v += bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(v), 0x128, 0xF, 0xF, false));   // row_ror:8
-    v += bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(v), 0x124, 0xF, 0xF, false));   // row_ror:4
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    if (b == 0) red[wv][m][j] = v;
-  }
-  __syncthreads();
-  if (part == 0 && b == 0 && nok) {
+  for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      if (m < M) {
-        float v = red[wv][m][j];
+      float v = res[r][m];
+      v += bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(v), 0x128, 0xF, 0xF, false));   // row_ror:8
+      v += bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(v), 0x124, 0xF, 0xF, false));   // row_ror:4
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (b == 0) red[wv][r][m][j] = v;
+    }
+  __syncthreads();
+  if (part == 0 && b == 0) {
 #pragma unroll
-        for (int q = 1; q < kKsw; ++q) v += red[wv + q][m][j];
-        store_out<OUTK>(Y, static_cast<size_t>(m) * N + n, v);
+    for (int r = 0; r < R; ++r) {
+      if (nok[r]) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m < M) {
+            float v = red[wv][r][m][j];
+#pragma unroll
+            for (int q = 1; q < kKsw; ++q) v += red[wv + q][r][m][j];
+            store_out<OUTK>(Y, static_cast<size_t>(m) * N + n[r], v);
+          }
+        }
       }
     }
   }
 }
 
-template <int MT, int S>
+// LDS budget per workgroup: two workgroups per CU (160 KB) with the static
+// reduction array beside it.
+constexpr size_t lds_budget(int R) { return R == 1 ? 72 * 1024 : 77 * 1024; }
+
+template <int MT, int S, int R>
 void launch_k(const SpqrArgs& a, int KS, hipStream_t stream) {
+  constexpr int ROWS = R * kRows;
   const int CS = KS / 32, BS = KS / 256;
   const size_t lds = static_cast<size_t>(MT) * (4 * CS + CS / 4 + 1) * 16 + static_cast<size_t>(CS) * MT * 8 +
-                     static_cast<size_t>(kRows) * BS * 28;
-  const int grid = (a.N + kRows - 1) / kRows;
+                     static_cast<size_t>(ROWS) * BS * 28;
+  const int grid = (a.N + ROWS - 1) / ROWS;
   // more than 64 KB of dynamic LDS must be allowed per kernel (once per process,
   // thread-safe initialisation of function-local statics)
-  static const bool lds_f32 = (hipFuncSetAttribute(reinterpret_cast<const void*>(spqr_quad_kernel<MT, S, OUT_F32>),
+  static const bool lds_f32 = (hipFuncSetAttribute(reinterpret_cast<const void*>(spqr_quad_kernel<MT, S, R, OUT_F32>),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   static_cast<int>(kLdsBudget + 1024)) == hipSuccess);
-  static const bool lds_f16 = (hipFuncSetAttribute(reinterpret_cast<const void*>(spqr_quad_kernel<MT, S, OUT_F16>),
+                                                   static_cast<int>(lds_budget(R) + 1024)) == hipSuccess);
+  static const bool lds_f16 = (hipFuncSetAttribute(reinterpret_cast<const void*>(spqr_quad_kernel<MT, S, R, OUT_F16>),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   static_cast<int>(kLdsBudget + 1024)) == hipSuccess);
+                                                   static_cast<int>(lds_budget(R) + 1024)) == hipSuccess);
   (void)lds_f32;
   (void)lds_f16;
   if (a.y_dtype == QLIN_F32)
-    hipLaunchKernelGGL((spqr_quad_kernel<MT, S, OUT_F32>), dim3(grid), dim3(kThreads), lds, stream,
+    hipLaunchKernelGGL((spqr_quad_kernel<MT, S, R, OUT_F32>), dim3(grid), dim3(kThreads), lds, stream,
                        a.X, a.M, a.K, KS, a.codes, a.stats1, a.stats2, a.row_ptr, a.col_idx, a.vals, a.N, a.Y);
   else
-    hipLaunchKernelGGL((spqr_quad_kernel<MT, S, OUT_F16>), dim3(grid), dim3(kThreads), lds, stream,
+    hipLaunchKernelGGL((spqr_quad_kernel<MT, S, R, OUT_F16>), dim3(grid), dim3(kThreads), lds, stream,
                        a.X, a.M, a.K, KS, a.codes, a.stats1, a.stats2, a.row_ptr, a.col_idx, a.vals, a.N, a.Y);
 }
 
-template <int MT>
-void launch_m(const SpqrArgs& a, hipStream_t stream) {
-  // K slice (multiple of 256): staged activations (2.375 bytes per value and
-  // token with the bank skew, plus 16 per token) and the rows' statistics (28
-  // bytes per 256 values and row) within the LDS budget, at most 8192 values
-  // (so the workgroup's 8 rows hold at most 768 first-level and 512
-  // second-level statistic words per slice, two and one per thread), in slices
-  // of equal size
-  const double per_k = 2.375 * MT + 28.0 * kRows / 256.0;
-  int KS = static_cast<int>(static_cast<double>(kLdsBudget - 16 * MT) / per_k);
+// K slice (multiple of 256): staged activations (2.375 bytes per value and
+// token with the bank skew, plus 16 per token) and the rows' statistics (28
+// bytes per 256 values and row) within the LDS budget, at most 8192 values (so
+// the workgroup's 8 R rows hold at most 768 R first-level and 512 R
+// second-level statistic words per slice), in slices of equal size.
+template <int MT, int R>
+int slice_k(int K) {
+  const double per_k = 2.375 * MT + 28.0 * R * kRows / 256.0;
+  int KS = static_cast<int>(static_cast<double>(lds_budget(R) - 16 * MT) / per_k);
   if (KS > 8192) KS = 8192;
   KS = KS / 256 * 256;
   if (KS < 256) KS = 256;
-  if (KS > a.K) KS = a.K;
-  const int nslices = (a.K + KS - 1) / KS;
-  KS = (a.K / 256 + nslices - 1) / nslices * 256;
+  if (KS > K) KS = K;
+  const int nslices = (K + KS - 1) / KS;
+  return (K / 256 + nslices - 1) / nslices * 256;
+}
+
+template <int MT, int R>
+void launch_r(const SpqrArgs& a, hipStream_t stream) {
+  const int KS = slice_k<MT, R>(a.K);
   // steps of 16 chunks per wave: the wave's run of ceil(cs / 4) chunks rounded
   // up to a multiple of 4, as in the kernel
   const int cs = KS / 32;
   const int steps = ((((cs + kKsw - 1) / kKsw + 3) & ~3) + 15) / 16;
-  if (steps <= 1) launch_k<MT, 1>(a, KS, stream);
-  else if (steps == 2) launch_k<MT, 2>(a, KS, stream);
-  else if (steps == 3) launch_k<MT, 3>(a, KS, stream);
-  else launch_k<MT, 4>(a, KS, stream);
+  if (steps <= 1) launch_k<MT, 1, R>(a, KS, stream);
+  else if (steps == 2) launch_k<MT, 2, R>(a, KS, stream);
+  else if (steps == 3) launch_k<MT, 3, R>(a, KS, stream);
+  else launch_k<MT, 4, R>(a, KS, stream);
+}
+
+// Two row groups per workgroup where a row is one K slice (up to 4 tokens):
+// 33B-shaped layers at M = 4, one group vs two (us): 6656 x 6656 16.7-17.2
+// vs 14.9, 17920 x 6656 35.2 vs 34.8; with three slices (6656 x 17920) the
+// second group gained nothing at M = 2..4 and lost 1 us at M = 1.  Five to
+// eight tokens keep one group (two would spill registers).
+template <int MT>
+void launch_m(const SpqrArgs& a, hipStream_t stream) {
+  if constexpr (MT == 4) {
+    if (slice_k<MT, 2>(a.K) == a.K) {
+      launch_r<MT, 2>(a, stream);
+      return;
+    }
+  }
+  launch_r<MT, 1>(a, stream);
 }
 
 }  // namespace
