@@ -262,6 +262,12 @@ qlin_status spqr_forward(const uint16_t* X, int M, int K,
   // one workspace can serve this call and the split-K calls in any order
   const size_t total = spqr_use_mfma(M, K, N) ? kCounterBytes + spqr_prep_bytes(K) : 0;
   QLIN_TRY(need_workspace(fn, workspace, workspace_bytes, total));
+  // with no outliers the CSR arrays may be NULL; the kernels that read CSR
+  // entries unconditionally (flagging those past a row) then read row_ptr
+  if (nnz == 0) {
+    col_idx = row_ptr;
+    vals = reinterpret_cast<const uint16_t*>(row_ptr);
+  }
   SpqrArgs a{X, M, K, N, codes, stats1, stats2, row_ptr, col_idx, vals, Y, y_dtype};
   if (total) spqr_mfma_launch(a, spqr_prep_view(static_cast<char*>(workspace) + kCounterBytes, K), stream);
   else if (spqr_use_quad(M, K)) spqr_quad_launch(a, stream);

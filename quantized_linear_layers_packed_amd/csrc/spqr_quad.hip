@@ -98,7 +98,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int b = lane >> 2, j = lane & 3;              // chunk slot of the step; row of the quad and token of the group
   const int n0 = blockIdx.x * ROWS;
   const int C = K >> 5, nb = K >> 8;
-  int rowl[R], n[R], e0[R], e1[R];                    // row of group r within the workgroup, its index, its CSR range
+  int rowl[R], n[R], p0[R], p1[R];                    // row of group r within the workgroup, its index, row_ptr of its row
+  int e0[R], e1[R];                                   // its CSR range (empty past N), set on the first slice
   bool nok[R];
   const uint32_t* crow[R];
 #pragma unroll
@@ -106,9 +107,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     rowl[r] = r * kRows + 4 * (wv / kKsw) + j;
     n[r] = n0 + rowl[r];
     nok[r] = n[r] < N;
-    crow[r] = codes + static_cast<size_t>(min(n[r], N - 1)) * C * 3;
-    e0[r] = nok[r] ? row_ptr[n[r]] : 0;
-    e1[r] = nok[r] ? row_ptr[n[r] + 1] : 0;
+    const int nc = min(n[r], N - 1);
+    crow[r] = codes + static_cast<size_t>(nc) * C * 3;
+    p0[r] = row_ptr[nc];                              // unconditional: a select here would wait for the load
+    p1[r] = row_ptr[nc + 1];
+    e0[r] = 0;
+    e1[r] = 0;
   }
   int tok[NG];                                        // this lane's A-operand token per group (rows past M re-read M - 1)
 #pragma unroll
@@ -127,7 +131,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
     for (int m = 0; m < MT; ++m) res[r][m] = 0.0f;
 
-  for (int k0 = 0; k0 < K; k0 += KS) {
+  // one K slice; the first is peeled off the loop (straight-line code, so the
+  // row_ptr values are waited for where the CSR preload uses them, after the
+  // stream is issued, not hoisted ahead of it)
+  auto slice = [&](const int k0, auto first_c) {
+    constexpr bool kFirst = decltype(first_c)::value;
     const int ks = min(KS, K - k0);
     const int cs = ks >> 5, bs = ks >> 8;
     const int cbase = k0 >> 5, bbase = k0 >> 8;
@@ -193,22 +201,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const int c = min(c0 + 16 * s + b, cs - 1);
       w[s] = *reinterpret_cast<const uint3*>(crow[0] + 3 * (cbase + c));
     }
-    if (k0 == 0) {
+    __builtin_amdgcn_sched_barrier(0);               // the whole code stream is issued before anything below
+    if constexpr (kFirst) {
+      // the row_ptr values pass through an empty asm after the stream is
+      // issued, so that nothing using them is scheduled ahead of it
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        asm volatile("" : "+v"(p0[r]), "+v"(p1[r]));
+        e0[r] = nok[r] ? p0[r] : 0;
+        e1[r] = nok[r] ? p1[r] : 0;
+      }
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < kCsr; ++i) {
+          // unconditional (a conditional load here is followed by a wait for
+          // it): entries past the row re-read one inside the arrays, which are
+          // never empty (with no outliers the entry point passes row_ptr)
           const int e = e0[r] + 16 * (kKsw * i + part) + b;
-          if (e < e1[r]) {
-            ccol[r][i] = col_idx[e];
-            cbits[r][i] = vals[e];
-            cvalid |= 1u << (r * kCsr + i);
-          }
+          const int ec = max(min(e, p1[r] - 1), 0);
+          ccol[r][i] = col_idx[ec];
+          cbits[r][i] = vals[ec];
+          cvalid |= e < e1[r] ? 1u << (r * kCsr + i) : 0u;
         }
     }
     // ---- 3. staging (after a barrier from the second slice on: the previous
     //      slice's readers must be done)
-    if (k0 > 0) __syncthreads();
+    if constexpr (!kFirst) __syncthreads();
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int it = tid + kThreads * r;
@@ -334,7 +353,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       for (int e = e0[r] + 16 * (kKsw * kCsr + part) + b; e < e1[r]; e += 16 * kKsw)
         outlier(col_idx[e], f16_bits_to_f32(vals[e]));
     }
-  }
+  };
+  slice(0, std::true_type{});
+  for (int k0 = KS; k0 < K; k0 += KS) slice(k0, std::false_type{});
 
   // ---- sum over the 16 lanes of each row (lanes j, j + 4, ..., j + 60), then
   //      over the row's waves in a fixed order through LDS (rotations by 8 and
