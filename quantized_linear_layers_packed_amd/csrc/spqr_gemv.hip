@@ -106,25 +106,27 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
   const int C = K >> 5, nb = K >> 8;
   const size_t nrow = static_cast<size_t>(min(n, N - 1));
   const uint32_t* crow = codes + nrow * C * 3;
-  const int e0 = nok ? row_ptr[n] : 0;
-  const int e1 = nok ? row_ptr[n + 1] : 0;
+  int p0 = row_ptr[nrow];                            // unconditional: a select here would wait for the load
+  int p1 = row_ptr[nrow + 1];
+  int e0 = 0, e1 = 0;                                 // this row's CSR range (empty past N), set on the first slice
 
   // CSR entries of this row held by this lane: e0 + 64 (KSW i + part) + lane,
   // loaded on the first slice behind the dense stream and kept as raw fp16
-  // bits until used (a conversion here would make the wave wait for each load)
+  // bits until used (a conversion here would make the wave wait for each
+  // load); bit i of cvalid flags a real entry
   int ccol[kCsr];
   uint32_t cbits[kCsr];
-#pragma unroll
-  for (int i = 0; i < kCsr; ++i) {
-    ccol[i] = -1;
-    cbits[i] = 0u;
-  }
+  uint32_t cvalid = 0u;
 
   float res[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) res[m] = 0.0f;
 
-  for (int k0 = 0; k0 < K; k0 += KS) {
+  // one K slice; the first is peeled off the loop (straight-line code, so the
+  // row_ptr values are waited for where the CSR preload uses them, after the
+  // stream is issued, not hoisted ahead of it)
+  auto slice = [&](const int k0, auto first_c) {
+    constexpr bool kFirst = decltype(first_c)::value;
     const int ks = min(KS, K - k0);
     const int cs = ks >> 5, bs = ks >> 8;
     const int cbase = k0 >> 5, bbase = k0 >> 8;
@@ -186,21 +188,30 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
       const int c = min(c0 + 64 * b + lane, cs - 1);
       w[b] = *reinterpret_cast<const uint3*>(crow + 3 * (cbase + c));
     }
-    if (k0 == 0) {
+    __builtin_amdgcn_sched_barrier(0);               // the whole code stream is issued before anything below
+    if constexpr (kFirst) {
+      // the row_ptr values pass through an empty asm after the stream is
+      // issued, so that nothing using them is scheduled ahead of it
+      asm volatile("" : "+v"(p0), "+v"(p1));
+      e0 = nok ? p0 : 0;
+      e1 = nok ? p1 : 0;
 #pragma unroll
       for (int i = 0; i < kCsr; ++i) {
+        // unconditional (a conditional load here is followed by a wait for
+        // it): entries past the row re-read one inside the arrays, which are
+        // never empty (with no outliers the entry point passes row_ptr)
         const int e = e0 + 64 * (KSW * i + part) + lane;
-        if (e < e1) {
-          ccol[i] = col_idx[e];
-          cbits[i] = vals[e];
-        }
+        const int ec = max(min(e, p1 - 1), 0);
+        ccol[i] = col_idx[ec];
+        cbits[i] = vals[ec];
+        cvalid |= e < e1 ? 1u << i : 0u;
       }
     }
     // ---- 3. staging (after a barrier from the second slice on: the previous
     //      slice's readers must be done); the activations first: they were
     //      loaded first, so this VALU work overlaps the weight loads still in
     //      flight
-    if (k0 > 0) __syncthreads();
+    if constexpr (!kFirst) __syncthreads();
     for (int it = tid; it < items; it += kThreads) {
       const int m = static_cast<int>((static_cast<float>(it) + 0.5f) * invcs), c = it - m * cs;
       uint32_t u[16];
@@ -317,11 +328,13 @@ __global__ __launch_bounds__(kThreads) void spqr_gemv_kernel(
     if (nok) {
 #pragma unroll
       for (int i = 0; i < kCsr; ++i)
-        if (ccol[i] >= 0) outlier(ccol[i], f16_bits_to_f32(static_cast<uint16_t>(cbits[i])));
+        if ((cvalid >> i) & 1u) outlier(ccol[i], f16_bits_to_f32(static_cast<uint16_t>(cbits[i])));
       for (int e = e0 + 64 * (KSW * kCsr + part) + lane; e < e1; e += 64 * KSW)
         outlier(col_idx[e], f16_bits_to_f32(vals[e]));
     }
-  }
+  };
+  slice(0, std::true_type{});
+  for (int k0 = KS; k0 < K; k0 += KS) slice(k0, std::false_type{});
 
   // ---- reduction over the row's lanes, then over its KSW waves in a fixed order
 #pragma unroll
