@@ -75,7 +75,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int32_t* col_idx, const uint16_t* vals,
     int N, void* Y) {
   constexpr int kCsr = R == 1 ? 4 : 1;                // CSR entries per lane and row held in registers
-  constexpr int NG = MT / 4;                          // token groups of 4
+  constexpr int NG = (MT + 3) / 4;                    // token groups of 4 (a single token fills one)
+  constexpr int TG = MT < 4 ? MT : 4;                 // tokens used per group
   constexpr int ROWS = R * kRows;                     // rows of the workgroup
   constexpr int NR1 = (ROWS * 32 * 3 + kThreads - 1) / kThreads;   // statistic piece rounds (bs <= 32)
   constexpr int NR2 = (ROWS * 32 * 2 + kThreads - 1) / kThreads;
@@ -312,12 +313,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             dA = mfma4(a1.z, a1.w, pk[6], pk[7], dA);
             dB = mfma4(a3.z, a3.w, pk[14], pk[15], dB);
             // the group sums of tokens 4 g .. 4 g + 3 at this chunk: (A, B) per token
-            const float4* xq = reinterpret_cast<const float4*>(xs + static_cast<size_t>(cc) * MT + 4 * g);
-            const float4 s01 = xq[0], s23 = xq[1];
-            const float xA[4] = {s01.x, s01.z, s23.x, s23.z};
-            const float xB[4] = {s01.y, s01.w, s23.y, s23.w};
+            float xA[4], xB[4];
+            if constexpr (TG == 4) {
+              const float4* xq = reinterpret_cast<const float4*>(xs + static_cast<size_t>(cc) * MT + 4 * g);
+              const float4 s01 = xq[0], s23 = xq[1];
+              xA[0] = s01.x; xA[1] = s01.z; xA[2] = s23.x; xA[3] = s23.z;
+              xB[0] = s01.y; xB[1] = s01.w; xB[2] = s23.y; xB[3] = s23.w;
+            } else {
+              const float2 s0 = xs[static_cast<size_t>(cc) * MT];
+              xA[0] = s0.x;
+              xB[0] = s0.y;
+            }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < TG; ++t) {
               // sum x (c - z_hat) = acc / 8 - (128 + z_hat) * sum(x)
               res[r][4 * g + t] = fmaf(sA, fmaf(dA[t], 0.125f, cA * xA[t]), res[r][4 * g + t]);
               res[r][4 * g + t] = fmaf(sB, fmaf(dB[t], 0.125f, cB * xB[t]), res[r][4 * g + t]);
@@ -469,7 +477,8 @@ void launch_m(const SpqrArgs& a, hipStream_t stream) {
 }  // namespace
 
 void spqr_quad_launch(const SpqrArgs& a, hipStream_t stream) {
-  if (a.M <= 4) launch_m<4>(a, stream);
+  if (a.M == 1) launch_m<1>(a, stream);
+  else if (a.M <= 4) launch_m<4>(a, stream);
   else launch_m<8>(a, stream);
 }
 
