@@ -44,6 +44,11 @@ constexpr size_t kLdsBudget = 72 * 1024;
 
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 
+// Largest K slice in statistic blocks of 256: 32 (8192 values); 72 (18432)
+// for a single token, whose staging is small enough to take a 17920-wide row
+// in one slice.
+constexpr int max_blocks(int MT) { return MT == 1 ? 72 : 32; }
+
 // 16 blocks of D (4 x 4) += A (4 x 4) B (4 x 4): lane 4 b + i supplies row i of
 // A_b and column i of B_b (4 fp16 each, element e of both at the same k) and
 // receives column i of D_b (rows 0..3).
@@ -78,8 +83,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   constexpr int NG = (MT + 3) / 4;                    // token groups of 4 (a single token fills one)
   constexpr int TG = MT < 4 ? MT : 4;                 // tokens used per group
   constexpr int ROWS = R * kRows;                     // rows of the workgroup
-  constexpr int NR1 = (ROWS * 32 * 3 + kThreads - 1) / kThreads;   // statistic piece rounds (bs <= 32)
-  constexpr int NR2 = (ROWS * 32 * 2 + kThreads - 1) / kThreads;
+  constexpr int NR1 = (ROWS * max_blocks(MT) * 3 + kThreads - 1) / kThreads;   // statistic piece rounds
+  constexpr int NR2 = (ROWS * max_blocks(MT) * 2 + kThreads - 1) / kThreads;
   extern __shared__ uint4 smem[];
   __shared__ float red[kWaves][R][MT][4];
   const int CS = KS >> 5;                             // chunks per slice
@@ -430,14 +435,14 @@ void launch_k(const SpqrArgs& a, int KS, hipStream_t stream) {
 
 // K slice (multiple of 256): staged activations (2.375 bytes per value and
 // token with the bank skew, plus 16 per token) and the rows' statistics (28
-// bytes per 256 values and row) within the LDS budget, at most 8192 values (so
-// the workgroup's 8 R rows hold at most 768 R first-level and 512 R
-// second-level statistic words per slice), in slices of equal size.
+// bytes per 256 values and row) within the LDS budget, at most max_blocks
+// statistic blocks (which sizes the statistic piece rounds), in slices of
+// equal size.
 template <int MT, int R>
 int slice_k(int K) {
   const double per_k = 2.375 * MT + 28.0 * R * kRows / 256.0;
   int KS = static_cast<int>(static_cast<double>(lds_budget(R) - 16 * MT) / per_k);
-  if (KS > 8192) KS = 8192;
+  if (KS > 256 * max_blocks(MT)) KS = 256 * max_blocks(MT);
   KS = KS / 256 * 256;
   if (KS < 256) KS = 256;
   if (KS > K) KS = K;
@@ -455,14 +460,19 @@ void launch_r(const SpqrArgs& a, hipStream_t stream) {
   if (steps <= 1) launch_k<MT, 1, R>(a, KS, stream);
   else if (steps == 2) launch_k<MT, 2, R>(a, KS, stream);
   else if (steps == 3) launch_k<MT, 3, R>(a, KS, stream);
-  else launch_k<MT, 4, R>(a, KS, stream);
+  else if (steps == 4 || MT > 1) launch_k<MT, 4, R>(a, KS, stream);
+  else if constexpr (MT == 1) {
+    if (steps <= 6) launch_k<MT, 6, R>(a, KS, stream);
+    else launch_k<MT, 9, R>(a, KS, stream);
+  }
 }
 
 // Two row groups per workgroup where a row is one K slice (up to 4 tokens):
 // 33B-shaped layers at M = 4, one group vs two (us): 6656 x 6656 16.7-17.2
 // vs 14.9, 17920 x 6656 35.2 vs 34.8; with three slices (6656 x 17920) the
 // second group gained nothing at M = 2..4 and lost 1 us at M = 1.  Five to
-// eight tokens keep one group (two would spill registers).
+// eight tokens, and single tokens (whose rows of up to 18432 take 9 steps),
+// keep one group: two would spill registers.
 template <int MT>
 void launch_m(const SpqrArgs& a, hipStream_t stream) {
   if constexpr (MT == 4) {
