@@ -230,9 +230,11 @@ qlin_status spqr_workspace_bytes(int M, int K, int N, int y_dtype, size_t* bytes
  * (device, y_dtype QLIN_F16 or QLIN_F32).  The CSR row of output n is added into
  * the same fp32 accumulator as the dense dot product, in the same kernel pass.
  * Small batches run fused kernels on the exact codes (no workspace): M = 1 a
- * GEMV (v_dot2 on fp16 code pairs), M = 2..6 four rows per wave on the 4x4x4
+ * GEMV (v_dot2 on fp16 code pairs; rows longer than 8192 take the next
+ * kernel), M = 2..6, and 7..8 where N > K, four rows per wave on the 4x4x4
  * matrix instruction (16 chunks x 4 tokens x 4 rows per instruction), both with
- * the group statistics applied in fp32.  M = 7..16 run a matrix-core kernel:
+ * the group statistics applied in fp32.  Other batches up to M = 16 run a
+ * matrix-core kernel:
  * a small prepass lays the activations out in the
  * workspace (operand order, group sums and a transposed copy, K * 68 bytes),
  * then each group's exact codes go through v_mfma_f32_16x16x16_f16 with the

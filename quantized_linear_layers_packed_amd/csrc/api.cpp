@@ -270,7 +270,7 @@ qlin_status spqr_forward(const uint16_t* X, int M, int K,
   }
   SpqrArgs a{X, M, K, N, codes, stats1, stats2, row_ptr, col_idx, vals, Y, y_dtype};
   if (total) spqr_mfma_launch(a, spqr_prep_view(static_cast<char*>(workspace) + kCounterBytes, K), stream);
-  else if (spqr_use_quad(M, K)) spqr_quad_launch(a, stream);
+  else if (spqr_use_quad(M, K, N)) spqr_quad_launch(a, stream);
   else spqr_gemv_launch(a, stream);
   return check_launch(fn);
 }

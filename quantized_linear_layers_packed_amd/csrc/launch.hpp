@@ -70,8 +70,8 @@ struct SpqrArgs {
 };
 
 void spqr_gemv_launch(const SpqrArgs& a, hipStream_t stream);
-// 2 .. 8 tokens: four rows per wave on the 4 x 4 x 4 matrix instruction (no
-// workspace); the forward routes 2 .. 6 here.
+// 1 .. 8 tokens: four rows per wave on the 4 x 4 x 4 matrix instruction (no
+// workspace); the forward's routing is spqr_use_quad.
 void spqr_quad_launch(const SpqrArgs& a, hipStream_t stream);
 
 // Matrix-core path for small batches: activations laid out by a prepass in the
@@ -83,19 +83,20 @@ struct SpqrPrep {
 };
 // Routing of the SpQR forward by batch: one token runs the GEMV (spqr_gemv),
 // 2 .. 6 the four-rows-per-wave kernel on the 4 x 4 x 4 matrix instruction
-// (spqr_quad), 7 .. 16 the matrix-core path (16 tokens per 16 x 16 x 16
-// instruction, spqr_mfma).  Three 33B-shaped layers (us): M = 2: 84.8 GEMV,
-// 81.2 quad; M = 4: 107.6 GEMV, 91.9 quad; M = 6: 132.8 quad, 138.1 matrix-core;
-// M = 8: 145.6 quad, 137.9 matrix-core (whose time hardly moves with M).
-inline bool spqr_use_mfma(int M, int K, int N) {
-  (void)K;
-  (void)N;
-  return M >= 7;
-}
+// (spqr_quad), 7 and 8 that kernel on layers wider than deep (N > K) and the
+// matrix-core path (16 tokens per 16 x 16 x 16 instruction, spqr_mfma)
+// otherwise, 9 .. 16 the matrix-core path.  33B-shaped layers (us), quad vs
+// matrix-core: M = 7: 6656 x 6656 24.5 vs 22.3, 17920 x 6656 52.5 vs 57.4,
+// 6656 x 17920 56.0 vs 56.0; M = 8: 25.5 vs 22.3, 56.2 vs 57.3, 58.3 vs 56.0
+// (the matrix-core time hardly moves with M); at M = 6 the quad kernel is
+// level or ahead on all three.
+inline bool spqr_use_mfma(int M, int K, int N) { return M >= 9 || (M >= 7 && N <= K); }
 // Single tokens on rows longer than 8192 also go to the four-row kernel: there
 // the GEMV splits a row over several waves whose 64-chunk blocks leave a
 // quarter of its lanes idle (6656 x 17920: 30.5 against 33.1 us).
-inline bool spqr_use_quad(int M, int K) { return (M >= 2 && M <= 6) || (M == 1 && K > 8192); }
+inline bool spqr_use_quad(int M, int K, int N) {
+  return (M >= 2 && M <= 6) || (M == 1 && K > 8192) || (M >= 7 && M <= 8 && N > K);
+}
 size_t spqr_prep_bytes(int K);
 SpqrPrep spqr_prep_view(char* base, int K);
 void spqr_mfma_launch(const SpqrArgs& a, const SpqrPrep& p, hipStream_t stream);

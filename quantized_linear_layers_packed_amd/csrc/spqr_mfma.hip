@@ -1,4 +1,5 @@
-// SpQR product for batches of 7..16 tokens on the matrix cores, gfx950.
+// SpQR product for batches of 7..16 tokens (9..16 where N > K) on the matrix
+// cores, gfx950.
 //
 // Y[m][n] = sum_g s_hat[n][g] * (sum_{k in g} x[m][k] q[n][k] - z_hat[n][g] * sum_{k in g} x[m][k])
 //           + sum_{(n,k,v) in CSR} x[m][k] * v

@@ -46,10 +46,12 @@ def test_unpack_is_bit_exact():
 
 @pytest.mark.parametrize("p", [0.0, 0.01, 0.05])
 def test_ragged_shapes(p):
-    # M = 1 runs the GEMV, 2..6 the four-rows-per-wave kernel (one token group
-    # up to 4, two beyond), 7 and 16 the matrix-core path (two column tiles per
-    # wave where K >= 2N, one where K < 2N)
-    for (N, K) in ((37, 512), (16, 256), (50, 2560), (21, 26624), (133, 256), (600, 768), (1100, 2048)):
+    # M = 1 runs the GEMV (the four-row kernel where K > 8192), 2..6 the
+    # four-rows-per-wave kernel (one token group up to 4, two beyond), 7 the
+    # four-row kernel where N > K (here 300 x 256) and else, like 16, the
+    # matrix-core path (two column tiles per wave where K >= 2N, one where K < 2N)
+    for (N, K) in ((37, 512), (16, 256), (50, 2560), (21, 26624), (133, 256), (600, 768), (1100, 2048),
+                   (300, 256)):
         W = synth.student_t3_f32((N, K), 0.02, f"gpu/spqr/rag{N}")
         d = dev_pack(qlin.spqr_pack(W, p))
         st = ospqr.encode(W, p)
