@@ -1,4 +1,4 @@
-// SpQR GEMV for batches of 2 .. 8 tokens on the 4 x 4 x 4 matrix instruction
+// SpQR GEMV for batches of 1 .. 8 tokens on the 4 x 4 x 4 matrix instruction
 // with the CSR outliers fused, gfx950.
 //
 // Y[m][n] = sum_k x[m][k] * s_hat(q - z_hat)  +  sum_{(n,k,v) in CSR} x[m][k] * v
@@ -16,14 +16,23 @@
 //   * lane 4 b + j then holds the group's sums for the four tokens of row j
 //     and applies the group statistics in fp32 as the GEMV does:
 //     s_hat * (acc / 8 - (128 + z_hat) * sum x), sum x from the staging;
-//   * five to eight tokens run two token groups on the same codes;
+//   * five to eight tokens run two token groups on the same codes; a single
+//     token (routed here on long rows, where the GEMV's 64-chunk blocks leave
+//     lanes idle) has one group-sum pair and one accumulator per chunk and
+//     takes rows of up to 18432 in one K slice;
 //   * the row's statistics are staged per workgroup, the row's CSR entries are
 //     walked by the 16 lanes of the row in each of its waves and added into the
 //     same accumulators, and the lanes' and waves' parts are summed in a fixed
 //     order (no atomics).
 // Rows are split over KSW = 4 waves (each a contiguous run of the K slice's
 // chunks); activations are staged in K slices when M * K exceeds the LDS
-// budget, as in the GEMV.
+// budget, as in the GEMV.  A workgroup serves one or two groups of 8 rows (two
+// where a row of up to 4 tokens is one slice: one staging for 16 rows).  The
+// load order matters as much as the arithmetic: the code stream is issued
+// before anything waits for row_ptr (first slice peeled off the slice loop, a
+// scheduling barrier after the code loads) and the CSR preloads are
+// unconditional, so every wait the compiler inserts counts exactly the loads
+// it needs.
 
 #include <type_traits>
 
