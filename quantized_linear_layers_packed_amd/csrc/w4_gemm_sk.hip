@@ -61,6 +61,22 @@ __device__ __forceinline__ h8_t dequant_nat(uint32_t w, h2_t zz, h2_t ss) {
   return b;
 }
 
+// Eight exact fp16 values q - z in natural k order from one packed word (the
+// and-or gives 1024 + q, the packed subtraction of 1024 + z is exact).
+__device__ __forceinline__ h8_t codes_minus_zero(uint32_t w, h2_t zz) {
+  const uint32_t t = w >> 4;
+  h8_t b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t sel = static_cast<uint32_t>(j) | (0x0Cu << 8) | (static_cast<uint32_t>(4 + j) << 16) | (0x0Cu << 24);
+    const uint32_t pr = __builtin_amdgcn_perm(t, w, sel);
+    const h2_t d = bitcast<h2_t>(and_or(pr, 0x000F000Fu, 0x64006400u)) - zz;
+    b[2 * j] = d[0];
+    b[2 * j + 1] = d[1];
+  }
+  return b;
+}
+
 template <int TM, int NW, int R, int RV, int OUTK>
 __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
     const uint16_t* X, int M, int K, const uint32_t* qweight, const uint16_t* scales,
@@ -72,6 +88,11 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
   constexpr int kBN = 32 * NW;                // output columns per tile
   constexpr int BM = 32 * TM;
   constexpr int APT = BM * 16 / kThreads;   // 16-byte activation pieces per thread per step
+  // 32- and 64-row tiles feed exact q - z to the matrix cores and apply the
+  // scale per K step in fp32 (fewer VALU per matrix instruction there, and no
+  // fp16 rounding of the weights); 128-row tiles dequantize to s (q - z) in
+  // fp16, where the per-step rescale of 4 x 16 accumulators would cost more
+  constexpr bool kExact = TM <= 2;
   static_assert(APT >= 1, "tile too small");
   extern __shared__ uint4 smem[];
   __shared__ int s_last;
@@ -177,16 +198,38 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_sk_kernel(
       };
       h8_t afr[2][TM];
       read_a(0, afr[0]);
+      if constexpr (kExact) {
+        // exact q - z into a step accumulator, scaled into the tile in fp32
+        // after the step's matrix instructions (a K step lies in one group)
+        const float sf = f16_bits_to_f32(static_cast<uint16_t>(bs[S]));
+        f32x16_t accs[TM];
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        if (st + 1 < 8) read_a(st + 1, afr[(st + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);     // the reads stay ahead of this group's math
-        const uint4 q4 = bq[S][st >> 2];
-        const uint32_t w = (st & 3) == 0 ? q4.x : (st & 3) == 1 ? q4.y : (st & 3) == 2 ? q4.z : q4.w;
-        const h8_t b = dequant_nat(w, zz, ss);
+        for (int st = 0; st < 8; ++st) {
+          if (st + 1 < 8) read_a(st + 1, afr[(st + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);   // the reads stay ahead of this group's math
+          const uint4 q4 = bq[S][st >> 2];
+          const uint32_t w = (st & 3) == 0 ? q4.x : (st & 3) == 1 ? q4.y : (st & 3) == 2 ? q4.z : q4.w;
+          const h8_t b = codes_minus_zero(w, zz);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            accs[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[st & 1][i], b, st == 0 ? f32x16_t{} : accs[i], 0, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[st & 1][i], b, acc[i], 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < RV; ++r) acc[i][r] = fmaf(sf, accs[i][r], acc[i][r]);
+      } else {
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          if (st + 1 < 8) read_a(st + 1, afr[(st + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);   // the reads stay ahead of this group's math
+          const uint4 q4 = bq[S][st >> 2];
+          const uint32_t w = (st & 3) == 0 ? q4.x : (st & 3) == 1 ? q4.y : (st & 3) == 2 ? q4.z : q4.w;
+          const h8_t b = dequant_nat(w, zz, ss);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[st & 1][i], b, acc[i], 0, 0, 0);
+        }
       }
       // the next step's activations (past the range end this rewrites the idle
       // buffer), then the fetch R steps ahead into the set of step kk
