@@ -49,7 +49,6 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKsw = 4;                          // waves per row quad
 constexpr int kRows = 4 * (kWaves / kKsw);       // rows per workgroup
-constexpr size_t kLdsBudget = 72 * 1024;
 
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 
