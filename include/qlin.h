@@ -120,8 +120,10 @@ qlin_status qlin_w4_workspace_bytes(int x_dtype, int M, int K, int N, int G, int
  *   - 4 <= M <= 16, G = 128 / 256: a small-batch fp16 MFMA kernel (16 columns
  *     per workgroup, K split over its waves) on weights S * (q - z) rounded
  *     once to fp16;
- *   - larger M, G = 128 / 256: an fp16 MFMA GEMM on the same fp16 weights,
- *     split over the device's compute units (stream-K, workspace);
+ *   - larger M, G = 128 / 256: an fp16 MFMA GEMM split over the device's
+ *     compute units (stream-K, workspace); up to 64 rows per tile it takes the
+ *     exact codes q - z and applies S per 128-wide K step in fp32, 128-row
+ *     tiles take the same fp16 weights as the small-batch kernel;
  *   - larger M, G = 32 / 64: an fp16 MFMA GEMM on exact codes q - z with a
  *     per-group fp32 rescale.
  * The MFMA paths take fp16 activations.  bf16 X on those paths is first
