@@ -113,6 +113,22 @@ def test_gemv_ragged_shapes_and_dtypes(G, x_dtype, K):
         assert np.array_equal(yb, f32_to_bf16_bits(y32)), "bf16 store is not RNE of the fp32 result"
 
 
+@pytest.mark.parametrize("K", [14336, 16384, 16384 + 256])
+@pytest.mark.parametrize("G", [32, 128])
+def test_longest_gemv_rows_and_just_beyond(G, K):
+    """The GEMV's widest instance (two waves per row, four blocks of 64 chunks
+    per lane: 12288 < K <= 16384, the last block ragged at K = 14336) and the
+    first K past the GEMV's range, which the MFMA kernels take at every batch."""
+    N = 37
+    W = synth.normal_f32((N, K), 0.02, f"gpu/w4/long{G}")
+    packed = dev_pack(W, G)
+    ref_st = ow4.encode(W, G)
+    for M, x_dtype in ((1, F16), (2, BF16), (3, F16), (16, F16)):
+        say(f"w4 long rows N={N} K={K} G={G} M={M} x={x_dtype}")
+        X = synth.x_f16(M, K, f"gpu/w4/longx{M}") if x_dtype == F16 else synth.x_bf16_bits(M, K, f"gpu/w4/longx{M}")
+        check_close(gpu_w4(X, x_dtype, packed, N, K, G, F32), ow4.forward(X, *ref_st, K, G), f"K={K} G={G} M={M}")
+
+
 def test_batch_rows_are_independent():
     """A row's result does not depend on the other rows of its batch, bit for
     bit within each kernel: the GEMV (M <= 3), the small-batch kernel
