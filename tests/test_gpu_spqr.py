@@ -63,6 +63,21 @@ def test_ragged_shapes(p):
             check_close(gpu_spqr(X, d, N, K, F16), ref, f"M={M} f16")
 
 
+@pytest.mark.parametrize("N,K,M", [(45, 8448, 1), (45, 7168, 3), (45, 4352, 2), (29, 4352, 6)])
+def test_four_row_kernel_step_counts(N, K, M):
+    """Row lengths that put the four-row kernel on the instances the layers
+    above do not reach: one token with a single 8448-long slice (six steps of
+    16 chunks per wave), a 4-token group over two 3584-long slices (two steps),
+    two tokens with both row groups over one 4352-long slice (three steps), and
+    six tokens (two groups) over two slices."""
+    W = synth.student_t3_f32((N, K), 0.02, f"gpu/spqr/steps{K}")
+    d = dev_pack(qlin.spqr_pack(W, 0.01))
+    st = ospqr.encode(W, 0.01)
+    say(f"spqr four-row steps N={N} K={K} M={M}")
+    X = synth.x_f16(M, K, f"gpu/spqr/stepsx{M}")
+    check_close(gpu_spqr(X, d, N, K, F32), ospqr.forward(X, st, K), f"N={N} K={K} M={M}")
+
+
 def test_csr_part_alone_matches_sparse_product():
     """Dense part forced to zero (codes 0, z_hat = 0): the output is the CSR
     product alone, so every outlier entry must be consumed once at its column."""
