@@ -271,7 +271,8 @@ qlin_status spqr_forward(const uint16_t* X, int M, int K,
   SpqrArgs a{X, M, K, N, codes, stats1, stats2, row_ptr, col_idx, vals, Y, y_dtype};
   if (total) spqr_mfma_launch(a, spqr_prep_view(static_cast<char*>(workspace) + kCounterBytes, K), stream);
   else if (spqr_use_quad(M, K, N)) spqr_quad_launch(a, stream);
-  else spqr_gemv_launch(a, stream);
+  else if (M == 1) spqr_gemv_launch(a, stream);
+  else return fail(QLIN_EUNSUPPORTED, std::string(fn) + ": no kernel for this batch size");
   return check_launch(fn);
 }
 

@@ -69,6 +69,7 @@ struct SpqrArgs {
   int y_dtype;
 };
 
+// one token (M == 1); rows of any length (the router sends it those up to 8192)
 void spqr_gemv_launch(const SpqrArgs& a, hipStream_t stream);
 // 1 .. 8 tokens: four rows per wave on the 4 x 4 x 4 matrix instruction (no
 // workspace); the forward's routing is spqr_use_quad.

@@ -463,11 +463,9 @@ __global__ void spqr_unpack_kernel(const uint32_t* __restrict__ codes, const uin
 }  // namespace
 
 void spqr_gemv_launch(const SpqrArgs& a, hipStream_t stream) {
-  if (a.M <= 1) launch_m<1>(a, stream);
-  else if (a.M <= 2) launch_m<2>(a, stream);
-  else if (a.M <= 4) launch_m<4>(a, stream);
-  else if (a.M <= 8) launch_m<8>(a, stream);
-  else launch_m<16>(a, stream);
+  // single tokens only: from two tokens on the four-row and matrix-core
+  // kernels are faster at every shape measured, and the router sends them there
+  launch_m<1>(a, stream);
 }
 
 void spqr_unpack_launch(const uint32_t* codes, const uint32_t* stats1, int N, int K,

@@ -63,6 +63,19 @@ def test_ragged_shapes(p):
             check_close(gpu_spqr(X, d, N, K, F16), ref, f"M={M} f16")
 
 
+@pytest.mark.parametrize("K", [4352, 5120, 6144, 8192])
+def test_single_token_gemv_block_counts(K):
+    """One token on rows of 4097..8192 values: three and four 64-chunk blocks
+    per lane in the GEMV (the layer shapes above reach one, two and four)."""
+    N = 41
+    W = synth.student_t3_f32((N, K), 0.02, f"gpu/spqr/gemv{K}")
+    d = dev_pack(qlin.spqr_pack(W, 0.01))
+    st = ospqr.encode(W, 0.01)
+    say(f"spqr gemv blocks N={N} K={K} M=1")
+    X = synth.x_f16(1, K, "gpu/spqr/gemvx")
+    check_close(gpu_spqr(X, d, N, K, F32), ospqr.forward(X, st, K), f"N={N} K={K} M=1")
+
+
 @pytest.mark.parametrize("N,K,M", [(45, 8448, 1), (45, 7168, 3), (45, 4352, 2), (29, 4352, 6)])
 def test_four_row_kernel_step_counts(N, K, M):
     """Row lengths that put the four-row kernel on the instances the layers
