@@ -63,9 +63,6 @@ qlin_status dense_f16_gemm_launch(const uint16_t* X, const uint16_t* W, int M, i
   // 128 x 128 or 128 x 64 that still gives at least 160 tiles (the smallest one
   // otherwise), as for the int8 GEMM.
   if (M <= 64) return launch_o<2, 4, 1, 1, 6>(X, W, M, N, K, Y, y_dtype, ws, need, stream);
-#ifdef QLIN_DENSE_CFG
-  return launch_o<QLIN_DENSE_CFG>(X, W, M, N, K, Y, y_dtype, ws, need, stream);
-#endif
   auto tiles = [&](int bm, int bn) { return static_cast<long long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (tiles(256, 128) >= 160) return launch_o<4, 2, 2, 2, 3>(X, W, M, N, K, Y, y_dtype, ws, need, stream);
   if (tiles(128, 128) >= 160) return launch_o<4, 2, 1, 2, 4>(X, W, M, N, K, Y, y_dtype, ws, need, stream);

@@ -473,9 +473,6 @@ void spqr_mfma_launch(const SpqrArgs& a, const SpqrPrep& p, hipStream_t stream) 
   hipLaunchKernelGGL(spqr_prep_kernel, dim3((threads + kPrepThreads - 1) / kPrepThreads), dim3(kPrepThreads), 0,
                      stream, a.X, a.M, a.K, const_cast<uint4*>(p.Xp), const_cast<float*>(p.Xs),
                      const_cast<uint16_t*>(p.XT));
-#if defined(QLIN_SPQR_KSW) && defined(QLIN_SPQR_RING) && defined(QLIN_SPQR_CT)
-  launch_t<QLIN_SPQR_KSW, QLIN_SPQR_RING, QLIN_SPQR_CT>(a, p, stream);
-#else
   // Two column tiles per wave where rows are long against the column count
   // (one activation fragment then feeds two tiles, halving the activation
   // reads, at 165 VGPRs: one workgroup per CU): the 6656 x 17920 layer
@@ -483,7 +480,6 @@ void spqr_mfma_launch(const SpqrArgs& a, const SpqrPrep& p, hipStream_t stream) 
   // (57 -> 64) and the square one keep one tile and two workgroups per CU.
   if (a.K >= 2 * a.N) launch_t<8, 2, 2>(a, p, stream);
   else launch_t<8, 2, 1>(a, p, stream);
-#endif
 }
 
 }  // namespace qlin

@@ -640,10 +640,6 @@ qlin_status sq_gemm_launch(const int8_t* Xq, const float* x_scale, const int8_t*
   }
   if (M > 32 && M <= 64 && K % 128 == 0)
     return gemm_big_o<2, 4, 1, 1, 128, 6>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, ws, need, stream);
-#ifdef QLIN_BIG_CFG
-  if (M > 64 && K % 128 == 0)
-    return gemm_big_o<QLIN_BIG_CFG>(Xq, x_scale, Wq, w_scale, M, N, K, Y, y_dtype, acc_out, ws, need, stream);
-#endif
   if (M > 64 && K % 128 == 0) {
     auto tiles = [&](int bm, int bn) { return static_cast<long long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 128) >= 160)
