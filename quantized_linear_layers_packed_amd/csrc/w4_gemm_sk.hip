@@ -388,8 +388,7 @@ qlin_status w4_gemm_sk_launch(const W4Args& a, WsView ws, size_t* need, hipStrea
   // layers (three, fp16): 65.5 -> 50.6 us at 32 rows, 83.8 -> 64.0 at 64,
   // 130 -> 94 at 128, 128 -> 113 at 256; the 70B-shaped layers keep 8 waves
   // except the 8192 x 8192 one below 256 rows (29.7 -> 27.7 us at 32).
-  if (a.M <= 8) return launch_o<1, 8, 6, 4>(a, ws, need, stream);
-  if (a.M <= 16) return launch_o<1, 8, 6, 8>(a, ws, need, stream);
+  // (batches up to 16 rows take the small-batch kernel at these group sizes)
   const int TM = a.M <= 32 ? 1 : a.M <= 64 ? 2 : 4;
   const long long tiles8 = static_cast<long long>((a.M + 32 * TM - 1) / (32 * TM)) * ((a.N + 255) / 256);
   const int nw = (a.K > 16384 || tiles8 > 96) ? 8 : (TM <= 2 && tiles8 <= 48) ? 2 : 4;

@@ -129,6 +129,20 @@ def test_longest_gemv_rows_and_just_beyond(G, K):
         check_close(gpu_w4(X, x_dtype, packed, N, K, G, F32), ow4.forward(X, *ref_st, K, G), f"K={K} G={G} M={M}")
 
 
+@pytest.mark.parametrize("M,N,K,G", [(20, 12800, 1024, 128), (40, 12800, 512, 256), (100, 2, 256, 128)])
+def test_stream_k_tile_widths(M, N, K, G):
+    """Shapes that put the stream-K GEMM on 128-column tiles: 32-row tiles with
+    50 tiles of 256 columns, 64-row tiles with 50, and 128-row tiles on a
+    two-row layer too small for the direct-load kernel."""
+    W = synth.normal_f32((N, K), 0.015, f"gpu/w4/skw{N}")
+    packed = dev_pack(W, G)
+    st = ow4.encode(W, G)
+    for x_dtype in (F16, BF16):
+        say(f"w4 stream-K widths M={M} N={N} K={K} G={G} x={x_dtype}")
+        X = (synth.x_bf16_bits if x_dtype == BF16 else synth.x_f16)(M, K, f"gpu/w4/skwx{M}")
+        check_close(gpu_w4(X, x_dtype, packed, N, K, G, F32), ow4.forward(X, *st, K, G), f"M={M} N={N} K={K}")
+
+
 def test_batch_rows_are_independent():
     """A row's result does not depend on the other rows of its batch, bit for
     bit within each kernel: the GEMV (M <= 3), the small-batch kernel
